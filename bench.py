@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the register-tiled GEMM library on one MI355X.
+
+One step = one call of the hot path on one batch of synthetic input: the fp32 register-tiled
+GEMM C = A @ B at M = N = K = 4096 (row-major, U[-1,1], alpha = 1, beta = 0), inputs
+resident in HBM before the timed region. The same JSON line also carries the bf16 MFMA path
+at 8192^3 (A row-major, B column-major, N(0,1) rounded to bf16) and the kernel ladder
+(naive -> LDS-tiled -> register-tiled -> MFMA), each timed the same way.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-ladder] [--no-cpu]
+
+Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize() calls
+(wall clock -> ms_per_step and value), with a HIP event pair around every launch on the
+stream the library launches on (the caller's current stream) -> the average kernel
+duration used for the roofline figure. The CPU baseline times the fp64 oracle as it stands
+on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of FP32-vector / bf16-MFMA peak at M=N=K=4096/8192"
+
+
+def _parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-ladder", action="store_true", help="skip the naive/LDS rungs")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 8192^3 leg")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    return p.parse_args()
+
+
+def _time(torch, fn, steps, warmup):
+    """(wall ms per step, mean per-launch kernel ms from event pairs)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms, float(np.mean(kern)), float(np.min(kern))
+
+
+def _kernel_sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "register_tiled_matrix_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, launches_bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent
+    or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_digest") != _kernel_sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(inp, target_s):
+    """The fp64 oracle, as it stands, on the first R rows of the workload (R sized so the
+    sample takes about target_s seconds); rate in TFLOP/s of the same 2*R*N*K flop count."""
+    import oracle
+
+    def run_rows(r):
+        t0 = time.perf_counter()
+        oracle.gemm(inp.A[:r], inp.B, None, alpha=inp.alpha, beta=0.0)
+        return time.perf_counter() - t0
+
+    r = 16
+    dt = run_rows(r)
+    while dt < 0.5 and r < inp.M:
+        r = min(inp.M, r * 4)
+        dt = run_rows(r)
+    rate = r / dt
+    rows = int(min(inp.M, max(r, rate * target_s)))
+    if rows != r:
+        dt = run_rows(rows)
+    flop = 2.0 * rows * inp.N * inp.K
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {inp.M}x{inp.N}x{inp.K} fp32 workload "
+                      f"({rows}x{inp.N}x{inp.K} fp64 multiply-adds, {dt:.1f} s)",
+            "seconds": dt,
+            "host_cpu": platform.processor() or _cpu_model(),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gemm_inputs as gi
+    import register_tiled_matrix_amd as rt
+    from register_tiled_matrix_amd import accounting as acc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rt.load()  # raises RegtileLibraryMissing when the HIP library is not built
+    dev = torch.device("cuda:0")
+
+    # ---- headline: fp32 register-tiled 4096^3 ----------------------------------------------
+    w = gi.WORKLOADS["f32_4096"]
+    inp = gi.workload_inputs(w)
+    A = torch.from_numpy(inp.A).to(dev)
+    B = torch.from_numpy(inp.B).to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    f32_args = (w.M, w.N, w.K, 1.0, A.data_ptr(), w.K, B.data_ptr(), w.N, 0.0, C.data_ptr(), w.N,
+                stream)
+
+    def step_f32():
+        st = rt.gemm_f32_raw(*f32_args)
+        if st:
+            raise rt.RegtileError(st, rt.strerror(st))
+
+    step_f32()
+    kernel_name = rt.last_kernel()
+    torch.cuda.synchronize()
+    wall_ms, kern_ms, kern_min = _time(torch, step_f32, args.steps, args.warmup)
+    flop = w.flop
+    value = flop / (wall_ms * 1e-3) / 1e12
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    work = acc.GemmWork(w.M, w.N, w.K, 4)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "f32_4096: fp32 GEMM M=N=K=4096, A and B row-major, "
+                               "U[-1,1] seed 1002, alpha=1, beta=0",
+                   "M": w.M, "N": w.N, "K": w.K, "kernel": kernel_name},
+        "percent_of_fp32_vector_peak": round(100 * value / acc.PEAK_FP32_VECTOR_TFLOPS, 2),
+        "percent_of_fp32_nonpacked_ceiling": round(100 * value / acc.PEAK_FP32_NONPACKED_TFLOPS, 2),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": acc.PEAK_FP32_VECTOR_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / acc.PEAK_FP32_VECTOR_TFLOPS, 4),
+            "traffic": _traffic(kernel_name, work.hbm_bytes),
+            "kernel": kernel_name,
+            "kernel_ms_mean": round(kern_ms, 4),
+            "kernel_ms_min": round(kern_min, 4),
+            "flop_per_launch": flop,
+            "nonpacked_fp32_ceiling": acc.PEAK_FP32_NONPACKED_TFLOPS,
+            "frac_of_nonpacked_ceiling": round(achieved / acc.PEAK_FP32_NONPACKED_TFLOPS, 4),
+        },
+    }
+
+    # ---- bf16 MFMA 8192^3 -------------------------------------------------------------------
+    if not args.no_bf16:
+        wb = gi.WORKLOADS["bf16_8192"]
+        ib = gi.workload_inputs(wb)
+        Ab = torch.from_numpy(ib.A.view(np.int16)).to(dev)
+        Bb = torch.from_numpy(ib.B.view(np.int16)).to(dev)
+        Cb = torch.empty((wb.M, wb.N), dtype=torch.float32, device=dev)
+        bf_args = (wb.M, wb.N, wb.K, 1.0, Ab.data_ptr(), wb.K, Bb.data_ptr(), wb.K, 0.0,
+                   Cb.data_ptr(), wb.N, stream)
+
+        def step_bf16():
+            st = rt.gemm_bf16_raw(*bf_args)
+            if st:
+                raise rt.RegtileError(st, rt.strerror(st))
+
+        step_bf16()
+        kname = rt.last_kernel()
+        wms, kms, kmin = _time(torch, step_bf16, args.steps, args.warmup)
+        v = wb.flop / (wms * 1e-3) / 1e12
+        a = wb.flop / (kms * 1e-3) / 1e12
+        out["bf16_8192"] = {
+            "value": round(v, 2), "unit": "TFLOP/s", "ms_per_step": round(wms, 4),
+            "dtype": "bf16 in, f32 accumulate",
+            "workload": "bf16_8192: M=N=K=8192, A row-major, B column-major, N(0,1) -> bf16 "
+                        "seed 1004, fp32 C, alpha=1, beta=0",
+            "percent_of_bf16_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
+            "roofline": {"bound": "mfma", "achieved": round(a, 2), "peak": acc.PEAK_BF16_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(a / acc.PEAK_BF16_MFMA_TFLOPS, 4),
+                         "traffic": _traffic(kname, acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes),
+                         "kernel": kname, "kernel_ms_mean": round(kms, 4),
+                         "kernel_ms_min": round(kmin, 4), "flop_per_launch": wb.flop},
+        }
+        del Ab, Bb, Cb
+
+    # ---- the ladder on the headline workload ------------------------------------------------
+    if not args.no_ladder:
+        ladder = {}
+        for algo, label in ((rt.ALGO_F32_NAIVE, "naive"), (rt.ALGO_F32_LDS, "lds_32x32"),
+                            (rt.ALGO_F32_REGTILE, "regtile_8x8")):
+            def step(algo=algo):
+                st = rt.regtile_gemm_f32_algo(algo, *f32_args)
+                if st:
+                    raise rt.RegtileError(st, rt.strerror(st))
+            reps = 3 if algo != rt.ALGO_F32_REGTILE else args.steps
+            _, kms, _ = _time(torch, step, reps, 1)
+            ladder[label] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
+                             "TFLOP/s": round(flop / (kms * 1e-3) / 1e12, 3)}
+        if "bf16_8192" in out:
+            ladder["mfma_bf16_8192"] = {"kernel": out["bf16_8192"]["roofline"]["kernel"],
+                                        "kernel_ms": out["bf16_8192"]["roofline"]["kernel_ms_mean"],
+                                        "TFLOP/s": out["bf16_8192"]["roofline"]["achieved"]}
+        out["ladder"] = ladder
+
+    # ---- CPU baseline: the oracle on a bounded sample --------------------------------------
+    if not args.no_cpu:
+        out["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+
+    out["device"] = torch.cuda.get_device_name(dev)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,120 @@
+/*
+ * regtile.h -- C ABI of the register-tiled GEMM library (libregtile.so, gfx950 / MI355X).
+ *
+ * The library computes dense
+ *
+ *     C = alpha * A * B + beta * C
+ *
+ * on one GPU with three levels of tiling: a workgroup tile of C staged from HBM into LDS,
+ * and per-thread register micro-tiles of TM x TN accumulators fed by regA/regB fragments
+ * at each k step, so that LDS reads per FMA fall by the micro-tile size.
+ *   - "Understanding Register Tiling" (blog.csdn.net/sweet_ran, "【infra之路】理解 Register
+ *     Tiling"): the shared-memory version (one output per thread), the core idea (a thread
+ *     owns a 4x4 block of C), the key loop (regA[TM], regB[TN], TM*TN register FMAs per k)
+ *     and the three-version comparison (naive -> shared -> register).
+ *   - "寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507), sections 1.1-1.2 (global ->
+ *     shared -> register tiling, 128x128 block with 8x8 micro-tiles), section 3 (AMD CDNA:
+ *     wave64, VGPR/SGPR split, MFMA fragments) and section 6.3 (register prefetch of the
+ *     next k-slice).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout: row-major A (M x K, element (i,k) at A[i*lda + k], lda >= max(1,K)) and row-major
+ *   C (M x N, element (i,j) at C[i*ldc + j], ldc >= max(1,N)). B is row-major K x N for the
+ *   fp32 entry points (B[k*ldb + j], ldb >= max(1,N)) and column-major K x N for the bf16
+ *   entry points (B[j*ldb + k], ldb >= max(1,K)).
+ * Memory: A, B and C are device pointers owned by the caller (any HIP allocation, e.g. a
+ *   PyTorch tensor). The library never allocates, frees or synchronises; it only launches
+ *   kernels on `stream` (a hipStream_t; NULL means the default stream). Calls are
+ *   asynchronous: C is valid once the stream has been synchronised. Aliasing C with A or
+ *   B is not supported.
+ * alpha/beta (BLAS convention; the pages compute C = A*B only):
+ *   beta == 0  -> C is write-only (its prior contents, NaN included, are never read);
+ *   alpha == 0 or K == 0 -> A and B are not read and C = beta * C;
+ *   M == 0 or N == 0 -> nothing is launched.
+ * Return value: REGTILE_OK (0) on success; -i when argument i (1-based position in the
+ *   called function's signature) is invalid -- checked before any HIP call; > 0 is a
+ *   hipError_t from the launch. Errors raised while the kernel runs surface at the caller's
+ *   next synchronisation, as for any HIP launch.
+ * Sizes: M, N, K up to 2^31-1; offsets are computed in 64 bits.
+ */
+#ifndef REGTILE_H
+#define REGTILE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REGTILE_OK 0
+
+/* Kernel ladder for the fp32 entry points ("Understanding Register Tiling", the three-version
+ * comparison: naive -> shared memory -> register tiling). */
+enum regtile_algo_f32 {
+    REGTILE_F32_AUTO = 0,    /* library's choice: the register-tiled kernel */
+    REGTILE_F32_NAIVE = 1,   /* one thread per C element, operands straight from HBM */
+    REGTILE_F32_LDS = 2,     /* 32x32 LDS tiles, 1024 threads, one C element per thread */
+    REGTILE_F32_REGTILE = 3  /* 128x128 LDS tiles, 256 threads, 8x8 register micro-tiles */
+};
+
+/* Kernel ladder for the bf16 entry points. */
+enum regtile_algo_bf16 {
+    REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
+    REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
+    REGTILE_BF16_MFMA = 2    /* LDS-tiled, wave-level MFMA fragments, fp32 accumulators */
+};
+
+/*
+ * gemm_f32 -- fp32 C = alpha*A*B + beta*C with fp32 FMA accumulation, on the register-tiled
+ * kernel ("Understanding Register Tiling", the key loop; "寄存器Tiling跨架构解析" section 1.1).
+ *   M, N, K    (args 1-3)  sizes, >= 0
+ *   alpha      (arg 4)     scale of A*B
+ *   A, lda     (args 5-6)  device, row-major M x K, lda >= max(1,K); may be NULL if M*K == 0
+ *                          or alpha == 0
+ *   B, ldb     (args 7-8)  device, row-major K x N, ldb >= max(1,N); NULL allowed as for A
+ *   beta       (arg 9)     scale of the prior C
+ *   C, ldc     (args 10-11) device, row-major M x N, ldc >= max(1,N); may be NULL if M*N == 0
+ *   stream     (arg 12)    hipStream_t or NULL
+ */
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+             int ldb, float beta, float *C, int ldc, void *stream);
+
+/*
+ * gemm_bf16 -- C = alpha*A*B + beta*C with bf16 operands (raw bit patterns), exact products
+ * and fp32 accumulation on CDNA4 MFMA fragments ("寄存器Tiling跨架构解析" section 3.2: MFMA
+ * fragments held in VGPRs per lane, accumulators updated in place over k).
+ *   A, lda  bf16 row-major M x K (lda >= max(1,K));
+ *   B, ldb  bf16 column-major K x N: element (k,j) at B[j*ldb + k] (ldb >= max(1,K));
+ *   C, ldc  fp32 row-major M x N.
+ * Argument positions and rules as for gemm_f32.
+ */
+int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+              int ldb, float beta, float *C, int ldc, void *stream);
+
+/*
+ * regtile_gemm_f32_algo / regtile_gemm_bf16_algo -- the same operations on an explicit rung of
+ * the kernel ladder (arg 1: a regtile_algo_f32 / regtile_algo_bf16 value; -1 if unknown). The
+ * remaining arguments are those of gemm_f32 / gemm_bf16, shifted by one position.
+ */
+int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const float *A, int lda,
+                          const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A,
+                           int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
+                           void *stream);
+
+/* Name of the kernel the calling thread launched last ("none" before the first launch,
+ * "quick-return" when nothing was launched). Static storage; do not free. */
+const char *regtile_last_kernel(void);
+
+/* Human-readable text for a status code returned by the entry points. Static storage. */
+const char *regtile_strerror(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int regtile_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REGTILE_H */

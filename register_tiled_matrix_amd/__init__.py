@@ -1,0 +1,211 @@
+"""register_tiled_matrix_amd -- register-tiled GEMM for MI355X (gfx950), Python binding.
+
+A thin ctypes binding over the C ABI of ``libregtile.so`` (declared in ``include/regtile.h``).
+It only marshals arguments: every step of the product runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream.
+
+Entry points (same names as the C ABI):
+
+* ``gemm_f32(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_F32_AUTO)``
+  fp32 ``C = alpha*A@B + beta*C``; A (M x K) and B (K x N) row-major fp32 CUDA tensors
+  (row stride may exceed the width), C (M x N) row-major fp32.
+* ``gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO)``
+  bf16 A (M x K, row-major) times bf16 B given as a K x N column-major view (for example
+  ``Bt.t()`` for a contiguous N x K tensor ``Bt``), fp32 C.
+* ``gemm_f32_raw`` / ``gemm_bf16_raw`` take the C arguments verbatim (integers for pointers).
+* ``last_kernel()``, ``strerror(status)``, ``version()``.
+
+The library must be built (``python -m register_tiled_matrix_amd.build``); importing this
+package does not build it, and every call raises ``RegtileLibraryMissing`` when it is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "ALGO_F32_AUTO", "ALGO_F32_NAIVE", "ALGO_F32_LDS", "ALGO_F32_REGTILE",
+    "ALGO_BF16_AUTO", "ALGO_BF16_NAIVE", "ALGO_BF16_MFMA",
+    "RegtileError", "RegtileLibraryMissing", "lib_path", "load",
+    "gemm_f32", "gemm_bf16", "gemm_f32_raw", "gemm_bf16_raw",
+    "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo",
+    "last_kernel", "strerror", "version", "EXPORTED_SYMBOLS",
+]
+
+ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE = 0, 1, 2, 3
+ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA = 0, 1, 2
+
+EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo",
+                    "regtile_last_kernel", "regtile_strerror", "regtile_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libregtile.so")
+_lib = None
+_lock = threading.Lock()
+
+
+class RegtileError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"regtile status {status}: {message}")
+        self.status = status
+
+
+class RegtileLibraryMissing(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libregtile.so (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RegtileLibraryMissing(
+                f"{_LIB_PATH} is not built; run `python -m register_tiled_matrix_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        I, F, P = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        gemm = [I, I, I, F, P, I, P, I, F, P, I, P]
+        for name, args in (("gemm_f32", gemm), ("gemm_bf16", gemm),
+                           ("regtile_gemm_f32_algo", [I] + gemm),
+                           ("regtile_gemm_bf16_algo", [I] + gemm)):
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = I
+        lib.regtile_last_kernel.argtypes = []
+        lib.regtile_last_kernel.restype = ctypes.c_char_p
+        lib.regtile_strerror.argtypes = [I]
+        lib.regtile_strerror.restype = ctypes.c_char_p
+        lib.regtile_version.argtypes = []
+        lib.regtile_version.restype = I
+        _lib = lib
+        return lib
+
+
+def last_kernel() -> str:
+    return load().regtile_last_kernel().decode()
+
+
+def strerror(status: int) -> str:
+    return load().regtile_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().regtile_version())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RegtileError(status, strerror(status))
+
+
+# ---- raw entry points: the C arguments verbatim -------------------------------------------
+def gemm_f32_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_bf16_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_bf16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def regtile_gemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().regtile_gemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                        stream)
+
+
+def regtile_gemm_bf16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().regtile_gemm_bf16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                         stream)
+
+
+# ---- tensor entry points -------------------------------------------------------------------
+def _stream_handle(t, stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _row_major_ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} rows overlap (row stride below the width)")
+    return max(int(t.stride(0)), int(t.shape[1]), 1)
+
+
+def _col_major_ld(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[0] > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be column-major (unit row stride), e.g. Bt.t()")
+    if t.shape[1] > 1 and t.stride(1) < t.shape[0]:
+        raise ValueError(f"{name} columns overlap (column stride below the height)")
+    return max(int(t.stride(1)), int(t.shape[0]), 1)
+
+
+def _out(C, M, N, like):
+    import torch
+
+    if C is None:
+        return torch.empty((M, N), dtype=torch.float32, device=like.device)
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be float32 of shape {(M, N)}")
+    return C
+
+
+def gemm_f32(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_F32_AUTO, stream=None):
+    """C = alpha*A@B + beta*C on fp32 CUDA tensors; returns C (allocated when None)."""
+    import torch
+
+    if A.dtype != torch.float32 or B.dtype != torch.float32:
+        raise ValueError("gemm_f32 takes float32 A and B")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("gemm_f32 takes device tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if C is None and beta != 0.0:
+        raise ValueError("beta != 0 needs C")
+    C = _out(C, M, N, A)
+    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(C, "C")
+    st = regtile_gemm_f32_algo(int(algo), M, N, K, float(alpha), A.data_ptr(), lda,
+                               B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
+                               _stream_handle(A, stream))
+    _check(st)
+    return C
+
+
+def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
+    """C = alpha*A@B + beta*C; A bf16 (M x K) row-major, B bf16 (K x N) column-major view,
+    C fp32 (M x N) row-major; returns C (allocated when None)."""
+    import torch
+
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("gemm_bf16 takes bfloat16 A and B")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("gemm_bf16 takes device tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if C is None and beta != 0.0:
+        raise ValueError("beta != 0 needs C")
+    C = _out(C, M, N, A)
+    lda, ldb, ldc = _row_major_ld(A, "A"), _col_major_ld(B, "B"), _row_major_ld(C, "C")
+    st = regtile_gemm_bf16_algo(int(algo), M, N, K, float(alpha), A.data_ptr(), lda,
+                                B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
+                                _stream_handle(A, stream))
+    _check(st)
+    return C

@@ -1,0 +1,217 @@
+// gemm_bf16_mfma.hip -- rung 3 of the ladder: bf16 x bf16 -> fp32 on CDNA4 MFMA fragments.
+//
+// The register tile of this rung is the MFMA fragment rather than a per-thread SIMT block
+// ("寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507) section 3: on CDNA the A, B and C
+// fragments live in per-lane VGPRs while addresses and strides sit in SGPRs; section 3.1: the
+// instruction shape sets per-lane register counts; section 3.2: each k step loads A and B
+// fragments from LDS and accumulates C in place). On gfx950 (wave64) the instruction is
+// v_mfma_f32_32x32x16_bf16: per lane 8 bf16 of A, 8 bf16 of B (one 16-byte LDS read each)
+// and 16 fp32 accumulators; a 32x32 C block per instruction.
+//
+// Operands are K-contiguous on both sides (A row-major, B column-major), so A and B slabs
+// share one LDS layout: a tile row (an A row, or a B column) is BK = 64 bf16 = 8 chunks of
+// 16 bytes, and chunk c of row r is stored at slot c ^ (r & 7). A fragment read (lanes 0..31
+// = 32 consecutive rows, same chunk) then spreads every 8 consecutive lanes over 8 distinct
+// slots = 128 bytes = all 32 banks, so the reads are free of bank conflicts, and the
+// cooperative 16-byte stores (8 lanes per row) are too.
+//
+// Pipeline: two LDS stages; the next slab's global loads (16-byte, coalesced: 8 lanes cover
+// one 128-byte row segment) are issued into registers before the current slab's MFMAs and
+// stored to the other stage after them, one barrier per slab (section 6.3's prefetch).
+// Tile order: workgroups are renumbered so each XCD gets a contiguous block of tiles, walked
+// in groups of 8 tile-rows (L2 reuse of A rows and B columns inside an XCD).
+#include "regtile_internal.h"
+
+namespace regtile {
+
+namespace {
+
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int BK = 64;   // bf16 per slab row
+constexpr int KCH = 8;   // 16-byte chunks per slab row
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * KCH + (chunk ^ (row & 7)); }
+
+template <bool EDGE, bool VEC>
+__device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool row_ok,
+                                            int k_left) {
+    // 8 consecutive bf16 starting at p (k index k0); k_left = K - k0.
+    if (!EDGE) {
+        if (VEC) return *reinterpret_cast<const uint4 *>(p);
+    }
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0;
+    if (!EDGE || row_ok) {
+        if (VEC && (!EDGE || k_left >= 8)) {
+            return *reinterpret_cast<const uint4 *>(p);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!EDGE || e < k_left) v[e] = p[e];
+    }
+    uint4 r;
+    r.x = v[0] | ((uint32_t)v[1] << 16);
+    r.y = v[2] | ((uint32_t)v[3] << 16);
+    r.z = v[4] | ((uint32_t)v[5] << 16);
+    r.w = v[6] | ((uint32_t)v[7] << 16);
+    return r;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VEC_C>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
+    int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
+    const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n) {
+    constexpr int NT = WAVES_M * WAVES_N * 64;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int MI = WTM / 32, NI = WTN / 32;
+    constexpr int A_CH = BM * KCH / NT;  // 16-byte chunks per thread per slab
+    constexpr int B_CH = BN * KCH / NT;
+    constexpr int ROWS_PER_PASS = NT / KCH;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert((BM * KCH) % NT == 0 && (BN * KCH) % NT == 0, "slab must split evenly");
+
+    __shared__ uint4 sA[2][BM * KCH];
+    __shared__ uint4 sB[2][BN * KCH];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    int tm, tn;
+    grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Staging assignment: thread t owns chunk (t % KCH) of rows t / KCH + ROWS_PER_PASS * i.
+    const int ld_chunk = tid % KCH;
+    const int ld_row = tid / KCH;
+    const uint16_t *a_src = A + (int64_t)(m0 + ld_row) * lda + ld_chunk * 8;
+    const uint16_t *b_src = B + (int64_t)(n0 + ld_row) * ldb + ld_chunk * 8;
+    const int64_t a_pass = (int64_t)ROWS_PER_PASS * lda;
+    const int64_t b_pass = (int64_t)ROWS_PER_PASS * ldb;
+
+    uint4 ra[A_CH], rb[B_CH];
+    auto load_slab = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i)
+            ra[i] = load_chunk<EDGE, VEC>(a_src + i * a_pass + k0,
+                                          m0 + ld_row + i * ROWS_PER_PASS < M,
+                                          K - k0 - ld_chunk * 8);
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i)
+            rb[i] = load_chunk<EDGE, VEC>(b_src + i * b_pass + k0,
+                                          n0 + ld_row + i * ROWS_PER_PASS < N,
+                                          K - k0 - ld_chunk * 8);
+    };
+    auto store_slab = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) sA[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) sB[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = rb[i];
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // Fragment rows of this lane: A rows wm*WTM + i*32 + (lane & 31); B columns likewise.
+    const int frag_r = lane & 31;
+    const int frag_kh = lane >> 5;  // which 8-wide half of each 16-wide k step
+
+    auto compute_slab = [&](int buf) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int chunk = kk * 2 + frag_kh;
+            bf16x8 fa[MI], fb[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                fa[i] = __builtin_bit_cast(bf16x8, sA[buf][swz(wm * WTM + i * 32 + frag_r, chunk)]);
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                fb[j] = __builtin_bit_cast(bf16x8, sB[buf][swz(wn * WTN + j * 32 + frag_r, chunk)]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Software pipeline with the last slab peeled (the steady-state body is one basic
+    // block): global loads of slab s+1, MFMAs on slab s, LDS stores of slab s+1, barrier.
+    const int nslabs = (K + BK - 1) / BK;
+    if (nslabs > 0) {
+        load_slab(0);
+        store_slab(0);
+        __syncthreads();
+        for (int s = 0; s + 1 < nslabs; ++s) {
+            load_slab((s + 1) * BK);
+            compute_slab(s & 1);
+            store_slab((s + 1) & 1);
+            __syncthreads();
+        }
+        compute_slab((nslabs - 1) & 1);
+    }
+
+    // Epilogue. Accumulator v of lane l in a 32x32 block holds
+    // row (v / 4) * 8 + (l / 32) * 4 + (v % 4), column l % 32.
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + frag_kh * 4 + (v & 3);
+                if (EDGE && (row >= M || col >= N)) continue;
+                float *c = C + (int64_t)row * ldc + col;
+                *c = epilogue_value(acc[i][j][v], alpha, beta, c);
+            }
+        }
+    }
+    (void)VEC_C;
+}
+
+template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC>
+hipError_t launch_cfg(const Problem &p, hipStream_t s) {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false>),
+                       dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
+                       (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,
+                       p.ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name) {
+    const bool vec = (p.lda % 8) == 0 && (p.ldb % 8) == 0 && aligned16(p.A) && aligned16(p.B);
+    const bool big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
+    if (big) {
+        const bool edge = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % BK) != 0;
+        *name = edge ? (vec ? "bf16_mfma_256x256x64_w2x4_edge_vec" : "bf16_mfma_256x256x64_w2x4_edge")
+                     : (vec ? "bf16_mfma_256x256x64_w2x4_vec" : "bf16_mfma_256x256x64_w2x4");
+        if (edge) return vec ? launch_cfg<256, 256, 2, 4, true, true>(p, s)
+                             : launch_cfg<256, 256, 2, 4, true, false>(p, s);
+        return vec ? launch_cfg<256, 256, 2, 4, false, true>(p, s)
+                   : launch_cfg<256, 256, 2, 4, false, false>(p, s);
+    }
+    const bool edge = (p.M % 128) != 0 || (p.N % 128) != 0 || (p.K % BK) != 0;
+    *name = edge ? (vec ? "bf16_mfma_128x128x64_w2x2_edge_vec" : "bf16_mfma_128x128x64_w2x2_edge")
+                 : (vec ? "bf16_mfma_128x128x64_w2x2_vec" : "bf16_mfma_128x128x64_w2x2");
+    if (edge) return vec ? launch_cfg<128, 128, 2, 2, true, true>(p, s)
+                         : launch_cfg<128, 128, 2, 2, true, false>(p, s);
+    return vec ? launch_cfg<128, 128, 2, 2, false, true>(p, s)
+               : launch_cfg<128, 128, 2, 2, false, false>(p, s);
+}
+
+}  // namespace regtile

@@ -1,0 +1,273 @@
+// gemm_f32_regtile.hip -- rung 2 of the ladder: the fp32 register-tiled SIMT kernel.
+//
+// Three-level tiling ("寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507) section 1.1: a
+// 128x128 block tile per workgroup of 256 threads, an 8x8 micro-tile per thread, 64 FMAs per
+// k step held entirely in registers):
+//   HBM -> LDS      a BM x BK slab of A (stored k-major, i.e. transposed) and a BK x BN slab
+//                   of B per stage, two stages (the next slab's global loads are in flight
+//                   while the current slab is consumed; section 6.3's prefetch, done here
+//                   as double-buffered LDS plus register staging);
+//   LDS -> VGPR     per k: regA[8] (two 16-byte reads of a column of the A slab) and
+//                   regB[8] (two 16-byte reads of a row of the B slab) -- "Understanding
+//                   Register Tiling" (blog.csdn.net/sweet_ran), the key loop;
+//   VGPR FMA        acc[8][8] += regA[m] * regB[n]: 64 independent fp32 FMAs per k.
+// LDS reads per FMA: (TM + TN) / (TM * TN) = 16 / 64 = 0.25 floats, against 2 for the
+// one-output-per-thread kernel (the three-version comparison on the same page).
+//
+// Wave64 mapping. The 256 threads are 4 waves in a 2x2 grid; each wave owns a 64x64 quarter
+// and its 64 lanes form an 8x8 grid. A lane's 8 rows are {r0..r0+3, r0+32..r0+35} and its 8
+// columns {c0..c0+3, c0+32..c0+35}: the 4+4 split makes the 8 distinct 16-byte fragment
+// addresses of one wave-wide read a single contiguous 128-byte run (all 32 banks once, the
+// rest broadcasts), so fragment reads are free of bank conflicts (section 1.2/7.3 of the
+// same page: the register layout decides the LDS access pattern).
+//
+// Every output accumulates fmaf over k in natural order, like rungs 0 and 1, so the three
+// fp32 rungs agree bitwise.
+#include "regtile_internal.h"
+
+namespace regtile {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, TM = 8, TN = 8, NT = 256;
+#ifndef F32_WAVES_PER_EU
+#define F32_WAVES_PER_EU 3
+#endif
+constexpr int APAD = 4;  // A slab row stride BM + 4 floats: transposed stores hit 32 banks per half-wave
+
+template <int BK>
+struct alignas(16) Smem {
+    float a[2][BK][BM + APAD];
+    float b[2][BK][BN];
+};
+
+// Global -> register staging of one slab. A: BM x BK as BK/4 float4 chunks per row;
+// B: BK x BN as BN/4 float4 chunks per row. Each thread owns BK/8 chunks of each.
+template <int BK, bool EDGE, bool VEC>
+__device__ __forceinline__ float4 load4_rowwise(const float *__restrict__ p, int rows_left,
+                                                int cols_left) {
+    // p points at element (row, col) of a row-major matrix; rows_left = rows remaining from
+    // this row (> 0 means in range), cols_left = columns remaining from col.
+    if (!EDGE) {
+        if (VEC) return *reinterpret_cast<const float4 *>(p);
+        return make_float4(p[0], p[1], p[2], p[3]);
+    }
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rows_left > 0) {
+        if (VEC && cols_left >= 4) {
+            v = *reinterpret_cast<const float4 *>(p);
+        } else {
+            if (cols_left > 0) v.x = p[0];
+            if (cols_left > 1) v.y = p[1];
+            if (cols_left > 2) v.z = p[2];
+            if (cols_left > 3) v.w = p[3];
+        }
+    }
+    return v;
+}
+
+template <int BK, bool EDGE, bool VEC_A, bool VEC_B, bool VEC_C>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PER_EU, F32_WAVES_PER_EU))) void f32_regtile_kernel(int M, int N, int K, float alpha,
+                                                         const float *__restrict__ A, int64_t lda,
+                                                         const float *__restrict__ B, int64_t ldb,
+                                                         float beta, float *__restrict__ C,
+                                                         int64_t ldc, int tiles_m, int tiles_n) {
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    constexpr int CH = BK / 8;        // float4 chunks per thread per operand per slab
+    constexpr int A_CPR = BK / 4;     // A chunks per tile row
+    __shared__ Smem<BK> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r0 = (wave >> 1) * 64 + (lane >> 3) * 4;
+    const int c0 = (wave & 1) * 64 + (lane & 7) * 4;
+
+    int tm, tn;
+    grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // This thread's staging chunks: A chunk q = tid + NT*i -> (row q / A_CPR, k (q % A_CPR)*4);
+    // B chunk q -> (k q / 32, col (q % 32)*4).
+    int a_row[CH], a_k[CH], b_k[CH], b_col[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int q = tid + NT * i;
+        a_row[i] = q / A_CPR;
+        a_k[i] = (q % A_CPR) * 4;
+        b_k[i] = q / 32;
+        b_col[i] = (q % 32) * 4;
+    }
+    const float *a_ptr[CH];
+    const float *b_ptr[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        a_ptr[i] = A + (int64_t)(m0 + a_row[i]) * lda + a_k[i];
+        b_ptr[i] = B + (int64_t)b_k[i] * ldb + n0 + b_col[i];
+    }
+
+    float4 ra[CH], rb[CH];
+    auto load_slab = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            ra[i] = load4_rowwise<BK, EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_row[i]),
+                                                   K - (k0 + a_k[i]));
+            rb[i] = load4_rowwise<BK, EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
+                                                   K - (k0 + b_k[i]), N - (n0 + b_col[i]));
+        }
+    };
+    auto store_slab = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            sm.a[buf][a_k[i] + 0][a_row[i]] = ra[i].x;
+            sm.a[buf][a_k[i] + 1][a_row[i]] = ra[i].y;
+            sm.a[buf][a_k[i] + 2][a_row[i]] = ra[i].z;
+            sm.a[buf][a_k[i] + 3][a_row[i]] = ra[i].w;
+            *reinterpret_cast<float4 *>(&sm.b[buf][b_k[i]][b_col[i]]) = rb[i];
+        }
+    };
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[m][n] = 0.0f;
+
+    // One slab of the register-tile update from LDS stage `buf`.
+    auto compute_slab = [&](int buf) {
+        const float *sa = &sm.a[buf][0][0] + r0;
+        const float *sb = &sm.b[buf][0][0] + c0;
+        // Fragment double buffer: the reads for step k+1 are issued before the 64 FMAs of
+        // step k. The scheduling barrier keeps the compiler from hoisting the whole slab's
+        // reads (which would need BK*16 live registers and spill).
+        float4 fa[2][2], fb[2][2];
+        fa[0][0] = *reinterpret_cast<const float4 *>(sa);
+        fa[0][1] = *reinterpret_cast<const float4 *>(sa + 32);
+        fb[0][0] = *reinterpret_cast<const float4 *>(sb);
+        fb[0][1] = *reinterpret_cast<const float4 *>(sb + 32);
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            const int cb = k & 1, nb = cb ^ 1;
+            if (k + 1 < BK) {
+                fa[nb][0] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD));
+                fa[nb][1] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD) + 32);
+                fb[nb][0] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN);
+                fb[nb][1] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN + 32);
+            }
+            const float ra_[TM] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
+                                   fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
+            const float rb_[TN] = {fb[cb][0].x, fb[cb][0].y, fb[cb][0].z, fb[cb][0].w,
+                                   fb[cb][1].x, fb[cb][1].y, fb[cb][1].z, fb[cb][1].w};
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int n = 0; n < TN; ++n) acc[m][n] = fmaf(ra_[m], rb_[n], acc[m][n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Software pipeline, last slab peeled so the steady-state body is one basic block:
+    // issue the global loads of slab s+1, consume slab s from LDS, store slab s+1 to the
+    // other stage, one barrier.
+    const int nslabs = (K + BK - 1) / BK;
+    if (nslabs > 0) {
+        load_slab(0);
+        store_slab(0);
+        __syncthreads();
+        for (int s = 0; s + 1 < nslabs; ++s) {
+            load_slab((s + 1) * BK);
+            compute_slab(s & 1);
+            store_slab((s + 1) & 1);
+            __syncthreads();
+        }
+        compute_slab((nslabs - 1) & 1);
+    }
+
+    // Epilogue: rows r0+{0..3}, r0+32+{0..3}; columns c0+{0..3}, c0+32+{0..3}.
+#pragma unroll
+    for (int m = 0; m < TM; ++m) {
+        const int row = m0 + r0 + (m < 4 ? m : 28 + m);
+        if (EDGE && row >= M) continue;
+        float *crow = C + (int64_t)row * ldc;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = n0 + c0 + h * 32;
+            float *c = crow + col;
+            if (VEC_C && (!EDGE || col + 3 < N)) {
+                float4 v;
+                if (beta == 0.0f) {
+                    v = make_float4(alpha * acc[m][4 * h + 0], alpha * acc[m][4 * h + 1],
+                                    alpha * acc[m][4 * h + 2], alpha * acc[m][4 * h + 3]);
+                } else {
+                    const float4 old = *reinterpret_cast<const float4 *>(c);
+                    v = make_float4(fmaf(alpha, acc[m][4 * h + 0], beta * old.x),
+                                    fmaf(alpha, acc[m][4 * h + 1], beta * old.y),
+                                    fmaf(alpha, acc[m][4 * h + 2], beta * old.z),
+                                    fmaf(alpha, acc[m][4 * h + 3], beta * old.w));
+                }
+                *reinterpret_cast<float4 *>(c) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!EDGE || col + e < N) c[e] = epilogue_value(acc[m][4 * h + e], alpha, beta, c + e);
+            }
+        }
+    }
+}
+
+constexpr int kBK = 16;
+
+template <bool EDGE, bool VA, bool VB, bool VC>
+hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tiles_n) {
+    hipLaunchKernelGGL((f32_regtile_kernel<kBK, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
+                       dim3(NT), 0, s, p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda,
+                       (const float *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <bool EDGE, bool VA, bool VB>
+hipError_t pick_c(const Problem &p, hipStream_t s, int tm, int tn, bool vc) {
+    return vc ? launch_variant<EDGE, VA, VB, true>(p, s, tm, tn)
+              : launch_variant<EDGE, VA, VB, false>(p, s, tm, tn);
+}
+template <bool EDGE, bool VA>
+hipError_t pick_b(const Problem &p, hipStream_t s, int tm, int tn, bool vb, bool vc) {
+    return vb ? pick_c<EDGE, VA, true>(p, s, tm, tn, vc) : pick_c<EDGE, VA, false>(p, s, tm, tn, vc);
+}
+template <bool EDGE>
+hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, bool va, bool vb, bool vc) {
+    return va ? pick_b<EDGE, true>(p, s, tm, tn, vb, vc) : pick_b<EDGE, false>(p, s, tm, tn, vb, vc);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name) {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const bool edge = (p.M % BM) != 0 || (p.N % BN) != 0 || (p.K % kBK) != 0;
+    const bool va = (p.lda % 4) == 0 && aligned16(p.A);
+    const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
+    const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
+    struct Names {
+        char text[16][64];
+        const char *at[2][2][2][2];
+        Names() {
+            int n = 0;
+            for (int e = 0; e < 2; ++e)
+                for (int a = 0; a < 2; ++a)
+                    for (int b = 0; b < 2; ++b)
+                        for (int c = 0; c < 2; ++c) {
+                            snprintf(text[n], sizeof text[n], "f32_regtile_128x128x%d_8x8%s%s%s%s",
+                                     kBK, e ? "_edge" : "", a ? "_va" : "", b ? "_vb" : "",
+                                     c ? "_vc" : "");
+                            at[e][a][b][c] = text[n++];
+                        }
+        }
+    };
+    static const Names names;  // thread-safe one-time initialisation
+    *name = names.at[edge][va][vb][vc];
+    return edge ? pick_a<true>(p, s, tiles_m, tiles_n, va, vb, vc)
+                : pick_a<false>(p, s, tiles_m, tiles_n, va, vb, vc);
+}
+
+}  // namespace regtile

@@ -1,0 +1,135 @@
+// gemm_simple.hip -- the lower rungs of the kernel ladder and the scale-only kernel.
+//
+// Rung 0 (naive) and rung 1 (LDS-tiled) follow the first two versions compared in
+// "Understanding Register Tiling" (blog.csdn.net/sweet_ran), section comparing the three
+// versions: the naive kernel reads both operands from global memory for every product (2N
+// global reads per output), the shared-memory kernel stages 32x32 tiles and still reads
+// 32 + 32 = 64 values from LDS per output per tile pass (opening section).
+// All rungs accumulate each output with fmaf over k in natural order, so for the same
+// inputs they produce bitwise identical results.
+#include "regtile_internal.h"
+
+namespace regtile {
+
+// ---------------------------------------------------------------------------------------
+// C = beta * C (alpha == 0 or K == 0). beta == 0 writes zeros without reading C.
+__global__ __launch_bounds__(256) void scale_c_kernel(int M, int N, float beta, float *C,
+                                                      int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e / N, j = e - i * N;
+        float *c = C + i * ldc + j;
+        *c = beta == 0.0f ? 0.0f : beta * (*c);
+    }
+}
+
+hipError_t launch_scale_c(const Problem &p, hipStream_t s, const char **name) {
+    const int64_t total = (int64_t)p.M * p.N;
+    const int64_t blocks = (total + 255) / 256;
+    const int grid = (int)(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(scale_c_kernel, dim3(grid), dim3(256), 0, s, p.M, p.N, p.beta, p.C, p.ldc);
+    *name = "scale_c";
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Rung 0: one thread per output. A workgroup is 4 rows x 64 columns, so each wave64 covers
+// 64 consecutive columns of one row: its B reads are one 256-byte run and its A read is a
+// broadcast.
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T *p);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p) {
+    return __uint_as_float(((uint32_t)(*p)) << 16);
+}
+
+template <typename T, bool B_COL_MAJOR>
+__global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float alpha,
+                                                    const T *__restrict__ A, int64_t lda,
+                                                    const T *__restrict__ B, int64_t ldb,
+                                                    float beta, float *__restrict__ C,
+                                                    int64_t ldc) {
+    const int col = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (row >= M || col >= N) return;
+    const T *a = A + (int64_t)row * lda;
+    float acc = 0.0f;
+    if (B_COL_MAJOR) {
+        const T *b = B + (int64_t)col * ldb;
+        for (int k = 0; k < K; ++k) acc = fmaf(load_as_f32(a + k), load_as_f32(b + k), acc);
+    } else {
+        const T *b = B + col;
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(load_as_f32(a + k), load_as_f32(b + (int64_t)k * ldb), acc);
+    }
+    float *c = C + (int64_t)row * ldc + col;
+    *c = epilogue_value(acc, alpha, beta, c);
+}
+
+hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name) {
+    dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
+    hipLaunchKernelGGL((naive_kernel<float, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                       p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb, p.beta,
+                       p.C, p.ldc);
+    *name = "f32_naive";
+    return hipGetLastError();
+}
+
+hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name) {
+    dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
+    hipLaunchKernelGGL((naive_kernel<uint16_t, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                       p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
+                       p.beta, p.C, p.ldc);
+    *name = "bf16_naive";
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Rung 1: 32x32 tiles in LDS, 1024 threads (16 waves), one output per thread. Each k step
+// reads sA[ty][k] (a broadcast within a 32-lane row) and sB[k][tx]. sA rows are padded to
+// 33 floats so that the two rows one wave64 touches fall in different banks.
+constexpr int LDS_TILE = 32;
+
+__global__ __launch_bounds__(1024) void f32_lds_kernel(int M, int N, int K, float alpha,
+                                                       const float *__restrict__ A, int64_t lda,
+                                                       const float *__restrict__ B, int64_t ldb,
+                                                       float beta, float *__restrict__ C,
+                                                       int64_t ldc) {
+    __shared__ float sA[LDS_TILE][LDS_TILE + 1];
+    __shared__ float sB[LDS_TILE][LDS_TILE];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const int row = blockIdx.y * LDS_TILE + ty;
+    const int col = blockIdx.x * LDS_TILE + tx;
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += LDS_TILE) {
+        sA[ty][tx] = (row < M && k0 + tx < K) ? A[(int64_t)row * lda + k0 + tx] : 0.0f;
+        sB[ty][tx] = (k0 + ty < K && col < N) ? B[(int64_t)(k0 + ty) * ldb + col] : 0.0f;
+        __syncthreads();
+        const int kn = min(LDS_TILE, K - k0);
+        if (kn == LDS_TILE) {
+#pragma unroll
+            for (int k = 0; k < LDS_TILE; ++k) acc = fmaf(sA[ty][k], sB[k][tx], acc);
+        } else {
+            for (int k = 0; k < kn; ++k) acc = fmaf(sA[ty][k], sB[k][tx], acc);
+        }
+        __syncthreads();
+    }
+    if (row < M && col < N) {
+        float *c = C + (int64_t)row * ldc + col;
+        *c = epilogue_value(acc, alpha, beta, c);
+    }
+}
+
+hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name) {
+    dim3 grid((p.N + LDS_TILE - 1) / LDS_TILE, (p.M + LDS_TILE - 1) / LDS_TILE);
+    hipLaunchKernelGGL(f32_lds_kernel, grid, dim3(LDS_TILE * LDS_TILE), 0, s, p.M, p.N, p.K,
+                       p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb, p.beta,
+                       p.C, p.ldc);
+    *name = "f32_lds_32x32";
+    return hipGetLastError();
+}
+
+}  // namespace regtile

@@ -1,0 +1,146 @@
+// regtile_api.hip -- the C ABI declared in include/regtile.h: argument validation (before any
+// HIP call), the BLAS quick returns, the kernel-ladder selector and launch on the caller's
+// stream. The library never allocates, frees or synchronises.
+#include "regtile.h"
+
+#include <math.h>
+
+#include "regtile_internal.h"
+
+namespace {
+
+thread_local const char *g_last_kernel = "none";
+
+// LAPACK-style validation. `shift` is 1 for the *_algo entry points (their first argument is
+// the algorithm), so the returned -i always names the position in the called function.
+// b_col_major selects the ldb rule (>= K instead of >= N).
+int validate(int shift, int M, int N, int K, float alpha, const void *A, int lda, const void *B,
+             int ldb, float *C, int ldc, bool b_col_major) {
+    if (M < 0) return -(1 + shift);
+    if (N < 0) return -(2 + shift);
+    if (K < 0) return -(3 + shift);
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    if (reads_ab && A == nullptr) return -(5 + shift);
+    if (lda < (K > 1 ? K : 1)) return -(6 + shift);
+    if (reads_ab && B == nullptr) return -(7 + shift);
+    const int ldb_min = b_col_major ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
+    if (ldb < ldb_min) return -(8 + shift);
+    if (M > 0 && N > 0 && C == nullptr) return -(10 + shift);
+    if (ldc < (N > 1 ? N : 1)) return -(11 + shift);
+    return REGTILE_OK;
+}
+
+int finish(hipError_t err, const char *name) {
+    g_last_kernel = name;
+    return err == hipSuccess ? REGTILE_OK : (int)err;
+}
+
+regtile::Problem make_problem(int M, int N, int K, float alpha, const void *A, int lda,
+                              const void *B, int ldb, float beta, float *C, int ldc) {
+    regtile::Problem p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    p.C = C;
+    p.ldc = ldc;
+    return p;
+}
+
+// Quick returns shared by both element types. Returns true when the call is complete.
+bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
+    if (p.M == 0 || p.N == 0) {
+        g_last_kernel = "quick-return";
+        *status = REGTILE_OK;
+        return true;
+    }
+    if (p.K == 0 || p.alpha == 0.0f) {
+        const char *name = "scale_c";
+        *status = finish(regtile::launch_scale_c(p, s, &name), name);
+        return true;
+    }
+    return false;
+}
+
+int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *A, int lda,
+            const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    if (algo < REGTILE_F32_AUTO || algo > REGTILE_F32_REGTILE) return -1;
+    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, false);
+    if (v != REGTILE_OK) return v;
+    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int status;
+    if (quick_return(p, s, &status)) return status;
+    const char *name = "none";
+    hipError_t err;
+    switch (algo) {
+        case REGTILE_F32_NAIVE: err = regtile::launch_f32_naive(p, s, &name); break;
+        case REGTILE_F32_LDS: err = regtile::launch_f32_lds(p, s, &name); break;
+        default: err = regtile::launch_f32_regtile(p, s, &name); break;
+    }
+    return finish(err, name);
+}
+
+int run_bf16(int shift, int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+             const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA) return -1;
+    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    if (v != REGTILE_OK) return v;
+    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int status;
+    if (quick_return(p, s, &status)) return status;
+    const char *name = "none";
+    hipError_t err;
+    switch (algo) {
+        case REGTILE_BF16_NAIVE: err = regtile::launch_bf16_naive(p, s, &name); break;
+        default: err = regtile::launch_bf16_mfma(p, s, &name); break;
+    }
+    return finish(err, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream) {
+    return run_f32(0, REGTILE_F32_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+              int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_bf16(0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const float *A, int lda,
+                          const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_f32(1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A,
+                           int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
+                           void *stream) {
+    return run_bf16(1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+const char *regtile_last_kernel(void) { return g_last_kernel; }
+
+const char *regtile_strerror(int status) {
+    if (status == REGTILE_OK) return "success";
+    if (status < 0) {
+        static thread_local char buf[96];
+        snprintf(buf, sizeof buf, "invalid argument at position %d", -status);
+        return buf;
+    }
+    return hipGetErrorString(static_cast<hipError_t>(status));
+}
+
+int regtile_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// regtile_internal.h -- internal interface between the C-ABI front end (regtile_api.hip) and
+// the kernel translation units. Not installed; the public interface is include/regtile.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace regtile {
+
+// One validated GEMM problem. Leading dimensions are widened to 64 bits so every offset
+// computed from them is 64-bit.
+struct Problem {
+    int M, N, K;
+    float alpha, beta;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    float *C;
+    int64_t ldc;
+};
+
+// A launch reports the kernel it chose through `name` (static storage).
+hipError_t launch_scale_c(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name);
+
+// C element update shared by every kernel's epilogue: beta == 0 never reads C.
+__device__ __forceinline__ float epilogue_value(float acc, float alpha, float beta,
+                                                const float *c) {
+    return beta == 0.0f ? alpha * acc : fmaf(alpha, acc, beta * (*c));
+}
+
+// The hardware hands out workgroup ids round-robin over the 8 XCDs (id % 8). Renumber so
+// that each XCD receives a contiguous run of logical tile ids (neighbouring tiles share A
+// rows / B columns in that XCD's L2). Identity when the count is not a multiple of 8.
+__device__ __forceinline__ int xcd_contiguous_id(int hw_id, int count) {
+    if ((count & 7) != 0) return hw_id;
+    return (hw_id & 7) * (count >> 3) + (hw_id >> 3);
+}
+
+// Grouped tile order: walk GROUP_M tile-rows at a time, column by column, so consecutive
+// logical ids reuse the same B column panel and a small set of A row panels.
+template <int GROUP_M>
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int per_group = GROUP_M * tiles_n;
+    const int group = id / per_group;
+    const int first_m = group * GROUP_M;
+    const int rows = min(tiles_m - first_m, GROUP_M);
+    const int in_group = id - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+}  // namespace regtile

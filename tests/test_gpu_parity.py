@@ -1,0 +1,244 @@
+"""GPU parity of the HIP library against the fp64 CPU oracle, through the C ABI.
+
+Bar: every compared element satisfies |C_gpu - C_ref| <= 1e-5 * (|alpha| sum_k |a_ik b_kj|
++ |beta c_ij|) (oracle.check), and integer-valued inputs, whose every partial sum is exact
+in fp32, must match bitwise. Small and ragged problems are compared in full; the full-size
+workloads run in the launch configuration the benchmark times and are compared on a
+stratified sample the oracle computes entry by entry.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+import register_tiled_matrix_amd as rt
+from gpu_util import announce, assert_parity_full, assert_parity_sampled, device_operands, run
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS, rt.ALGO_F32_REGTILE, rt.ALGO_F32_AUTO]
+BF16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_AUTO]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rt.load()
+    yield
+
+
+# ---- the five workloads ----------------------------------------------------------------
+@pytest.mark.parametrize("algo", F32_ALGOS)
+def test_f32_256_full(algo):
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_256"])
+    announce(f"f32_256 algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    assert_parity_full(inp, got, f"f32_256 algo {algo} ({rt.last_kernel()})")
+
+
+@pytest.mark.parametrize("algo", F32_ALGOS)
+def test_f32_ragged_full(algo):
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_ragged"])
+    announce(f"f32_ragged algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    assert_parity_full(inp, got, f"f32_ragged algo {algo} ({rt.last_kernel()})")
+
+
+def test_f32_4096_sampled():
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_4096"])
+    announce("f32_4096 default entry point")
+    got = run(inp, torch).cpu().numpy()
+    assert "regtile" in rt.last_kernel()
+    assert_parity_sampled(inp, got, "f32_4096")
+
+
+def test_f32_tall_sampled():
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
+    announce("f32_tall default entry point")
+    got = run(inp, torch).cpu().numpy()
+    assert_parity_sampled(inp, got, "f32_tall")
+
+
+def test_bf16_8192_sampled():
+    inp = gi.workload_inputs(gi.WORKLOADS["bf16_8192"])
+    announce("bf16_8192 default entry point")
+    got = run(inp, torch).cpu().numpy()
+    assert "mfma" in rt.last_kernel()
+    assert_parity_sampled(inp, got, "bf16_8192", n_random=30000)
+
+
+# ---- bf16 at a size the oracle finishes in full -----------------------------------------
+@pytest.mark.parametrize("algo", BF16_ALGOS)
+@pytest.mark.parametrize("shape", [(512, 768, 1024), (300, 257, 777), (1024, 1024, 256)])
+def test_bf16_full(algo, shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=1.5, beta=-0.5, seed=M + N + K)
+    announce(f"bf16 {shape} algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    assert_parity_full(inp, got, f"bf16 {shape} algo {algo} ({rt.last_kernel()})")
+
+
+# ---- edges: every tile boundary on either side ---------------------------------------------
+EDGE_SHAPES = [(1, 1, 1), (1, 7, 3), (2, 3, 5), (3, 1, 2), (17, 33, 9), (127, 129, 15),
+               (128, 128, 16), (129, 127, 17), (255, 257, 63), (256, 256, 64), (257, 255, 65),
+               (131, 293, 300), (64, 1024, 31), (1000, 8, 100), (8, 1000, 1000)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
+def test_f32_regtile_edges(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=-1.25, beta=0.75, seed=M * 7 + N + K)
+    announce(f"f32 edges {shape}")
+    got = run(inp, torch, rt.ALGO_F32_REGTILE).cpu().numpy()
+    assert_parity_full(inp, got, f"f32 edges {shape}")
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
+def test_bf16_mfma_edges(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=-1.25, beta=0.75, seed=M * 7 + N + K)
+    announce(f"bf16 edges {shape}")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    assert_parity_full(inp, got, f"bf16 edges {shape}")
+
+
+# ---- bitwise: integer-valued operands (every partial sum exact in fp32) ---------------------
+@pytest.mark.parametrize("algo", F32_ALGOS)
+def test_f32_integer_inputs_are_bitwise_exact(algo):
+    rng = np.random.Generator(np.random.PCG64(77))
+    M, N, K = 384, 260, 4096
+    A = rng.integers(-16, 17, (M, K)).astype(np.float32)
+    B = rng.integers(-16, 17, (K, N)).astype(np.float32)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f32", False, A, B, None)
+    announce(f"f32 integer bitwise algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    ref, _ = oracle.gemm_inputs(inp)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_bf16_integer_inputs_are_bitwise_exact():
+    rng = np.random.Generator(np.random.PCG64(78))
+    M, N, K = 256, 512, 8192
+    A = gi.f32_to_bf16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_bf16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, A, Bt, None)
+    announce("bf16 integer bitwise")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    ref, _ = oracle.gemm_inputs(inp)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_closed_forms_on_gpu():
+    n = 300
+    eye = np.eye(n, dtype=np.float32)
+    rng = np.random.Generator(np.random.PCG64(79))
+    Bm = rng.standard_normal((n, 200), dtype=np.float32)
+    announce("closed forms")
+    got = run(gi.GemmInputs(n, 200, n, 1.0, 0.0, "f32", False, eye, Bm, None), torch).cpu().numpy()
+    assert np.array_equal(got, Bm)  # identity: C == B bitwise
+    ones = gi.GemmInputs(130, 70, 1000, 1.0, 0.0, "f32", False, np.ones((130, 1000), np.float32),
+                         np.ones((1000, 70), np.float32), None)
+    assert np.all(run(ones, torch).cpu().numpy() == 1000.0)
+    hones = gi.GemmInputs(130, 70, 1000, 1.0, 0.0, "bf16", True, np.full((130, 1000), 0x3F80, np.uint16),
+                          np.full((70, 1000), 0x3F80, np.uint16), None)
+    assert np.all(run(hones, torch).cpu().numpy() == 1000.0)
+
+
+# ---- epilogue conventions -----------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beta_zero_never_reads_c(dtype):
+    inp = gi.make_inputs(200, 300, 64, dtype=dtype, dist="normal", seed=3)
+    announce(f"beta=0 NaN C {dtype}")
+    got = run(inp, torch, C_init=torch.full((200, 300), float("nan"), device="cuda")).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert_parity_full(inp, got, "beta=0 with NaN C")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_alpha_zero_and_k_zero_scale_c(dtype):
+    M, N = 70, 90
+    rng = np.random.Generator(np.random.PCG64(5))
+    C0 = rng.standard_normal((M, N), dtype=np.float32)
+    announce(f"alpha=0 / K=0 {dtype}")
+    inp = gi.make_inputs(M, N, 33, dtype=dtype, seed=4, beta=-2.0, alpha=0.0)
+    inp.C = C0
+    A, B, C = device_operands(inp, torch)
+    A.fill_(float("nan"))
+    fn = rt.gemm_f32 if dtype == "f32" else rt.gemm_bf16
+    fn(A, B, C, alpha=0.0, beta=-2.0)
+    torch.cuda.synchronize()
+    assert rt.last_kernel() == "scale_c"
+    assert np.array_equal(C.cpu().numpy(), -2.0 * C0)
+    # K == 0 with beta == 0 gives zeros (C not read)
+    C2 = torch.full((M, N), float("nan"), device="cuda")
+    fn(A[:, :0], B[:0, :], C2, alpha=1.0, beta=0.0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C2).item() == 0
+
+
+# ---- strides, misalignment, streams, determinism --------------------------------------------
+def test_f32_strided_and_misaligned_views():
+    rng = np.random.Generator(np.random.PCG64(6))
+    M, N, K = 300, 260, 301
+    big_a = torch.from_numpy(rng.standard_normal((M, K + 9), dtype=np.float32)).cuda()
+    big_b = torch.from_numpy(rng.standard_normal((K, N + 5), dtype=np.float32)).cuda()
+    big_c = torch.zeros((M, N + 3), device="cuda")
+    A = big_a[:, 1:K + 1]  # lda = K + 9, pointer offset by one float
+    B = big_b[:, 3:N + 3]
+    C = big_c[:, 1:N + 1]
+    announce("f32 strided/misaligned")
+    rt.gemm_f32(A, B, C)
+    torch.cuda.synchronize()
+    assert "_va" not in rt.last_kernel() and "_vb" not in rt.last_kernel()
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f32", False, A.cpu().numpy(), B.cpu().numpy(), None)
+    assert_parity_full(inp, C.cpu().numpy(), "strided views")
+    assert torch.count_nonzero(big_c[:, 0]).item() == 0  # nothing written outside C
+    assert torch.count_nonzero(big_c[:, N + 1:]).item() == 0
+
+
+def test_bf16_strided_and_misaligned_views():
+    rng = np.random.Generator(np.random.PCG64(7))
+    M, N, K = 260, 300, 200
+    ha = gi.f32_to_bf16_bits(rng.standard_normal(M * (K + 5), dtype=np.float32)).reshape(M, K + 5)
+    hb = gi.f32_to_bf16_bits(rng.standard_normal(N * (K + 3), dtype=np.float32)).reshape(N, K + 3)
+    da = torch.from_numpy(ha.view(np.int16)).cuda().view(torch.bfloat16)
+    db = torch.from_numpy(hb.view(np.int16)).cuda().view(torch.bfloat16)
+    A = da[:, 1:K + 1]
+    B = db[:, 2:K + 2].t()
+    announce("bf16 strided/misaligned")
+    C = rt.gemm_bf16(A, B)
+    torch.cuda.synchronize()
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, np.ascontiguousarray(ha[:, 1:K + 1]),
+                        np.ascontiguousarray(hb[:, 2:K + 2]), None)
+    assert_parity_full(inp, C.cpu().numpy(), "bf16 strided views")
+
+
+def test_runs_on_the_callers_stream_and_is_deterministic():
+    inp = gi.make_inputs(1024, 1024, 1024, dist="uniform", seed=8)
+    A, B, C = device_operands(inp, torch)
+    s = torch.cuda.Stream()
+    announce("stream + determinism")
+    outs = []
+    with torch.cuda.stream(s):
+        for _ in range(5):
+            C.zero_()
+            rt.gemm_f32(A, B, C)
+            outs.append(C.clone())
+    s.synchronize()
+    first = outs[0].cpu().numpy()
+    for o in outs[1:]:
+        assert np.array_equal(o.cpu().numpy(), first)
+    assert_parity_full(inp, first, "stream run")
+
+
+def test_f32_ladder_rungs_agree_bitwise():
+    # rungs 0-2 accumulate every output with fmaf over k in natural order
+    inp = gi.make_inputs(333, 517, 1029, dist="normal", seed=9)
+    announce("ladder bitwise agreement")
+    outs = [run(inp, torch, a).cpu().numpy() for a in (rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS,
+                                                        rt.ALGO_F32_REGTILE)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
