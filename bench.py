@@ -44,6 +44,11 @@ def _parse():
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 8192^3 leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
+    p.add_argument("--only", choices=["f32_4096", "bf16_8192", "f32_ragged", "f32_tall",
+                                      "f32_256", "copy"],
+                   help="profiler mode: run just this workload's kernel (warmup + steps) and "
+                        "print one summary line; 'copy' runs a plain 1 GiB device copy used to "
+                        "calibrate the HBM byte counters")
     return p.parse_args()
 
 
@@ -65,25 +70,32 @@ def _time(torch, fn, steps, warmup):
     return wall_ms, float(np.mean(kern)), float(np.min(kern))
 
 
-def _kernel_sources_digest():
+def _sources_digest(files):
+    """Digest of the named kernel sources (register_tiled_matrix_amd/csrc)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "register_tiled_matrix_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in files:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key, launches_bytes_alg):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent
-    or taken on other kernel sources."""
+def _traffic(kernel_name):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for a plain copy of known size),
+    or None when absent or when the kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel_key)
+            rec = json.load(f).get("kernels", {}).get(kernel_name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources_digest") != _kernel_sources_digest():
+    if not rec:
+        return None
+    try:
+        if rec.get("sources_digest") != _sources_digest(rec["sources"]):
+            return None
+    except (OSError, KeyError):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -127,6 +139,44 @@ def _cpu_model():
     return "unknown"
 
 
+def _only(args, torch, gi, rt, dev):
+    """Run one workload's kernel alone (for rocprofv3 runs)."""
+    if args.only == "copy":
+        n = 1 << 28  # 2^28 floats = 1 GiB each way
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        wms, kms, _ = _time(torch, lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"only": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "kernel_ms_mean": kms}), flush=True)
+        return 0
+    w = gi.WORKLOADS[args.only]
+    inp = gi.workload_inputs(w)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if w.dtype == "f32":
+        A = torch.from_numpy(inp.A).to(dev)
+        B = torch.from_numpy(inp.B).to(dev)
+        fn = rt.gemm_f32_raw
+    else:
+        A = torch.from_numpy(inp.A.view(np.int16)).to(dev)
+        B = torch.from_numpy(inp.B.view(np.int16)).to(dev)
+        fn = rt.gemm_bf16_raw
+    C = (torch.from_numpy(inp.C).to(dev) if inp.C is not None
+         else torch.empty((w.M, w.N), dtype=torch.float32, device=dev))
+    call = (w.M, w.N, w.K, w.alpha, A.data_ptr(), inp.lda, B.data_ptr(), inp.ldb, w.beta,
+            C.data_ptr(), w.N, stream)
+
+    def step():
+        st = fn(*call)
+        if st:
+            raise rt.RegtileError(st, rt.strerror(st))
+
+    wms, kms, kmin = _time(torch, step, args.steps, args.warmup)
+    print(json.dumps({"only": args.only, "kernel": rt.last_kernel(), "kernel_ms_mean": kms,
+                      "kernel_ms_min": kmin, "TFLOP/s": w.flop / (kms * 1e-3) / 1e12}),
+          flush=True)
+    return 0
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,6 +195,8 @@ def main():
         return 2
     rt.load()  # raises RegtileLibraryMissing when the HIP library is not built
     dev = torch.device("cuda:0")
+    if args.only:
+        return _only(args, torch, gi, rt, dev)
 
     # ---- headline: fp32 register-tiled 4096^3 ----------------------------------------------
     w = gi.WORKLOADS["f32_4096"]
@@ -193,7 +245,8 @@ def main():
             "peak": acc.PEAK_FP32_VECTOR_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / acc.PEAK_FP32_VECTOR_TFLOPS, 4),
-            "traffic": _traffic(kernel_name, work.hbm_bytes),
+            "traffic": _traffic(kernel_name),
+            "algorithmic_hbm_bytes": work.hbm_bytes,
             "kernel": kernel_name,
             "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_min": round(kern_min, 4),
@@ -231,7 +284,8 @@ def main():
             "percent_of_bf16_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
             "roofline": {"bound": "mfma", "achieved": round(a, 2), "peak": acc.PEAK_BF16_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(a / acc.PEAK_BF16_MFMA_TFLOPS, 4),
-                         "traffic": _traffic(kname, acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes),
+                         "traffic": _traffic(kname),
+                         "algorithmic_hbm_bytes": acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes,
                          "kernel": kname, "kernel_ms_mean": round(kms, 4),
                          "kernel_ms_min": round(kmin, 4), "flop_per_launch": wb.flop},
         }
