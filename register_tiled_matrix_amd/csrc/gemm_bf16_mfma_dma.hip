@@ -1,0 +1,247 @@
+// gemm_bf16_mfma_dma.hip -- the bf16 MFMA rung for full, aligned tiles: HBM -> LDS by direct
+// DMA loads, a multi-stage LDS ring, and wave tiles of 32x32x16 MFMA fragments.
+//
+// Same three levels as the other rungs ("寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507)
+// section 1.1: global block tile -> shared tile -> register tile), with the register level
+// made of MFMA fragments (section 3.2: per k step, A and B fragments are read from LDS into
+// VGPRs and the C accumulators are updated in place). What is specific to gfx950 here:
+//
+//  * HBM -> LDS without registers: global_load_lds_dwordx4 writes each lane's 16 bytes
+//    straight into LDS at (wave-uniform base + lane * 16). The LDS image of a slab is the
+//    swizzled layout below, so lane l of a load instruction fetches the global chunk that
+//    belongs in LDS slot (base + l): the permutation is applied to the global addresses.
+//  * Slab layout: a tile row (an A row, or a B column: both operands are K-contiguous) of
+//    BK bf16 is KCH = BK/8 chunks of 16 bytes; chunk c of row r sits in slot c ^ key(r).
+//    128-bit LDS reads are served 16 lanes at a time over 64 banks (256 bytes). A fragment
+//    read covers 16 consecutive rows at one chunk, and the key makes those 16 reads hit 16
+//    distinct 16-byte bank groups:
+//      KCH = 8 (128-byte rows): key(r) = (r & 7) ^ ((r >> 3) & 1)
+//      KCH = 4 ( 64-byte rows): key(r) = (r >> 2) & 3
+//  * STAGES slabs in flight: slab s+STAGES-1 is requested while slab s is consumed, and
+//    each wave waits (s_waitcnt vmcnt) only for the slab it is about to read; one barrier
+//    per slab both publishes that slab and retires the stage the next request overwrites
+//    (section 6.3: prefetch of the next k-slice while the current one is computed).
+//  * Wave tile WTM x WTN of 32x32 blocks: per 16-wide k step a wave reads WTM/32 A and
+//    WTN/32 B fragments (one 16-byte LDS read each) and issues (WTM/32)*(WTN/32) MFMAs, so
+//    LDS reads per MFMA fall as the wave tile grows.
+//  * Tile order: contiguous blocks of tiles per XCD, grouped 8 tile-rows at a time.
+#include "regtile_internal.h"
+
+namespace regtile {
+
+namespace {
+
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+template <int KCH>
+__device__ __forceinline__ int slab_key(int row) {
+    static_assert(KCH == 4 || KCH == 8, "slab rows of 64 or 128 bytes");
+    if (KCH == 8) return (row & 7) ^ ((row >> 3) & 1);
+    return (row >> 2) & 3;
+}
+
+// One 16-byte-per-lane DMA load: global `src` -> LDS at `dst` + lane * 16 (dst wave-uniform).
+// The body exists only in the device pass: the host pass cannot form LDS-space pointers.
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+#else
+    (void)src;
+    (void)dst;
+#endif
+}
+
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
+    int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
+    const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n) {
+    constexpr int NWAVES = WAVES_M * WAVES_N;
+    constexpr int KCH = BK / 8;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int MI = WTM / 32, NI = WTN / 32;
+    constexpr int A_SLOTS = BM * KCH, B_SLOTS = BN * KCH;  // 16-byte slots per stage
+    constexpr int STAGE_SLOTS = A_SLOTS + B_SLOTS;
+    constexpr int JA = A_SLOTS / (64 * NWAVES), JB = B_SLOTS / (64 * NWAVES);
+    constexpr int PER_SLAB = JA + JB;  // DMA instructions per wave per slab
+    static_assert(A_SLOTS % (64 * NWAVES) == 0 && B_SLOTS % (64 * NWAVES) == 0, "even DMA split");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "fragment shapes");
+    static_assert(PER_SLAB * (STAGES - 1) < 64, "vmcnt range");
+
+    __shared__ uint4 smem[STAGES * STAGE_SLOTS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    int tm, tn;
+    grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Global source of every slot this lane fills: slot p = (wave*J + j)*64 + lane holds
+    // chunk (p % KCH) ^ key(row) of tile row p / KCH.
+    const uint16_t *a_src[JA];
+    const uint16_t *b_src[JB];
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+        const int p = (wave * JA + j) * 64 + lane;
+        const int row = p / KCH, chunk = (p % KCH) ^ slab_key<KCH>(row);
+        a_src[j] = A + (int64_t)(m0 + row) * lda + chunk * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+        const int p = (wave * JB + j) * 64 + lane;
+        const int row = p / KCH, chunk = (p % KCH) ^ slab_key<KCH>(row);
+        b_src[j] = B + (int64_t)(n0 + row) * ldb + chunk * 8;
+    }
+
+    auto issue = [&](int slab, int stage) {
+        const int k0 = slab * BK;
+        uint4 *sa = smem + stage * STAGE_SLOTS;
+        uint4 *sb = sa + A_SLOTS;
+#pragma unroll
+        for (int j = 0; j < JA; ++j)
+            dma16(a_src[j] + k0, sa + (wave * JA + j) * 64);
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+            dma16(b_src[j] + k0, sb + (wave * JB + j) * 64);
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int frag_r = lane & 31;
+    const int frag_kh = lane >> 5;
+
+    // Fragment reads of one 16-wide k step into register buffer `buf`.
+    bf16x8 fa[2][MI], fb[2][NI];
+    auto read_frags = [&](const uint4 *sa, const uint4 *sb, int kk, int buf) {
+        const int chunk = kk * 2 + frag_kh;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int row = wm * WTM + i * 32 + frag_r;
+            fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH>(row))]);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int row = wn * WTN + j * 32 + frag_r;
+            fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH>(row))]);
+        }
+    };
+    // One slab: the reads of step kk+1 are issued between the MFMAs of step kk, so LDS
+    // latency hides behind the matrix pipe.
+    auto compute = [&](int stage) {
+        const uint4 *sa = smem + stage * STAGE_SLOTS;
+        const uint4 *sb = sa + A_SLOTS;
+        read_frags(sa, sb, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cb = kk & 1;
+            if (kk + 1 < BK / 16) read_frags(sa, sb, kk + 1, cb ^ 1);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+            if (kk + 1 < BK / 16) {
+                // interleave: one LDS read after every other MFMA
+#pragma unroll
+                for (int g = 0; g < MI + NI; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI) / (MI + NI), 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nslabs = K / BK;
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+        if (t < nslabs) issue(t, t);
+
+    for (int s = 0; s < nslabs; ++s) {
+        // Slab s must have landed; the requests of up to STAGES-2 later slabs may still fly.
+        if (s + STAGES - 2 < nslabs) wait_vmcnt<PER_SLAB * (STAGES - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const int next = s + STAGES - 1;
+        if (next < nslabs) issue(next, next % STAGES);
+        compute(s % STAGES);
+    }
+
+    // Epilogue: accumulator v of lane l in a 32x32 block holds row (v/4)*8 + (l/32)*4 + v%4,
+    // column l%32. beta == 0 never reads C.
+    const bool read_c = beta != 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + frag_r;
+            float *cbase = C + (int64_t)(m0 + wm * WTM + i * 32 + frag_kh * 4) * ldc + col;
+            if (read_c) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float *c = cbase + (int64_t)((v >> 2) * 8 + (v & 3)) * ldc;
+                    *c = fmaf(alpha, acc[i][j][v], beta * *c);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    cbase[(int64_t)((v >> 2) * 8 + (v & 3)) * ldc] = alpha * acc[i][j][v];
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int STAGES, int WM, int WN>
+hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
+    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, STAGES, WM, WN>), dim3(tiles_m * tiles_n),
+                       dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
+                       p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REGTILE_STR2(x) #x
+#define REGTILE_STR(x) REGTILE_STR2(x)
+
+#ifndef DMA_BM
+#define DMA_BM 256
+#define DMA_BN 256
+#define DMA_BK 64
+#define DMA_STAGES 2
+#define DMA_WM 2
+#define DMA_WN 2
+#endif
+
+}  // namespace
+
+// Returns hipErrorNotSupported (and launches nothing) unless the problem is made of full
+// tiles with 16-byte aligned, K-contiguous rows.
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name) {
+    const bool ok = p.M % DMA_BM == 0 && p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
+                    p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
+                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128;
+    if (!ok) return hipErrorNotSupported;
+    *name = "bf16_mfma_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)
+            "_s" REGTILE_STR(DMA_STAGES) "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN);
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN>(p, s);
+}
+
+}  // namespace regtile

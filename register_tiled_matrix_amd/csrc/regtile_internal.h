@@ -27,6 +27,8 @@ hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name);
+// Full aligned tiles only; returns hipErrorNotSupported without launching otherwise.
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name);
 
 // C element update shared by every kernel's epilogue: beta == 0 never reads C.
 __device__ __forceinline__ float epilogue_value(float acc, float alpha, float beta,

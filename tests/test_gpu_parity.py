@@ -73,12 +73,15 @@ def test_bf16_8192_sampled():
 
 # ---- bf16 at a size the oracle finishes in full -----------------------------------------
 @pytest.mark.parametrize("algo", BF16_ALGOS)
-@pytest.mark.parametrize("shape", [(512, 768, 1024), (300, 257, 777), (1024, 1024, 256)])
+@pytest.mark.parametrize("shape", [(512, 768, 1024), (300, 257, 777), (1024, 1024, 256),
+                                   (2048, 4096, 192)])
 def test_bf16_full(algo, shape):
     M, N, K = shape
     inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=1.5, beta=-0.5, seed=M + N + K)
     announce(f"bf16 {shape} algo={algo}")
     got = run(inp, torch, algo).cpu().numpy()
+    if shape == (2048, 4096, 192) and algo != rt.ALGO_BF16_NAIVE:
+        assert "dma" in rt.last_kernel()  # full aligned 256x256 tiles take the DMA kernel
     assert_parity_full(inp, got, f"bf16 {shape} algo {algo} ({rt.last_kernel()})")
 
 
