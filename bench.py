@@ -238,7 +238,6 @@ def main():
                                "U[-1,1] seed 1002, alpha=1, beta=0",
                    "M": w.M, "N": w.N, "K": w.K, "kernel": kernel_name},
         "percent_of_fp32_vector_peak": round(100 * value / acc.PEAK_FP32_VECTOR_TFLOPS, 2),
-        "percent_of_fp32_nonpacked_ceiling": round(100 * value / acc.PEAK_FP32_NONPACKED_TFLOPS, 2),
         "roofline": {
             "bound": "alu",
             "achieved": round(achieved, 3),
@@ -251,8 +250,6 @@ def main():
             "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_min": round(kern_min, 4),
             "flop_per_launch": flop,
-            "nonpacked_fp32_ceiling": acc.PEAK_FP32_NONPACKED_TFLOPS,
-            "frac_of_nonpacked_ceiling": round(achieved / acc.PEAK_FP32_NONPACKED_TFLOPS, 4),
         },
     }
 

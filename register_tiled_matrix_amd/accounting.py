@@ -88,7 +88,6 @@ class GemmWork:
 
 
 # MI355X published peaks used as roofline ceilings.
-PEAK_FP32_VECTOR_TFLOPS = 157.3  # counts packed FP32 FMA (two per lane per instruction)
-PEAK_FP32_NONPACKED_TFLOPS = 78.6  # one FMA per lane per instruction: 256 CU * 2.4 GHz * 128
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # 256 CU * 2.4 GHz * 256 flop/clk/CU
 PEAK_BF16_MFMA_TFLOPS = 2516.6  # dense
 PEAK_HBM_GBS = 8000.0

@@ -25,6 +25,8 @@
 //    WTN/32 B fragments (one 16-byte LDS read each) and issues (WTM/32)*(WTN/32) MFMAs, so
 //    LDS reads per MFMA fall as the wave tile grows.
 //  * Tile order: contiguous blocks of tiles per XCD, grouped 8 tile-rows at a time.
+#include <type_traits>
+
 #include "regtile_internal.h"
 
 namespace regtile {
@@ -51,6 +53,9 @@ __device__ __forceinline__ void dma16(const void *src, void *dst) {
     (void)dst;
 #endif
 }
+
+// s_waitcnt lgkmcnt(0) only (LDS reads; LDS DMA is counted by vmcnt, not lgkmcnt).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
 template <int N>
@@ -87,21 +92,27 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     const int m0 = tm * BM, n0 = tn * BN;
 
     // Global source of every slot this lane fills: slot p = (wave*J + j)*64 + lane holds
-    // chunk (p % KCH) ^ key(row) of tile row p / KCH.
-    const uint16_t *a_src[JA];
-    const uint16_t *b_src[JB];
+    // chunk (p % KCH) ^ key(row) of tile row p / KCH. One instruction covers 64/KCH rows, so
+    // instruction j's row is instruction (j & 1)'s row plus a uniform (j & ~1) * 64/KCH, and
+    // its key equals instruction (j & 1)'s (the key depends on the row only through bits that
+    // an even number of instructions leaves unchanged): two per-lane pointers per operand.
+    constexpr int ROWS_PER_INSTR = 64 / KCH;
+    static_assert(KCH == 4 || (ROWS_PER_INSTR == 8 && JA % 2 == 0 && JB % 2 == 0), "key periodicity");
+    const uint16_t *a_lane[2];
+    const uint16_t *b_lane[2];
 #pragma unroll
-    for (int j = 0; j < JA; ++j) {
-        const int p = (wave * JA + j) * 64 + lane;
-        const int row = p / KCH, chunk = (p % KCH) ^ slab_key<KCH>(row);
-        a_src[j] = A + (int64_t)(m0 + row) * lda + chunk * 8;
+    for (int j = 0; j < 2; ++j) {
+        const int pa = (wave * JA + j) * 64 + lane;
+        const int ra = pa / KCH, ca = (pa % KCH) ^ slab_key<KCH>(ra);
+        a_lane[j] = A + (int64_t)(m0 + ra) * lda + ca * 8;
+        const int pb = (wave * JB + j) * 64 + lane;
+        const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH>(rb);
+        b_lane[j] = B + (int64_t)(n0 + rb) * ldb + cb * 8;
     }
-#pragma unroll
-    for (int j = 0; j < JB; ++j) {
-        const int p = (wave * JB + j) * 64 + lane;
-        const int row = p / KCH, chunk = (p % KCH) ^ slab_key<KCH>(row);
-        b_src[j] = B + (int64_t)(n0 + row) * ldb + chunk * 8;
-    }
+    const int64_t a_step = (int64_t)ROWS_PER_INSTR * lda;  // per instruction pair: 2 * a_step
+    const int64_t b_step = (int64_t)ROWS_PER_INSTR * ldb;
+    auto a_src = [&](int j) { return a_lane[j & 1] + (j & ~1) * a_step; };
+    auto b_src = [&](int j) { return b_lane[j & 1] + (j & ~1) * b_step; };
 
     auto issue = [&](int slab, int stage) {
         const int k0 = slab * BK;
@@ -109,10 +120,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         uint4 *sb = sa + A_SLOTS;
 #pragma unroll
         for (int j = 0; j < JA; ++j)
-            dma16(a_src[j] + k0, sa + (wave * JA + j) * 64);
+            dma16(a_src(j) + k0, sa + (wave * JA + j) * 64);
 #pragma unroll
         for (int j = 0; j < JB; ++j)
-            dma16(b_src[j] + k0, sb + (wave * JB + j) * 64);
+            dma16(b_src(j) + k0, sb + (wave * JB + j) * 64);
     };
 
     f32x16 acc[MI][NI];
@@ -141,47 +152,80 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH>(row))]);
         }
     };
-    // One slab: the reads of step kk+1 are issued between the MFMAs of step kk, so LDS
-    // latency hides behind the matrix pipe.
-    auto compute = [&](int stage) {
+    // One slab. Each 16-wide k step starts by waiting for its own fragments (read during the
+    // previous step), then issues its MFMAs with the next step's fragment reads and a share
+    // of the next slab's DMA loads woven between them: MFMA, read, MFMA, DMA, ... A 1 KB DMA
+    // instruction occupies the wave's issue for about 20 cycles (the address unit moves
+    // 64 bytes per clock), less than one 32-cycle MFMA, so spread out it costs no matrix
+    // cycles, while a burst of them would stall the MFMAs queued behind it.
+    constexpr int KSTEPS = BK / 16;
+    constexpr int NMFMA = MI * NI;
+    constexpr int NREAD = MI + NI;
+    constexpr int DMA_PER_STEP = (PER_SLAB + KSTEPS - 1) / KSTEPS;
+    static_assert(NREAD <= NMFMA && DMA_PER_STEP <= NMFMA, "one extra instruction per MFMA slot");
+    auto compute = [&](int stage, int next_slab, int next_stage) {
         const uint4 *sa = smem + stage * STAGE_SLOTS;
         const uint4 *sb = sa + A_SLOTS;
+        const int k0n = next_slab * BK;
+        uint4 *na = smem + next_stage * STAGE_SLOTS;
+        uint4 *nb = na + A_SLOTS;
         read_frags(sa, sb, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
+        for (int kk = 0; kk < KSTEPS; ++kk) {
             const int cb = kk & 1;
-            if (kk + 1 < BK / 16) read_frags(sa, sb, kk + 1, cb ^ 1);
+            wait_lgkmcnt0();  // this step's fragments have landed
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < KSTEPS) read_frags(sa, sb, kk + 1, cb ^ 1);
+#pragma unroll
+            for (int d = 0; d < DMA_PER_STEP; ++d) {
+                const int q = kk * DMA_PER_STEP + d;  // DMA instruction index within the slab
+                if (q < JA) dma16(a_src(q) + k0n, na + (wave * JA + q) * 64);
+                else if (q < PER_SLAB) dma16(b_src(q - JA) + k0n, nb + (wave * JB + (q - JA)) * 64);
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
-            if (kk + 1 < BK / 16) {
-                // interleave: one LDS read after every other MFMA
+            // issue order: every MFMA is followed by at most one read or one DMA
+            const int reads = (kk + 1 < KSTEPS) ? NREAD : 0;
+            const int dmas = (kk * DMA_PER_STEP < PER_SLAB)
+                                     ? ((PER_SLAB - kk * DMA_PER_STEP) < DMA_PER_STEP
+                                            ? (PER_SLAB - kk * DMA_PER_STEP) : DMA_PER_STEP)
+                                     : 0;
+            int r_left = reads, d_left = dmas;
 #pragma unroll
-                for (int g = 0; g < MI + NI; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI) / (MI + NI), 0);
+            for (int g = 0; g < NMFMA; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                // spread reads and DMAs evenly over the MFMA slots
+                const bool want_dma = d_left > 0 && (g * dmas) / NMFMA != ((g + 1) * dmas) / NMFMA;
+                if (want_dma) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    --d_left;
+                } else if (r_left > 0) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    --r_left;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // Every iteration requests exactly one slab, so the wait count is the same each time.
+    // Past the end the request is clamped to the last slab: it rewrites a stage that has
+    // already been consumed with valid data and keeps the loop body uniform.
     const int nslabs = K / BK;
 #pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-        if (t < nslabs) issue(t, t);
+    for (int t = 0; t < STAGES - 1; ++t) issue(min(t, nslabs - 1), t);
 
     for (int s = 0; s < nslabs; ++s) {
-        // Slab s must have landed; the requests of up to STAGES-2 later slabs may still fly.
-        if (s + STAGES - 2 < nslabs) wait_vmcnt<PER_SLAB * (STAGES - 2)>();
-        else wait_vmcnt<0>();
+        // Slab s must have landed; the requests of the STAGES-2 slabs after it may still fly.
+        wait_vmcnt<PER_SLAB * (STAGES - 2)>();
         __syncthreads();
         const int next = s + STAGES - 1;
-        if (next < nslabs) issue(next, next % STAGES);
-        compute(s % STAGES);
+        compute(s % STAGES, min(next, nslabs - 1), next % STAGES);
     }
+    wait_vmcnt<0>();  // no LDS DMA may still be in flight when the workgroup retires
 
     // Epilogue: accumulator v of lane l in a 32x32 block holds row (v/4)*8 + (l/32)*4 + v%4,
     // column l%32. beta == 0 never reads C.

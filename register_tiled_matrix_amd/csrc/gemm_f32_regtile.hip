@@ -31,7 +31,7 @@ namespace {
 
 constexpr int BM = 128, BN = 128, TM = 8, TN = 8, NT = 256;
 #ifndef F32_WAVES_PER_EU
-#define F32_WAVES_PER_EU 3
+#define F32_WAVES_PER_EU 2
 #endif
 constexpr int APAD = 4;  // A slab row stride BM + 4 floats: transposed stores hit 32 banks per half-wave
 
@@ -214,7 +214,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
     }
 }
 
-constexpr int kBK = 16;
+#ifndef F32_BK
+#define F32_BK 16
+#endif
+constexpr int kBK = F32_BK;
 
 template <bool EDGE, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tiles_n) {
