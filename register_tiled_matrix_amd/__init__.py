@@ -25,7 +25,7 @@ import os
 import threading
 
 __all__ = [
-    "ALGO_F32_AUTO", "ALGO_F32_NAIVE", "ALGO_F32_LDS", "ALGO_F32_REGTILE",
+    "ALGO_F32_AUTO", "ALGO_F32_NAIVE", "ALGO_F32_LDS", "ALGO_F32_REGTILE", "ALGO_F32_SPLITK",
     "ALGO_BF16_AUTO", "ALGO_BF16_NAIVE", "ALGO_BF16_MFMA",
     "RegtileError", "RegtileLibraryMissing", "lib_path", "load",
     "gemm_f32", "gemm_bf16", "gemm_f32_raw", "gemm_bf16_raw",
@@ -33,7 +33,7 @@ __all__ = [
     "last_kernel", "strerror", "version", "EXPORTED_SYMBOLS",
 ]
 
-ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE = 0, 1, 2, 3
+ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE, ALGO_F32_SPLITK = 0, 1, 2, 3, 4
 ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo",

@@ -24,8 +24,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libregtile.so")
 ARCH = "gfx950"
 
-SOURCES = ["regtile_api.hip", "gemm_simple.hip", "gemm_f32_regtile.hip", "gemm_bf16_mfma.hip",
-           "gemm_bf16_mfma_dma.hip"]
+SOURCES = ["regtile_api.hip", "gemm_simple.hip", "gemm_f32_regtile.hip", "gemm_f32_splitk.hip",
+           "gemm_bf16_mfma.hip", "gemm_bf16_mfma_dma.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

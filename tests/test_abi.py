@@ -90,7 +90,7 @@ def test_bf16_argument_validation(lib, args, expect):
 
 def test_unknown_algorithm_is_argument_one(lib):
     a = (4, 4, 4, 1.0, DUMMY, 4, DUMMY, 4, 0.0, DUMMY, 4, 0)
-    assert rt.regtile_gemm_f32_algo(4, *a) == -1
+    assert rt.regtile_gemm_f32_algo(5, *a) == -1
     assert rt.regtile_gemm_f32_algo(-1, *a) == -1
     assert rt.regtile_gemm_bf16_algo(3, *a) == -1
 

@@ -19,7 +19,8 @@ from gpu_util import announce, assert_parity_full, assert_parity_sampled, device
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS, rt.ALGO_F32_REGTILE, rt.ALGO_F32_AUTO]
+F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS, rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK,
+             rt.ALGO_F32_AUTO]
 BF16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_AUTO]
 
 
@@ -60,6 +61,7 @@ def test_f32_tall_sampled():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
     announce("f32_tall default entry point")
     got = run(inp, torch).cpu().numpy()
+    assert "splitk" in rt.last_kernel()  # 128 tiles of 128x128: the split-K variant
     assert_parity_sampled(inp, got, "f32_tall")
 
 
@@ -91,13 +93,14 @@ EDGE_SHAPES = [(1, 1, 1), (1, 7, 3), (2, 3, 5), (3, 1, 2), (17, 33, 9), (127, 12
                (131, 293, 300), (64, 1024, 31), (1000, 8, 100), (8, 1000, 1000)]
 
 
+@pytest.mark.parametrize("algo", [rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK])
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
-def test_f32_regtile_edges(shape):
+def test_f32_regtile_edges(shape, algo):
     M, N, K = shape
     inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=-1.25, beta=0.75, seed=M * 7 + N + K)
-    announce(f"f32 edges {shape}")
-    got = run(inp, torch, rt.ALGO_F32_REGTILE).cpu().numpy()
-    assert_parity_full(inp, got, f"f32 edges {shape}")
+    announce(f"f32 edges {shape} algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    assert_parity_full(inp, got, f"f32 edges {shape} ({rt.last_kernel()})")
 
 
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
@@ -196,7 +199,6 @@ def test_f32_strided_and_misaligned_views():
     announce("f32 strided/misaligned")
     rt.gemm_f32(A, B, C)
     torch.cuda.synchronize()
-    assert "_va" not in rt.last_kernel() and "_vb" not in rt.last_kernel()
     inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f32", False, A.cpu().numpy(), B.cpu().numpy(), None)
     assert_parity_full(inp, C.cpu().numpy(), "strided views")
     assert torch.count_nonzero(big_c[:, 0]).item() == 0  # nothing written outside C
@@ -245,3 +247,32 @@ def test_f32_ladder_rungs_agree_bitwise():
     outs = [run(inp, torch, a).cpu().numpy() for a in (rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS,
                                                         rt.ALGO_F32_REGTILE)]
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_f32_strided_views_every_register_tiled_kernel():
+    # unaligned lda/ldb/ldc and pointers offset by one float take the scalar load paths
+    rng = np.random.Generator(np.random.PCG64(10))
+    M, N, K = 300, 260, 301
+    big_a = torch.from_numpy(rng.standard_normal((M, K + 9), dtype=np.float32)).cuda()
+    big_b = torch.from_numpy(rng.standard_normal((K, N + 5), dtype=np.float32)).cuda()
+    A, B = big_a[:, 1:K + 1], big_b[:, 3:N + 3]
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f32", False, A.cpu().numpy(), B.cpu().numpy(), None)
+    for algo in (rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK):
+        announce(f"f32 strided algo={algo}")
+        big_c = torch.zeros((M, N + 3), device="cuda")
+        C = big_c[:, 1:N + 1]
+        rt.gemm_f32(A, B, C, algo=algo)
+        torch.cuda.synchronize()
+        name = rt.last_kernel()
+        assert "_va" not in name and "_vb" not in name
+        assert_parity_full(inp, C.cpu().numpy(), f"strided views ({name})")
+        assert torch.count_nonzero(big_c[:, 0]).item() == 0
+        assert torch.count_nonzero(big_c[:, N + 1:]).item() == 0
+
+
+def test_splitk_is_deterministic_and_matches_oracle_at_tall_shape():
+    inp = gi.make_inputs(4096, 192, 2000, dist="uniform", seed=12)
+    announce("splitk determinism")
+    outs = [run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy() for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert_parity_sampled(inp, outs[0], "splitk tall")
