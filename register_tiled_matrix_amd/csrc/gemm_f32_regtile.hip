@@ -29,7 +29,14 @@ namespace regtile {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, TM = 8, TN = 8, NT = 256;
+#ifndef F32_TN
+#define F32_TN 16
+#endif
+// TM x TN micro-tile per lane: TM = 8 rows in two groups of 4 (32 rows apart), TN columns in
+// TN / 4 groups of 4 (32 columns apart). A wave is an 8x8 grid of lanes, 4 waves in 2x2.
+constexpr int TM = 8, TN = F32_TN, NG = TN / 4, NT = 256;
+constexpr int BM = 128, BN = 16 * TN;
+static_assert(TN == 8 || TN == 16, "8x8 or 8x16 micro-tiles");
 #ifndef F32_WAVES_PER_EU
 #define F32_WAVES_PER_EU 2
 #endif
@@ -73,47 +80,53 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
                                                          float beta, float *__restrict__ C,
                                                          int64_t ldc, int tiles_m, int tiles_n) {
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    constexpr int CH = BK / 8;        // float4 chunks per thread per operand per slab
-    constexpr int A_CPR = BK / 4;     // A chunks per tile row
+    constexpr int CH = BK / 8;              // A float4 chunks per thread per slab
+    constexpr int A_CPR = BK / 4;           // A chunks per tile row
+    constexpr int B_CPR = BN / 4;           // B chunks per slab row
+    constexpr int CHB = BK * BN / (4 * NT);  // B float4 chunks per thread per slab
     __shared__ Smem<BK> sm;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int r0 = (wave >> 1) * 64 + (lane >> 3) * 4;
-    const int c0 = (wave & 1) * 64 + (lane & 7) * 4;
+    const int c0 = (wave & 1) * (8 * TN) + (lane & 7) * 4;
 
     int tm, tn;
     grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // This thread's staging chunks: A chunk q = tid + NT*i -> (row q / A_CPR, k (q % A_CPR)*4);
-    // B chunk q -> (k q / 32, col (q % 32)*4).
-    int a_row[CH], a_k[CH], b_k[CH], b_col[CH];
+    // B chunk q -> (k q / B_CPR, col (q % B_CPR)*4).
+    int a_row[CH], a_k[CH], b_k[CHB], b_col[CHB];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int q = tid + NT * i;
         a_row[i] = q / A_CPR;
         a_k[i] = (q % A_CPR) * 4;
-        b_k[i] = q / 32;
-        b_col[i] = (q % 32) * 4;
+    }
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) {
+        const int q = tid + NT * i;
+        b_k[i] = q / B_CPR;
+        b_col[i] = (q % B_CPR) * 4;
     }
     const float *a_ptr[CH];
-    const float *b_ptr[CH];
+    const float *b_ptr[CHB];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        a_ptr[i] = A + (int64_t)(m0 + a_row[i]) * lda + a_k[i];
-        b_ptr[i] = B + (int64_t)b_k[i] * ldb + n0 + b_col[i];
-    }
+    for (int i = 0; i < CH; ++i) a_ptr[i] = A + (int64_t)(m0 + a_row[i]) * lda + a_k[i];
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) b_ptr[i] = B + (int64_t)b_k[i] * ldb + n0 + b_col[i];
 
-    float4 ra[CH], rb[CH];
+    float4 ra[CH], rb[CHB];
     auto load_slab = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
+        for (int i = 0; i < CH; ++i)
             ra[i] = load4_rowwise<BK, EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_row[i]),
                                                    K - (k0 + a_k[i]));
+#pragma unroll
+        for (int i = 0; i < CHB; ++i)
             rb[i] = load4_rowwise<BK, EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
                                                    K - (k0 + b_k[i]), N - (n0 + b_col[i]));
-        }
     };
     auto store_slab = [&](int buf) {
 #pragma unroll
@@ -122,8 +135,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
             sm.a[buf][a_k[i] + 1][a_row[i]] = ra[i].y;
             sm.a[buf][a_k[i] + 2][a_row[i]] = ra[i].z;
             sm.a[buf][a_k[i] + 3][a_row[i]] = ra[i].w;
-            *reinterpret_cast<float4 *>(&sm.b[buf][b_k[i]][b_col[i]]) = rb[i];
         }
+#pragma unroll
+        for (int i = 0; i < CHB; ++i)
+            *reinterpret_cast<float4 *>(&sm.b[buf][b_k[i]][b_col[i]]) = rb[i];
     };
 
     float acc[TM][TN];
@@ -139,24 +154,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
         // Fragment double buffer: the reads for step k+1 are issued before the 64 FMAs of
         // step k. The scheduling barrier keeps the compiler from hoisting the whole slab's
         // reads (which would need BK*16 live registers and spill).
-        float4 fa[2][2], fb[2][2];
+        float4 fa[2][2], fb[2][NG];
         fa[0][0] = *reinterpret_cast<const float4 *>(sa);
         fa[0][1] = *reinterpret_cast<const float4 *>(sa + 32);
-        fb[0][0] = *reinterpret_cast<const float4 *>(sb);
-        fb[0][1] = *reinterpret_cast<const float4 *>(sb + 32);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) fb[0][g] = *reinterpret_cast<const float4 *>(sb + g * 32);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const int cb = k & 1, nb = cb ^ 1;
             if (k + 1 < BK) {
                 fa[nb][0] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD));
                 fa[nb][1] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD) + 32);
-                fb[nb][0] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN);
-                fb[nb][1] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN + 32);
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN + g * 32);
             }
             const float ra_[TM] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
                                    fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
-            const float rb_[TN] = {fb[cb][0].x, fb[cb][0].y, fb[cb][0].z, fb[cb][0].w,
-                                   fb[cb][1].x, fb[cb][1].y, fb[cb][1].z, fb[cb][1].w};
+            float rb_[TN];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                rb_[4 * g + 0] = fb[cb][g].x;
+                rb_[4 * g + 1] = fb[cb][g].y;
+                rb_[4 * g + 2] = fb[cb][g].z;
+                rb_[4 * g + 3] = fb[cb][g].w;
+            }
 #pragma unroll
             for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -182,14 +204,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
         compute_slab((nslabs - 1) & 1);
     }
 
-    // Epilogue: rows r0+{0..3}, r0+32+{0..3}; columns c0+{0..3}, c0+32+{0..3}.
+    // Epilogue: rows r0+{0..3}, r0+32+{0..3}; columns c0 + 32*h + {0..3}, h < TN/4.
 #pragma unroll
     for (int m = 0; m < TM; ++m) {
         const int row = m0 + r0 + (m < 4 ? m : 28 + m);
         if (EDGE && row >= M) continue;
         float *crow = C + (int64_t)row * ldc;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NG; ++h) {
             const int col = n0 + c0 + h * 32;
             float *c = crow + col;
             if (VEC_C && (!EDGE || col + 3 < N)) {
@@ -260,8 +282,8 @@ hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name
                 for (int a = 0; a < 2; ++a)
                     for (int b = 0; b < 2; ++b)
                         for (int c = 0; c < 2; ++c) {
-                            snprintf(text[n], sizeof text[n], "f32_regtile_128x128x%d_8x8%s%s%s%s",
-                                     kBK, e ? "_edge" : "", a ? "_va" : "", b ? "_vb" : "",
+                            snprintf(text[n], sizeof text[n], "f32_regtile_%dx%dx%d_%dx%d%s%s%s%s",
+                                     BM, BN, kBK, TM, TN, e ? "_edge" : "", a ? "_va" : "", b ? "_vb" : "",
                                      c ? "_vc" : "");
                             at[e][a][b][c] = text[n++];
                         }
