@@ -13,7 +13,8 @@ Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize
 (wall clock -> ms_per_step and value), with a HIP event pair around every launch on the
 stream the library launches on (the caller's current stream) -> the average kernel
 duration used for the roofline figure. The CPU baseline times the fp64 oracle as it stands
-on a bounded row sample of the same workload.
+on a bounded row sample of the same workload, and a blocked multithreaded fp32 CPU GEMM
+(cpu_baseline/) on the whole workload.
 """
 from __future__ import annotations
 
@@ -127,6 +128,23 @@ def _cpu_baseline(inp, target_s):
             "seconds": dt,
             "host_cpu": platform.processor() or _cpu_model(),
             "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def _cpu_blocked(inp):
+    """The blocked multithreaded fp32 CPU GEMM on the whole workload (best of two runs)."""
+    import cpu_baseline
+
+    best = None
+    for _ in range(2):
+        t0 = time.perf_counter()
+        cpu_baseline.sgemm(inp.A, inp.B)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    flop = 2.0 * inp.M * inp.N * inp.K
+    return {"value": flop / best / 1e12, "unit": "TFLOP/s", "cores": cpu_baseline.num_threads(),
+            "kind": "blocked fp32 (8x16 register micro-kernel, AVX2/FMA, OpenMP)",
+            "sample": f"the whole {inp.M}x{inp.N}x{inp.K} fp32 workload, best of 2 ({best:.2f} s)",
+            "seconds": best}
 
 
 def _cpu_model():
@@ -310,6 +328,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------
     if not args.no_cpu:
         out["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_blocked_gemm"] = _cpu_blocked(inp)
     else:
         out["cpu_baseline"] = None
 
