@@ -50,6 +50,9 @@ def _parse():
                    help="profiler mode: run just this workload's kernel (warmup + steps) and "
                         "print one summary line; 'copy' runs a plain 1 GiB device copy used to "
                         "calibrate the HBM byte counters")
+    p.add_argument("--algo", type=int, default=0,
+                   help="with --only: kernel ladder rung (the regtile_algo_f32 / _bf16 value; "
+                        "0 = the default entry point)")
     return p.parse_args()
 
 
@@ -173,11 +176,13 @@ def _only(args, torch, gi, rt, dev):
     if w.dtype == "f32":
         A = torch.from_numpy(inp.A).to(dev)
         B = torch.from_numpy(inp.B).to(dev)
-        fn = rt.gemm_f32_raw
+        fn = rt.gemm_f32_raw if args.algo == 0 else (
+            lambda *a: rt.regtile_gemm_f32_algo(args.algo, *a))
     else:
         A = torch.from_numpy(inp.A.view(np.int16)).to(dev)
         B = torch.from_numpy(inp.B.view(np.int16)).to(dev)
-        fn = rt.gemm_bf16_raw
+        fn = rt.gemm_bf16_raw if args.algo == 0 else (
+            lambda *a: rt.regtile_gemm_bf16_algo(args.algo, *a))
     C = (torch.from_numpy(inp.C).to(dev) if inp.C is not None
          else torch.empty((w.M, w.N), dtype=torch.float32, device=dev))
     call = (w.M, w.N, w.K, w.alpha, A.data_ptr(), inp.lda, B.data_ptr(), inp.ldb, w.beta,
@@ -304,6 +309,19 @@ def main():
                          "kernel": kname, "kernel_ms_mean": round(kms, 4),
                          "kernel_ms_min": round(kmin, 4), "flop_per_launch": wb.flop},
         }
+
+        # the same tiles and pipeline on 16x16x32 MFMA fragments (the fragment-shape rung)
+        def step_bf16_16():
+            st = rt.regtile_gemm_bf16_algo(rt.ALGO_BF16_MFMA_16X16, *bf_args)
+            if st:
+                raise rt.RegtileError(st, rt.strerror(st))
+
+        step_bf16_16()
+        k16 = rt.last_kernel()
+        _, kms16, _ = _time(torch, step_bf16_16, args.steps, args.warmup)
+        out["bf16_8192"]["mfma_16x16x32"] = {
+            "kernel": k16, "kernel_ms_mean": round(kms16, 4),
+            "TFLOP/s": round(wb.flop / (kms16 * 1e-3) / 1e12, 2)}
         del Ab, Bb, Cb
 
     # ---- the ladder on the headline workload ------------------------------------------------
@@ -323,6 +341,10 @@ def main():
             ladder["mfma_bf16_8192"] = {"kernel": out["bf16_8192"]["roofline"]["kernel"],
                                         "kernel_ms": out["bf16_8192"]["roofline"]["kernel_ms_mean"],
                                         "TFLOP/s": out["bf16_8192"]["roofline"]["achieved"]}
+            ladder["mfma16_bf16_8192"] = {
+                "kernel": out["bf16_8192"]["mfma_16x16x32"]["kernel"],
+                "kernel_ms": out["bf16_8192"]["mfma_16x16x32"]["kernel_ms_mean"],
+                "TFLOP/s": out["bf16_8192"]["mfma_16x16x32"]["TFLOP/s"]}
         out["ladder"] = ladder
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------

@@ -64,7 +64,10 @@ enum regtile_algo_f32 {
 enum regtile_algo_bf16 {
     REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
     REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
-    REGTILE_BF16_MFMA = 2    /* LDS-tiled, wave-level MFMA fragments, fp32 accumulators */
+    REGTILE_BF16_MFMA = 2,   /* LDS-tiled, wave-level 32x32x16 MFMA fragments, fp32 accumulators */
+    REGTILE_BF16_MFMA_16X16 = 3 /* the same with 16x16x32 fragments on full aligned 256x256
+                                   tiles (other shapes as REGTILE_BF16_MFMA): the shape
+                                   comparison ("寄存器Tiling跨架构解析" section 3.1) */
 };
 
 /*

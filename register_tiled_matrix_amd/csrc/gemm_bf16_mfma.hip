@@ -195,13 +195,14 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
-hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name) {
-    {
-        const hipError_t e = launch_bf16_mfma_dma(p, s, name);
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape) {
+    // Full aligned 256x256 tiles, enough of them to fill the chip: the LDS-DMA kernel,
+    // else the register-staged kernel below.
+    if ((int64_t)(p.M / 256) * (p.N / 256) >= 128) {
+        const hipError_t e = launch_bf16_mfma_dma(p, s, name, shape);
         if (e != hipErrorNotSupported) return e;
     }
     const bool vec = (p.lda % 8) == 0 && (p.ldb % 8) == 0 && aligned16(p.A) && aligned16(p.B);

@@ -25,46 +25,15 @@
 //    WTN/32 B fragments (one 16-byte LDS read each) and issues (WTM/32)*(WTN/32) MFMAs, so
 //    LDS reads per MFMA fall as the wave tile grows.
 //  * Tile order: contiguous blocks of tiles per XCD, grouped 8 tile-rows at a time.
-#include <type_traits>
-
+#include "mfma_common.h"
 #include "regtile_internal.h"
 
 namespace regtile {
 
 namespace {
+using namespace mfma;
 
-typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-
-template <int KCH>
-__device__ __forceinline__ int slab_key(int row) {
-    static_assert(KCH == 4 || KCH == 8, "slab rows of 64 or 128 bytes");
-    if (KCH == 8) return (row & 7) ^ ((row >> 3) & 1);
-    return (row >> 2) & 3;
-}
-
-// One 16-byte-per-lane DMA load: global `src` -> LDS at `dst` + lane * 16 (dst wave-uniform).
-// The body exists only in the device pass: the host pass cannot form LDS-space pointers.
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-#else
-    (void)src;
-    (void)dst;
-#endif
-}
-
-// s_waitcnt lgkmcnt(0) only (LDS reads; LDS DMA is counted by vmcnt, not lgkmcnt).
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, int MF>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -72,13 +41,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int KCH = BK / 8;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    constexpr int MI = WTM / 32, NI = WTN / 32;
+    typedef Frag<MF> F;
+    constexpr int MI = WTM / MF, NI = WTN / MF;
     constexpr int A_SLOTS = BM * KCH, B_SLOTS = BN * KCH;  // 16-byte slots per stage
     constexpr int STAGE_SLOTS = A_SLOTS + B_SLOTS;
     constexpr int JA = A_SLOTS / (64 * NWAVES), JB = B_SLOTS / (64 * NWAVES);
     constexpr int PER_SLAB = JA + JB;  // DMA instructions per wave per slab
     static_assert(A_SLOTS % (64 * NWAVES) == 0 && B_SLOTS % (64 * NWAVES) == 0, "even DMA split");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 16 == 0, "fragment shapes");
+    static_assert(WTM % MF == 0 && WTN % MF == 0 && BK % F::KSTEP == 0, "fragment shapes");
     static_assert(PER_SLAB * (STAGES - 1) < 64, "vmcnt range");
 
     __shared__ uint4 smem[STAGES * STAGE_SLOTS];
@@ -126,29 +96,30 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             dma16(b_src(j) + k0, sb + (wave * JB + j) * 64);
     };
 
-    f32x16 acc[MI][NI];
+    typename F::acc_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            for (int v = 0; v < F::NACC; ++v) acc[i][j][v] = 0.0f;
 
-    const int frag_r = lane & 31;
-    const int frag_kh = lane >> 5;
+    const int frag_r = lane % MF;   // fragment row (A) / column (B) of this lane
+    const int frag_kg = lane / MF;  // its group of 8 k values within the instruction's k step
 
-    // Fragment reads of one 16-wide k step into register buffer `buf`.
+    // Fragment reads of one k step (F::KSTEP wide) into register buffer `buf`. Every group
+    // of MF lanes reads MF consecutive slab rows at one chunk: conflict-free under the key.
     bf16x8 fa[2][MI], fb[2][NI];
     auto read_frags = [&](const uint4 *sa, const uint4 *sb, int kk, int buf) {
-        const int chunk = kk * 2 + frag_kh;
+        const int chunk = kk * (F::KSTEP / 8) + frag_kg;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int row = wm * WTM + i * 32 + frag_r;
+            const int row = wm * WTM + i * MF + frag_r;
             fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH>(row))]);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int row = wn * WTN + j * 32 + frag_r;
+            const int row = wn * WTN + j * MF + frag_r;
             fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH>(row))]);
         }
     };
@@ -158,7 +129,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // instruction occupies the wave's issue for about 20 cycles (the address unit moves
     // 64 bytes per clock), less than one 32-cycle MFMA, so spread out it costs no matrix
     // cycles, while a burst of them would stall the MFMAs queued behind it.
-    constexpr int KSTEPS = BK / 16;
+    constexpr int KSTEPS = BK / F::KSTEP;
     constexpr int NMFMA = MI * NI;
     constexpr int NREAD = MI + NI;
     constexpr int DMA_PER_STEP = (PER_SLAB + KSTEPS - 1) / KSTEPS;
@@ -186,7 +157,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
             // issue order: every MFMA is followed by at most one read or one DMA
             const int reads = (kk + 1 < KSTEPS) ? NREAD : 0;
             const int dmas = (kk * DMA_PER_STEP < PER_SLAB)
@@ -227,43 +198,40 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     }
     wait_vmcnt<0>();  // no LDS DMA may still be in flight when the workgroup retires
 
-    // Epilogue: accumulator v of lane l in a 32x32 block holds row (v/4)*8 + (l/32)*4 + v%4,
-    // column l%32. beta == 0 never reads C.
+    // Epilogue: accumulator v of a fragment lands at (row_lane + row_acc(v), lane % MF) of
+    // its MF x MF block. beta == 0 never reads C.
     const bool read_c = beta != 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + frag_r;
-            float *cbase = C + (int64_t)(m0 + wm * WTM + i * 32 + frag_kh * 4) * ldc + col;
+            const int col = n0 + wn * WTN + j * MF + frag_r;
+            float *cbase = C + (int64_t)(m0 + wm * WTM + i * MF + F::row_lane(lane)) * ldc + col;
             if (read_c) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    float *c = cbase + (int64_t)((v >> 2) * 8 + (v & 3)) * ldc;
+                for (int v = 0; v < F::NACC; ++v) {
+                    float *c = cbase + (int64_t)F::row_acc(v) * ldc;
                     *c = fmaf(alpha, acc[i][j][v], beta * *c);
                 }
             } else {
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    cbase[(int64_t)((v >> 2) * 8 + (v & 3)) * ldc] = alpha * acc[i][j][v];
+                for (int v = 0; v < F::NACC; ++v)
+                    cbase[(int64_t)F::row_acc(v) * ldc] = alpha * acc[i][j][v];
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int MF>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, STAGES, WM, WN>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, STAGES, WM, WN, MF>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-#define REGTILE_STR2(x) #x
-#define REGTILE_STR(x) REGTILE_STR2(x)
 
 #ifndef DMA_BM
 #define DMA_BM 256
@@ -278,14 +246,21 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Returns hipErrorNotSupported (and launches nothing) unless the problem is made of full
 // tiles with 16-byte aligned, K-contiguous rows.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name) {
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape) {
     const bool ok = p.M % DMA_BM == 0 && p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
                     p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
-                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128;
+                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128 && (shape == 32 || shape == 16);
     if (!ok) return hipErrorNotSupported;
-    *name = "bf16_mfma_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)
-            "_s" REGTILE_STR(DMA_STAGES) "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN);
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN>(p, s);
+#define REGTILE_DMA_NAME(mf)                                                                   \
+    "bf16_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK) \
+        "_s" REGTILE_STR(DMA_STAGES) "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN)
+    if (shape == 16) {
+        *name = REGTILE_DMA_NAME("16x16x32");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN, 16>(p, s);
+    }
+    *name = REGTILE_DMA_NAME("32x32x16");
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN, 32>(p, s);
+#undef REGTILE_DMA_NAME
 }
 
 }  // namespace regtile

@@ -263,7 +263,6 @@ hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, bool va, bool
     return va ? pick_b<EDGE, true>(p, s, tm, tn, vb, vc) : pick_b<EDGE, false>(p, s, tm, tn, vb, vc);
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 

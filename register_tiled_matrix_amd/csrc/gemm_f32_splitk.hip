@@ -221,7 +221,6 @@ hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, int spw, bool
     return va ? pick_b<G, true>(p, s, tm, tn, spw, vb, vc) : pick_b<G, false>(p, s, tm, tn, spw, vb, vc);
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 

@@ -1,0 +1,89 @@
+// mfma_common.h -- device helpers shared by the bf16 MFMA kernels that stage operands with
+// LDS DMA: fragment types, the slab swizzle, the DMA load, counter waits, a barrier that
+// waits on nothing, and the two gfx950 bf16 MFMA fragment shapes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace regtile {
+namespace mfma {
+
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+template <int KCH>
+__device__ __forceinline__ int slab_key(int row) {
+    static_assert(KCH == 4 || KCH == 8, "slab rows of 64 or 128 bytes");
+    if (KCH == 8) return (row & 7) ^ ((row >> 3) & 1);
+    return (row >> 2) & 3;
+}
+
+// One 16-byte-per-lane DMA load: global `src` -> LDS at `dst` + lane * 16 (dst wave-uniform).
+// The body exists only in the device pass: the host pass cannot form LDS-space pointers.
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+#else
+    (void)src;
+    (void)dst;
+#endif
+}
+
+// s_waitcnt lgkmcnt(0) only (LDS reads; LDS DMA is counted by vmcnt, not lgkmcnt).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The two gfx950 bf16 MFMA fragment shapes. Per lane: 8 bf16 of A (row lane % MF, k group
+// lane / MF), 8 bf16 of B (column lane % MF, same k group), and MF*MF/64 fp32 accumulators.
+//   MF = 32: v_mfma_f32_32x32x16_bf16, 16 k per instruction, accumulator v of lane l holds
+//            row (v/4)*8 + (l/32)*4 + v%4, column l%32;
+//   MF = 16: v_mfma_f32_16x16x32_bf16, 32 k per instruction, accumulator v holds row
+//            (l/16)*4 + v, column l%16.
+// The row splits into a per-lane part (row_lane) and a compile-time per-accumulator part
+// (row_acc), so the epilogue's address arithmetic stays constant offsets.
+template <int MF>
+struct Frag;
+template <>
+struct Frag<32> {
+    typedef f32x16 acc_t;
+    static constexpr int KSTEP = 16, NACC = 16;
+    __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row_lane(int lane) { return (lane >> 5) * 4; }
+    __device__ static constexpr int row_acc(int v) { return (v >> 2) * 8 + (v & 3); }
+};
+template <>
+struct Frag<16> {
+    typedef f32x4 acc_t;
+    static constexpr int KSTEP = 32, NACC = 4;
+    __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static int row_lane(int lane) { return (lane >> 4) * 4; }
+    __device__ static constexpr int row_acc(int v) { return v; }
+};
+
+// Workgroup barrier without the memory fence that __syncthreads() adds: the fence makes
+// the compiler wait for every outstanding vector-memory operation (vmcnt(0)), which would
+// drain the LDS DMA of slabs still in flight. Callers wait for exactly what they need
+// (wait_vmcnt / wait_lgkmcnt0) before it. The empty asm statements keep the compiler from
+// moving LDS accesses across it; sched_barrier keeps the machine scheduler from doing so.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace mfma
+}  // namespace regtile

@@ -94,7 +94,7 @@ int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *
 
 int run_bf16(int shift, int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
              const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
-    if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA) return -1;
+    if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA_16X16) return -1;
     const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
@@ -105,7 +105,8 @@ int run_bf16(int shift, int algo, int M, int N, int K, float alpha, const uint16
     hipError_t err;
     switch (algo) {
         case REGTILE_BF16_NAIVE: err = regtile::launch_bf16_naive(p, s, &name); break;
-        default: err = regtile::launch_bf16_mfma(p, s, &name); break;
+        case REGTILE_BF16_MFMA_16X16: err = regtile::launch_bf16_mfma(p, s, &name, 16); break;
+        default: err = regtile::launch_bf16_mfma(p, s, &name, 32); break;
     }
     return finish(err, name);
 }

@@ -27,9 +27,16 @@ hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name);
-hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name);
-// Full aligned tiles only; returns hipErrorNotSupported without launching otherwise.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name);
+// MFMA kernels; `shape` 32 selects 32x32x16 fragments, 16 selects 16x16x32 (full aligned
+// tiles only, others keep the 32x32x16 register-staged kernel).
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape);
+// Full aligned tiles only; return hipErrorNotSupported without launching otherwise.
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape);
+
+// Host-side launch checks.
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+#define REGTILE_STR2(x) #x
+#define REGTILE_STR(x) REGTILE_STR2(x)
 
 // C element update shared by every kernel's epilogue: beta == 0 never reads C.
 __device__ __forceinline__ float epilogue_value(float acc, float alpha, float beta,

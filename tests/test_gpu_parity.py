@@ -14,14 +14,16 @@ import pytest
 import gemm_inputs as gi
 import oracle
 import register_tiled_matrix_amd as rt
-from gpu_util import announce, assert_parity_full, assert_parity_sampled, device_operands, run
+from gpu_util import (announce, assert_parity_full, assert_parity_sampled, device_operands, run,
+                      sample_positions)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS, rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK,
              rt.ALGO_F32_AUTO]
-BF16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_AUTO]
+BF16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16, rt.ALGO_BF16_AUTO]
+BF16_MFMA_ALGOS = [rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,12 +67,14 @@ def test_f32_tall_sampled():
     assert_parity_sampled(inp, got, "f32_tall")
 
 
-def test_bf16_8192_sampled():
+@pytest.mark.parametrize("algo", [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16])
+def test_bf16_8192_sampled(algo):
     inp = gi.workload_inputs(gi.WORKLOADS["bf16_8192"])
-    announce("bf16_8192 default entry point")
-    got = run(inp, torch).cpu().numpy()
-    assert "mfma" in rt.last_kernel()
-    assert_parity_sampled(inp, got, "bf16_8192", n_random=30000)
+    announce(f"bf16_8192 algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    shape = "16x16x32" if algo == rt.ALGO_BF16_MFMA_16X16 else "32x32x16"
+    assert f"mfma{shape}_dma" in rt.last_kernel()
+    assert_parity_sampled(inp, got, f"bf16_8192 ({rt.last_kernel()})", n_random=30000)
 
 
 # ---- bf16 at a size the oracle finishes in full -----------------------------------------
@@ -83,7 +87,7 @@ def test_bf16_full(algo, shape):
     announce(f"bf16 {shape} algo={algo}")
     got = run(inp, torch, algo).cpu().numpy()
     if shape == (2048, 4096, 192) and algo != rt.ALGO_BF16_NAIVE:
-        assert "dma" in rt.last_kernel()  # full aligned 256x256 tiles take the DMA kernel
+        assert "_dma_" in rt.last_kernel()  # full aligned 256x256 tiles take the LDS-DMA kernel
     assert_parity_full(inp, got, f"bf16 {shape} algo {algo} ({rt.last_kernel()})")
 
 
@@ -103,12 +107,13 @@ def test_f32_regtile_edges(shape, algo):
     assert_parity_full(inp, got, f"f32 edges {shape} ({rt.last_kernel()})")
 
 
+@pytest.mark.parametrize("algo", BF16_MFMA_ALGOS)
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
-def test_bf16_mfma_edges(shape):
+def test_bf16_mfma_edges(shape, algo):
     M, N, K = shape
     inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=-1.25, beta=0.75, seed=M * 7 + N + K)
-    announce(f"bf16 edges {shape}")
-    got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    announce(f"bf16 edges {shape} algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
     assert_parity_full(inp, got, f"bf16 edges {shape}")
 
 
@@ -136,6 +141,22 @@ def test_bf16_integer_inputs_are_bitwise_exact():
     got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
     ref, _ = oracle.gemm_inputs(inp)
     assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("algo", BF16_MFMA_ALGOS)
+def test_bf16_full_tile_integer_inputs_are_bitwise_exact(algo):
+    # 128 full 256x256 tiles: the LDS-DMA kernels; |partial sums| <= 2^18, exact in fp32
+    rng = np.random.Generator(np.random.PCG64(79))
+    M, N, K = 2048, 4096, 1024
+    A = gi.f32_to_bf16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_bf16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, A, Bt, None)
+    announce(f"bf16 full-tile integer bitwise algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    assert "_dma_" in rt.last_kernel()
+    I, J = sample_positions(M, N, n_random=50000, seed=3)
+    ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref)
 
 
 def test_closed_forms_on_gpu():
