@@ -17,14 +17,17 @@
 //    distinct 16-byte bank groups:
 //      KCH = 8 (128-byte rows): key(r) = (r & 7) ^ ((r >> 3) & 1)
 //      KCH = 4 ( 64-byte rows): key(r) = (r >> 2) & 3
-//  * STAGES slabs in flight: slab s+STAGES-1 is requested while slab s is consumed, and
-//    each wave waits (s_waitcnt vmcnt) only for the slab it is about to read; one barrier
-//    per slab both publishes that slab and retires the stage the next request overwrites
-//    (section 6.3: prefetch of the next k-slice while the current one is computed).
+//  * Two LDS stages and one barrier per slab, placed inside the slab's last k step: the
+//    next slab is loaded while the current one is consumed, and its first fragments are
+//    read before the current slab's last MFMAs (section 6.3: prefetch of the next k slice
+//    while the current one is computed). The barrier carries no memory fence; each wave
+//    waits (s_waitcnt vmcnt) for exactly its own loads before it.
 //  * Wave tile WTM x WTN of 32x32 blocks: per 16-wide k step a wave reads WTM/32 A and
 //    WTN/32 B fragments (one 16-byte LDS read each) and issues (WTM/32)*(WTN/32) MFMAs, so
 //    LDS reads per MFMA fall as the wave tile grows.
 //  * Tile order: contiguous blocks of tiles per XCD, grouped 8 tile-rows at a time.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "regtile_internal.h"
 
@@ -33,7 +36,7 @@ namespace regtile {
 namespace {
 using namespace mfma;
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, int MF>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -49,12 +52,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int PER_SLAB = JA + JB;  // DMA instructions per wave per slab
     static_assert(A_SLOTS % (64 * NWAVES) == 0 && B_SLOTS % (64 * NWAVES) == 0, "even DMA split");
     static_assert(WTM % MF == 0 && WTN % MF == 0 && BK % F::KSTEP == 0, "fragment shapes");
-    static_assert(PER_SLAB * (STAGES - 1) < 64, "vmcnt range");
+    static_assert(PER_SLAB < 64, "vmcnt range");
+    constexpr int STAGES = 2;
 
     __shared__ uint4 smem[STAGES * STAGE_SLOTS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // wave-uniform by construction; readfirstlane tells the compiler so (scalar registers
+    // for everything derived from it, and a scalar M0 for the LDS DMA destination)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     int tm, tn;
@@ -65,35 +71,33 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // chunk (p % KCH) ^ key(row) of tile row p / KCH. One instruction covers 64/KCH rows, so
     // instruction j's row is instruction (j & 1)'s row plus a uniform (j & ~1) * 64/KCH, and
     // its key equals instruction (j & 1)'s (the key depends on the row only through bits that
-    // an even number of instructions leaves unchanged): two per-lane pointers per operand.
+    // an even number of instructions leaves unchanged). Loads go through buffer descriptors
+    // over the tile's BM rows of A and BN rows of B: per lane two 32-bit byte offsets per
+    // operand; instruction and slab offsets are wave-uniform (SGPR).
     constexpr int ROWS_PER_INSTR = 64 / KCH;
     static_assert(KCH == 4 || (ROWS_PER_INSTR == 8 && JA % 2 == 0 && JB % 2 == 0), "key periodicity");
-    const uint16_t *a_lane[2];
-    const uint16_t *b_lane[2];
+    const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(BM * lda * 2));
+    const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(BN * ldb * 2));
+    uint32_t a_voff[2], b_voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int pa = (wave * JA + j) * 64 + lane;
         const int ra = pa / KCH, ca = (pa % KCH) ^ slab_key<KCH>(ra);
-        a_lane[j] = A + (int64_t)(m0 + ra) * lda + ca * 8;
+        a_voff[j] = (uint32_t)(ra * lda + ca * 8) * 2u;
         const int pb = (wave * JB + j) * 64 + lane;
         const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH>(rb);
-        b_lane[j] = B + (int64_t)(n0 + rb) * ldb + cb * 8;
+        b_voff[j] = (uint32_t)(rb * ldb + cb * 8) * 2u;
     }
-    const int64_t a_step = (int64_t)ROWS_PER_INSTR * lda;  // per instruction pair: 2 * a_step
-    const int64_t b_step = (int64_t)ROWS_PER_INSTR * ldb;
-    auto a_src = [&](int j) { return a_lane[j & 1] + (j & ~1) * a_step; };
-    auto b_src = [&](int j) { return b_lane[j & 1] + (j & ~1) * b_step; };
-
-    auto issue = [&](int slab, int stage) {
-        const int k0 = slab * BK;
-        uint4 *sa = smem + stage * STAGE_SLOTS;
-        uint4 *sb = sa + A_SLOTS;
-#pragma unroll
-        for (int j = 0; j < JA; ++j)
-            dma16(a_src(j) + k0, sa + (wave * JA + j) * 64);
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-            dma16(b_src(j) + k0, sb + (wave * JB + j) * 64);
+    const uint32_t a_step = (uint32_t)(ROWS_PER_INSTR * lda) * 2u;  // bytes per instruction
+    const uint32_t b_step = (uint32_t)(ROWS_PER_INSTR * ldb) * 2u;
+    // DMA instruction q (A for q < JA, then B) of the slab starting at k0.
+    auto dma_q = [&](int q, int k0, uint4 *sa, uint4 *sb) {
+        if (q < JA)
+            dma16_buf(a_rsrc, a_voff[q & 1], (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u,
+                      sa + (wave * JA + q) * 64);
+        else
+            dma16_buf(b_rsrc, b_voff[(q - JA) & 1], (uint32_t)((q - JA) & ~1) * b_step + (uint32_t)k0 * 2u,
+                      sb + (wave * JB + (q - JA)) * 64);
     };
 
     typename F::acc_t acc[MI][NI];
@@ -123,109 +127,151 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH>(row))]);
         }
     };
-    // One slab. Each 16-wide k step starts by waiting for its own fragments (read during the
-    // previous step), then issues its MFMAs with the next step's fragment reads and a share
-    // of the next slab's DMA loads woven between them: MFMA, read, MFMA, DMA, ... A 1 KB DMA
-    // instruction occupies the wave's issue for about 20 cycles (the address unit moves
-    // 64 bytes per clock), less than one 32-cycle MFMA, so spread out it costs no matrix
-    // cycles, while a burst of them would stall the MFMAs queued behind it.
+    // One slab is KSTEPS k steps. Each starts by waiting for its own fragments (read during
+    // the previous step) and issues its MFMAs with the next step's fragment reads and a
+    // window of DMA loads woven between them: MFMA, read, MFMA, DMA, ... so the matrix pipe
+    // never waits on an LDS round trip, and DMA issue (which can hold the wave while the
+    // CU's address unit is busy) is spread thin.
+    //
+    // Two LDS stages, cur = s % 2 and nxt. The single barrier of a slab sits at the start
+    // of its last k step, when every wave has its last fragments of stage cur in registers
+    // and has waited for its own loads of slab s+1. After it, stage nxt is published and
+    // stage cur is free, so the same k step already reads slab s+1's first fragments and
+    // starts loading slab s+2 into stage cur. The DMA of a slab goes out in NWIN windows:
+    // right after that barrier, then in the first NWIN-1 k steps of the next slab, so every
+    // load has more than a k step to land before the barrier that waits for it.
     constexpr int KSTEPS = BK / F::KSTEP;
     constexpr int NMFMA = MI * NI;
     constexpr int NREAD = MI + NI;
-    constexpr int DMA_PER_STEP = (PER_SLAB + KSTEPS - 1) / KSTEPS;
-    static_assert(NREAD <= NMFMA && DMA_PER_STEP <= NMFMA, "one extra instruction per MFMA slot");
-    auto compute = [&](int stage, int next_slab, int next_stage) {
-        const uint4 *sa = smem + stage * STAGE_SLOTS;
-        const uint4 *sb = sa + A_SLOTS;
-        const int k0n = next_slab * BK;
-        uint4 *na = smem + next_stage * STAGE_SLOTS;
-        uint4 *nb = na + A_SLOTS;
-        read_frags(sa, sb, 0, 0);
+    constexpr int NWIN = KSTEPS - 1 < WINDOWS ? KSTEPS - 1 : WINDOWS;
+    constexpr int DMA_PER_WIN = (PER_SLAB + NWIN - 1) / NWIN;
+    static_assert(KSTEPS % 2 == 0 && NWIN >= 1, "even number of k steps per slab");
+    static_assert(NREAD <= NMFMA && DMA_PER_WIN <= NMFMA, "one extra instruction per MFMA slot");
+
+    auto dma_window = [&](int slab, int stage, int win) {
+        const int k0 = slab * BK;
+        uint4 *sa = smem + stage * STAGE_SLOTS;
+        uint4 *sb = sa + A_SLOTS;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const int cb = kk & 1;
-            wait_lgkmcnt0();  // this step's fragments have landed
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < KSTEPS) read_frags(sa, sb, kk + 1, cb ^ 1);
-#pragma unroll
-            for (int d = 0; d < DMA_PER_STEP; ++d) {
-                const int q = kk * DMA_PER_STEP + d;  // DMA instruction index within the slab
-                if (q < JA) dma16(a_src(q) + k0n, na + (wave * JA + q) * 64);
-                else if (q < PER_SLAB) dma16(b_src(q - JA) + k0n, nb + (wave * JB + (q - JA)) * 64);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
-            // issue order: every MFMA is followed by at most one read or one DMA
-            const int reads = (kk + 1 < KSTEPS) ? NREAD : 0;
-            const int dmas = (kk * DMA_PER_STEP < PER_SLAB)
-                                     ? ((PER_SLAB - kk * DMA_PER_STEP) < DMA_PER_STEP
-                                            ? (PER_SLAB - kk * DMA_PER_STEP) : DMA_PER_STEP)
-                                     : 0;
-            int r_left = reads, d_left = dmas;
-#pragma unroll
-            for (int g = 0; g < NMFMA; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                // spread reads and DMAs evenly over the MFMA slots
-                const bool want_dma = d_left > 0 && (g * dmas) / NMFMA != ((g + 1) * dmas) / NMFMA;
-                if (want_dma) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                    --d_left;
-                } else if (r_left > 0) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    --r_left;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int d = 0; d < DMA_PER_WIN; ++d) {
+            const int q = win * DMA_PER_WIN + d;  // DMA instruction index within the slab
+            if (q < PER_SLAB) dma_q(q, k0, sa, sb);
         }
     };
+    auto dmas_in = [](int win) {
+        const int left = PER_SLAB - win * DMA_PER_WIN;
+        return left <= 0 ? 0 : (left < DMA_PER_WIN ? left : DMA_PER_WIN);
+    };
+    // MFMAs of buffer cb; every MFMA is followed by at most one fragment read or one DMA.
+    auto mfma_woven = [&](int cb, int reads, int dmas) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+        int r_left = reads, d_left = dmas;
+#pragma unroll
+        for (int g = 0; g < NMFMA; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            const bool want_dma = d_left > 0 && (g * dmas) / NMFMA != ((g + 1) * dmas) / NMFMA;
+            if (want_dma) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                --d_left;
+            } else if (r_left > 0) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                --r_left;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // Every iteration requests exactly one slab, so the wait count is the same each time.
-    // Past the end the request is clamped to the last slab: it rewrites a stage that has
-    // already been consumed with valid data and keeps the loop body uniform.
+    // Past the end, requests are clamped to the last slab: they refill a stage nobody reads
+    // again with valid data and keep every iteration identical (same counts at every wait).
     const int nslabs = K / BK;
 #pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t) issue(min(t, nslabs - 1), t);
+    for (int q = 0; q < PER_SLAB; ++q) dma_q(q, 0, smem, smem + A_SLOTS);
+    wait_vmcnt<0>();
+    lds_barrier();
+    read_frags(smem, smem + A_SLOTS, 0, 0);
 
-    for (int s = 0; s < nslabs; ++s) {
-        // Slab s must have landed; the requests of the STAGES-2 slabs after it may still fly.
-        wait_vmcnt<PER_SLAB * (STAGES - 2)>();
-        __syncthreads();
-        const int next = s + STAGES - 1;
-        compute(s % STAGES, min(next, nslabs - 1), next % STAGES);
-    }
+    // DMA windows sit at positions of the k-step sequence: position 0 is the last k step of
+    // a slab (after its barrier), position p >= 1 is k step p-1 of the next slab. Window w of
+    // a wave with shift SH sits at position SH + w. With STAGGER the second half of the
+    // waves is shifted by one position, so on each SIMD (waves w and w + 4 of eight share
+    // one) only one wave issues DMA in a given k step while the other keeps the matrix pipe
+    // busy, and the CU's address unit sees half the burst.
+    auto main_loop = [&](auto shift_tag) {
+        constexpr int SH = decltype(shift_tag)::value;
+        static_assert(SH + NWIN <= KSTEPS, "every window lands at least one k step before its barrier");
+        if (SH == 0) dma_window(min(1, nslabs - 1), 1, 0);
+        for (int s = 0; s < nslabs; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            const uint4 *sa = smem + cur * STAGE_SLOTS, *sb = sa + A_SLOTS;
+            const uint4 *na = smem + nxt * STAGE_SLOTS, *nb = na + A_SLOTS;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const int cb = kk & 1;
+                wait_lgkmcnt0();  // this step's fragments have landed
+                if (kk + 1 < KSTEPS) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_frags(sa, sb, kk + 1, cb ^ 1);
+                    const int win = kk + 1 - SH;
+                    const bool has = win >= 0 && win < NWIN;
+                    if (has) dma_window(min(s + 1, nslabs - 1), nxt, win);
+                    mfma_woven(cb, NREAD, has ? dmas_in(win) : 0);
+                } else {
+                    wait_vmcnt<0>();  // own loads of slab s+1 have landed
+                    lds_barrier();    // slab s+1 published; stage cur read by nobody any more
+                    read_frags(na, nb, 0, cb ^ 1);
+                    if (SH == 0) dma_window(min(s + 2, nslabs - 1), cur, 0);
+                    mfma_woven(cb, NREAD, SH == 0 ? dmas_in(0) : 0);
+                }
+            }
+        }
+    };
+    if (STAGGER && wave >= NWAVES / 2)
+        main_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
+    else
+        main_loop(std::integral_constant<int, 0>{});
     wait_vmcnt<0>();  // no LDS DMA may still be in flight when the workgroup retires
 
     // Epilogue: accumulator v of a fragment lands at (row_lane + row_acc(v), lane % MF) of
-    // its MF x MF block. beta == 0 never reads C.
-    const bool read_c = beta != 0.0f;
+    // its MF x MF block. Stores go through a buffer descriptor over the tile's BM rows of C:
+    // one per-lane byte offset for the whole epilogue, the (i, j, v) part wave-uniform (the
+    // launch checks that BM rows of C span less than 2^31 bytes). beta == 0 never reads C.
+    const rsrc_t c_rsrc = make_rsrc(C + (int64_t)m0 * ldc + n0, (uint32_t)(BM * ldc * 4));
+    // (the lane index is recomputed from mbcnt so no thread-id register stays live across
+    // the main loop)
+    const int elane = __lane_id();
+    const uint32_t lane_off =
+        (uint32_t)((wm * WTM + F::row_lane(elane)) * ldc + wn * WTN + elane % MF) * 4u;
+    auto c_off = [&](int i, int j, int v) {
+        return (uint32_t)((i * MF + F::row_acc(v)) * ldc + j * MF) * 4u;
+    };
+    if (beta != 0.0f) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int col = n0 + wn * WTN + j * MF + frag_r;
-            float *cbase = C + (int64_t)(m0 + wm * WTM + i * MF + F::row_lane(lane)) * ldc + col;
-            if (read_c) {
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int v = 0; v < F::NACC; ++v) {
-                    float *c = cbase + (int64_t)F::row_acc(v) * ldc;
-                    *c = fmaf(alpha, acc[i][j][v], beta * *c);
+                    const float c = load_f32_buf(c_rsrc, lane_off, c_off(i, j, v));
+                    store_f32_buf(c_rsrc, lane_off, c_off(i, j, v), fmaf(alpha, acc[i][j][v], beta * c));
                 }
-            } else {
+    } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int v = 0; v < F::NACC; ++v)
-                    cbase[(int64_t)F::row_acc(v) * ldc] = alpha * acc[i][j][v];
-            }
-        }
+                    store_f32_buf(c_rsrc, lane_off, c_off(i, j, v), alpha * acc[i][j][v]);
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, int MF>
+template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, STAGES, WM, WN, MF>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -237,9 +283,16 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 #define DMA_BM 256
 #define DMA_BN 256
 #define DMA_BK 64
-#define DMA_STAGES 2
 #define DMA_WM 2
 #define DMA_WN 2
+#endif
+// DMA windows per slab and stagger, per fragment shape (tuned at 8192^3: one window right
+// after the barrier, the second half of the waves one k step later)
+#ifndef DMA_WIN32
+#define DMA_WIN32 1
+#define DMA_STAG32 1
+#define DMA_WIN16 1
+#define DMA_STAG16 0
 #endif
 
 }  // namespace
@@ -249,17 +302,20 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape) {
     const bool ok = p.M % DMA_BM == 0 && p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
                     p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
+                    (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
+                    (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31) &&
+                    (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
                     (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128 && (shape == 32 || shape == 16);
     if (!ok) return hipErrorNotSupported;
 #define REGTILE_DMA_NAME(mf)                                                                   \
     "bf16_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK) \
-        "_s" REGTILE_STR(DMA_STAGES) "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN)
+        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN)
     if (shape == 16) {
         *name = REGTILE_DMA_NAME("16x16x32");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN, 16>(p, s);
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16>(p, s);
     }
     *name = REGTILE_DMA_NAME("32x32x16");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_STAGES, DMA_WM, DMA_WN, 32>(p, s);
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32>(p, s);
 #undef REGTILE_DMA_NAME
 }
 

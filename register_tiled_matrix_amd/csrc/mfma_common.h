@@ -31,6 +31,65 @@ __device__ __forceinline__ void dma16(const void *src, void *dst) {
 #endif
 }
 
+// Buffer descriptor over `bytes` bytes at `base`, raw (untyped) dword access: data format
+// 32 in the fourth descriptor word, stride 0 (num_records counts bytes), and the hardware
+// returns zero for any byte past num_records. Host-pass stubs exist only to type-check.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // The arguments are wave-uniform; readfirstlane states it, so the descriptor lives in
+    // scalar registers (a descriptor the compiler believes divergent gets a readfirstlane
+    // loop around every load).
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *ub = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+    rsrc_t r;
+    return r;
+#endif
+}
+
+// 16 bytes per lane from buffer byte offset voff + soff (soff wave-uniform) into LDS at
+// `dst` + lane * 16 (dst wave-uniform): buffer_load_dwordx4 ... lds.
+__device__ __forceinline__ void dma16_buf(rsrc_t r, uint32_t voff, uint32_t soff, void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16,
+                                             (int)voff, (int)soff, 0, 0);
+#else
+    (void)r;
+    (void)voff;
+    (void)soff;
+    (void)dst;
+#endif
+}
+
+// One fp32 per lane at buffer byte offset voff + soff (soff wave-uniform).
+__device__ __forceinline__ float load_f32_buf(rsrc_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+#else
+    (void)r;
+    (void)voff;
+    (void)soff;
+    return 0.0f;
+#endif
+}
+__device__ __forceinline__ void store_f32_buf(rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, 0);
+#else
+    (void)r;
+    (void)voff;
+    (void)soff;
+    (void)x;
+#endif
+}
+
 // s_waitcnt lgkmcnt(0) only (LDS reads; LDS DMA is counted by vmcnt, not lgkmcnt).
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
