@@ -52,12 +52,14 @@ extern "C" {
 /* Kernel ladder for the fp32 entry points ("Understanding Register Tiling", the three-version
  * comparison: naive -> shared memory -> register tiling). */
 enum regtile_algo_f32 {
-    REGTILE_F32_AUTO = 0,    /* library's choice among the register-tiled kernels (3 or 4) */
+    REGTILE_F32_AUTO = 0,    /* library's choice among the register-tiled kernels (3 or 5) */
     REGTILE_F32_NAIVE = 1,   /* one thread per C element, operands straight from HBM */
     REGTILE_F32_LDS = 2,     /* 32x32 LDS tiles, 1024 threads, one C element per thread */
-    REGTILE_F32_REGTILE = 3, /* 128x128 LDS tiles, 256 threads, 8x8 register micro-tiles */
-    REGTILE_F32_SPLITK = 4   /* 64x64 tiles, each of 4 waves an 8x8-micro-tiled quarter of K,
+    REGTILE_F32_REGTILE = 3, /* 128x256 LDS tiles, 256 threads, 8x16 register micro-tiles */
+    REGTILE_F32_SPLITK = 4,  /* 64x64 tiles, each of 4 waves an 8x8-micro-tiled quarter of K,
                                 partials summed in fixed order (shapes with few tiles) */
+    REGTILE_F32_REGTILE_SMALL = 5 /* 64x64 tiles, 256 threads, 4x4 register micro-tiles, 4 waves
+                                     per SIMD (shapes with few 128x256 tiles) */
 };
 
 /* Kernel ladder for the bf16 entry points. */
@@ -73,8 +75,9 @@ enum regtile_algo_bf16 {
 /*
  * gemm_f32 -- fp32 C = alpha*A*B + beta*C with fp32 FMA accumulation, on the register-tiled
  * kernel ("Understanding Register Tiling", the key loop; "寄存器Tiling跨架构解析" section 1.1):
- * 128x128 workgroup tiles, or for problems with fewer than two such tiles per CU the split-K
- * variant (section 2.4 / 7.2 of the second page: tile size against resident waves).
+ * 128x256 workgroup tiles of 8x16 micro-tiles, or for problems with fewer than two 128x128 tiles
+ * per CU 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD (section 2.4 / 7.2 of the second
+ * page: tile size against resident waves).
  *   M, N, K    (args 1-3)  sizes, >= 0
  *   alpha      (arg 4)     scale of A*B
  *   A, lda     (args 5-6)  device, row-major M x K, lda >= max(1,K); may be NULL if M*K == 0

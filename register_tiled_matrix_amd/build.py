@@ -42,8 +42,8 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str, extra: list[str]) -> tuple[str, str]:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], obj_dir: str = BUILD_DIR) -> tuple[str, str]:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON_FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,31 +64,37 @@ def _resource_report(logs: list[str]) -> str:
     return "\n".join(out) + "\n"
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every HIP source for gfx950 and link libregtile.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags: list[str] | None = None,
+          out_dir: str | None = None, jobs: int | None = None) -> str:
+    """Compile every HIP source for gfx950 and link libregtile.so; returns its path.
+
+    With ``out_dir`` (used for tuning variants built with other ``-D`` values) the objects,
+    the library and the resource report go there instead of the in-tree locations."""
+    obj_dir = out_dir or BUILD_DIR
+    lib = os.path.join(out_dir, "libregtile.so") if out_dir else LIB
+    os.makedirs(obj_dir, exist_ok=True)
     extra = list(extra_flags or [])
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, extra, obj_dir), SOURCES))
     objs = [o for o, _ in results]
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     report = _resource_report([log for _, log in results])
-    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(obj_dir, "resource_usage.txt"), "w") as f:
         f.write(report)
     if verbose:
-        print(f"built {LIB}", flush=True)
-    return LIB
+        print(f"built {lib}", flush=True)
+    return lib
 
 
-def resource_usage() -> dict:
-    """Parse _build/resource_usage.txt into {kernel: {field: value}}."""
-    path = os.path.join(BUILD_DIR, "resource_usage.txt")
+def resource_usage(build_dir: str | None = None) -> dict:
+    """Parse <build_dir>/resource_usage.txt (default _build/) into {kernel: {field: value}}."""
+    path = os.path.join(build_dir or BUILD_DIR, "resource_usage.txt")
     res: dict = {}
     cur = None
     with open(path) as f:

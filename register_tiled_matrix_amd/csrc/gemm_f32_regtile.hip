@@ -2,24 +2,26 @@
 //
 // Three-level tiling ("寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507) section 1.1: a
 // 128x128 block tile per workgroup of 256 threads, an 8x8 micro-tile per thread, 64 FMAs per
-// k step held entirely in registers):
+// k step held entirely in registers), here with a TM x TN micro-tile (default 8 x 16):
 //   HBM -> LDS      a BM x BK slab of A (stored k-major, i.e. transposed) and a BK x BN slab
 //                   of B per stage, two stages (the next slab's global loads are in flight
 //                   while the current slab is consumed; section 6.3's prefetch, done here
 //                   as double-buffered LDS plus register staging);
-//   LDS -> VGPR     per k: regA[8] (two 16-byte reads of a column of the A slab) and
-//                   regB[8] (two 16-byte reads of a row of the B slab) -- "Understanding
+//   LDS -> VGPR     per k: regA[TM] (TM/4 16-byte reads of a column of the A slab) and
+//                   regB[TN] (TN/4 16-byte reads of a row of the B slab) -- "Understanding
 //                   Register Tiling" (blog.csdn.net/sweet_ran), the key loop;
-//   VGPR FMA        acc[8][8] += regA[m] * regB[n]: 64 independent fp32 FMAs per k.
-// LDS reads per FMA: (TM + TN) / (TM * TN) = 16 / 64 = 0.25 floats, against 2 for the
-// one-output-per-thread kernel (the three-version comparison on the same page).
+//   VGPR FMA        acc[TM][TN] += regA[m] * regB[n]: TM*TN independent fp32 FMAs per k.
+// LDS reads per FMA: (TM + TN) / (TM * TN) floats (0.19 for 8x16, 0.25 for 8x8), against 2
+// for the one-output-per-thread kernel (the three-version comparison on the same page).
 //
-// Wave64 mapping. The 256 threads are 4 waves in a 2x2 grid; each wave owns a 64x64 quarter
-// and its 64 lanes form an 8x8 grid. A lane's 8 rows are {r0..r0+3, r0+32..r0+35} and its 8
-// columns {c0..c0+3, c0+32..c0+35}: the 4+4 split makes the 8 distinct 16-byte fragment
-// addresses of one wave-wide read a single contiguous 128-byte run (all 32 banks once, the
-// rest broadcasts), so fragment reads are free of bank conflicts (section 1.2/7.3 of the
-// same page: the register layout decides the LDS access pattern).
+// Wave64 mapping. The 256 threads are 4 waves in a 2x2 grid; each wave's 64 lanes form an
+// 8x8 grid, so the workgroup tile is BM = 16 TM by BN = 16 TN. A lane's rows are
+// r0 + 32 g + {0..3} (g < TM/4) and its columns c0 + 32 h + {0..3} (h < TN/4): the groups of
+// 4 make the 8 distinct 16-byte fragment addresses of one wave-wide read a single contiguous
+// 128-byte run (all banks once, the rest broadcasts), so fragment reads are free of bank
+// conflicts (section 1.2/7.3 of the same page: the register layout decides the LDS access
+// pattern). TM, TN, BK and waves per SIMD are compile-time choices (F32_TM, F32_TN, F32_BK,
+// F32_WAVES_PER_EU) so the micro-tile / occupancy trade of sections 2.4 and 7.2 can be swept.
 //
 // Every output accumulates fmaf over k in natural order, like rungs 0 and 1, so the three
 // fp32 rungs agree bitwise.
@@ -29,20 +31,42 @@ namespace regtile {
 
 namespace {
 
+// Kernel configurations (TM, TN, BK, waves per SIMD). The square one is the default
+// register-tiled kernel; the small one (64x64 tiles) serves problems with few 128x256 tiles.
+// The F32_* macros exist so other values can be built for the micro-tile sweep.
 #ifndef F32_TN
 #define F32_TN 16
 #endif
-// TM x TN micro-tile per lane: TM = 8 rows in two groups of 4 (32 rows apart), TN columns in
-// TN / 4 groups of 4 (32 columns apart). A wave is an 8x8 grid of lanes, 4 waves in 2x2.
-constexpr int TM = 8, TN = F32_TN, NG = TN / 4, NT = 256;
-constexpr int BM = 128, BN = 16 * TN;
-static_assert(TN == 8 || TN == 16, "8x8 or 8x16 micro-tiles");
+#ifndef F32_TM
+#define F32_TM 8
+#endif
+#ifndef F32_BK
+#define F32_BK 16
+#endif
 #ifndef F32_WAVES_PER_EU
 #define F32_WAVES_PER_EU 2
 #endif
+struct SquareCfg {
+    static constexpr int TM = F32_TM, TN = F32_TN, BK = F32_BK, WAVES = F32_WAVES_PER_EU;
+};
+struct SmallCfg {
+    static constexpr int TM = 4, TN = 4, BK = 32, WAVES = 4;
+};
+
+constexpr int NT = 256;
 constexpr int APAD = 4;  // A slab row stride BM + 4 floats: transposed stores hit 32 banks per half-wave
 
-template <int BK>
+// TM x TN micro-tile per lane: TM rows in TM / 4 groups of 4 (32 rows apart), TN columns in
+// TN / 4 groups of 4 (32 columns apart). A wave is an 8x8 grid of lanes, 4 waves in 2x2, so
+// the workgroup tile is 16 TM x 16 TN.
+template <int TM, int TN>
+struct Shape {
+    static_assert((TM == 4 || TM == 8 || TM == 16) && (TN == 4 || TN == 8 || TN == 16),
+                  "micro-tiles of 4, 8 or 16 rows and columns");
+    static constexpr int MG = TM / 4, NG = TN / 4, BM = 16 * TM, BN = 16 * TN;
+};
+
+template <int BM, int BN, int BK>
 struct alignas(16) Smem {
     float a[2][BK][BM + APAD];
     float b[2][BK][BN];
@@ -50,7 +74,7 @@ struct alignas(16) Smem {
 
 // Global -> register staging of one slab. A: BM x BK as BK/4 float4 chunks per row;
 // B: BK x BN as BN/4 float4 chunks per row. Each thread owns BK/8 chunks of each.
-template <int BK, bool EDGE, bool VEC>
+template <bool EDGE, bool VEC>
 __device__ __forceinline__ float4 load4_rowwise(const float *__restrict__ p, int rows_left,
                                                 int cols_left) {
     // p points at element (row, col) of a row-major matrix; rows_left = rows remaining from
@@ -73,22 +97,26 @@ __device__ __forceinline__ float4 load4_rowwise(const float *__restrict__ p, int
     return v;
 }
 
-template <int BK, bool EDGE, bool VEC_A, bool VEC_B, bool VEC_C>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PER_EU, F32_WAVES_PER_EU))) void f32_regtile_kernel(int M, int N, int K, float alpha,
+template <class CFG, bool EDGE, bool VEC_A, bool VEC_B, bool VEC_C>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, CFG::WAVES))) void f32_regtile_kernel(int M, int N, int K, float alpha,
                                                          const float *__restrict__ A, int64_t lda,
                                                          const float *__restrict__ B, int64_t ldb,
                                                          float beta, float *__restrict__ C,
                                                          int64_t ldc, int tiles_m, int tiles_n) {
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    constexpr int CH = BK / 8;              // A float4 chunks per thread per slab
+    constexpr int TM = CFG::TM, TN = CFG::TN, BK = CFG::BK;
+    typedef Shape<TM, TN> S;
+    constexpr int MG = S::MG, NG = S::NG, BM = S::BM, BN = S::BN;
+    static_assert(BK % 4 == 0 && (BM * BK) % (4 * NT) == 0 && (BN * BK) % (4 * NT) == 0,
+                  "every thread stages whole float4 chunks");
+    constexpr int CH = BM * BK / (4 * NT);  // A float4 chunks per thread per slab
     constexpr int A_CPR = BK / 4;           // A chunks per tile row
     constexpr int B_CPR = BN / 4;           // B chunks per slab row
     constexpr int CHB = BK * BN / (4 * NT);  // B float4 chunks per thread per slab
-    __shared__ Smem<BK> sm;
+    __shared__ Smem<BM, BN, BK> sm;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int r0 = (wave >> 1) * 64 + (lane >> 3) * 4;
+    const int r0 = (wave >> 1) * (8 * TM) + (lane >> 3) * 4;
     const int c0 = (wave & 1) * (8 * TN) + (lane & 7) * 4;
 
     int tm, tn;
@@ -121,11 +149,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
     auto load_slab = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            ra[i] = load4_rowwise<BK, EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_row[i]),
+            ra[i] = load4_rowwise<EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_row[i]),
                                                    K - (k0 + a_k[i]));
 #pragma unroll
         for (int i = 0; i < CHB; ++i)
-            rb[i] = load4_rowwise<BK, EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
+            rb[i] = load4_rowwise<EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
                                                    K - (k0 + b_k[i]), N - (n0 + b_col[i]));
     };
     auto store_slab = [&](int buf) {
@@ -154,24 +182,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
         // Fragment double buffer: the reads for step k+1 are issued before the 64 FMAs of
         // step k. The scheduling barrier keeps the compiler from hoisting the whole slab's
         // reads (which would need BK*16 live registers and spill).
-        float4 fa[2][2], fb[2][NG];
-        fa[0][0] = *reinterpret_cast<const float4 *>(sa);
-        fa[0][1] = *reinterpret_cast<const float4 *>(sa + 32);
+        float4 fa[2][MG], fb[2][NG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) fa[0][g] = *reinterpret_cast<const float4 *>(sa + g * 32);
 #pragma unroll
         for (int g = 0; g < NG; ++g) fb[0][g] = *reinterpret_cast<const float4 *>(sb + g * 32);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const int cb = k & 1, nb = cb ^ 1;
             if (k + 1 < BK) {
-                fa[nb][0] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD));
-                fa[nb][1] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD) + 32);
+#pragma unroll
+                for (int g = 0; g < MG; ++g)
+                    fa[nb][g] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD) + g * 32);
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN + g * 32);
             }
-            const float ra_[TM] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
-                                   fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
-            float rb_[TN];
+            float ra_[TM], rb_[TN];
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                ra_[4 * g + 0] = fa[cb][g].x;
+                ra_[4 * g + 1] = fa[cb][g].y;
+                ra_[4 * g + 2] = fa[cb][g].z;
+                ra_[4 * g + 3] = fa[cb][g].w;
+            }
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 rb_[4 * g + 0] = fb[cb][g].x;
@@ -204,10 +238,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
         compute_slab((nslabs - 1) & 1);
     }
 
-    // Epilogue: rows r0+{0..3}, r0+32+{0..3}; columns c0 + 32*h + {0..3}, h < TN/4.
+    // Epilogue: rows r0 + 32*g + {0..3}, g < TM/4; columns c0 + 32*h + {0..3}, h < TN/4.
 #pragma unroll
     for (int m = 0; m < TM; ++m) {
-        const int row = m0 + r0 + (m < 4 ? m : 28 + m);
+        const int row = m0 + r0 + (m / 4) * 32 + (m % 4);
         if (EDGE && row >= M) continue;
         float *crow = C + (int64_t)row * ldc;
 #pragma unroll
@@ -236,62 +270,70 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F32_WAVES_PE
     }
 }
 
-#ifndef F32_BK
-#define F32_BK 16
-#endif
-constexpr int kBK = F32_BK;
-
-template <bool EDGE, bool VA, bool VB, bool VC>
+template <class CFG, bool EDGE, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tiles_n) {
-    hipLaunchKernelGGL((f32_regtile_kernel<kBK, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((f32_regtile_kernel<CFG, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
                        dim3(NT), 0, s, p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda,
                        (const float *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-template <bool EDGE, bool VA, bool VB>
+template <class CFG, bool EDGE, bool VA, bool VB>
 hipError_t pick_c(const Problem &p, hipStream_t s, int tm, int tn, bool vc) {
-    return vc ? launch_variant<EDGE, VA, VB, true>(p, s, tm, tn)
-              : launch_variant<EDGE, VA, VB, false>(p, s, tm, tn);
+    return vc ? launch_variant<CFG, EDGE, VA, VB, true>(p, s, tm, tn)
+              : launch_variant<CFG, EDGE, VA, VB, false>(p, s, tm, tn);
 }
-template <bool EDGE, bool VA>
+template <class CFG, bool EDGE, bool VA>
 hipError_t pick_b(const Problem &p, hipStream_t s, int tm, int tn, bool vb, bool vc) {
-    return vb ? pick_c<EDGE, VA, true>(p, s, tm, tn, vc) : pick_c<EDGE, VA, false>(p, s, tm, tn, vc);
+    return vb ? pick_c<CFG, EDGE, VA, true>(p, s, tm, tn, vc) : pick_c<CFG, EDGE, VA, false>(p, s, tm, tn, vc);
 }
-template <bool EDGE>
+template <class CFG, bool EDGE>
 hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, bool va, bool vb, bool vc) {
-    return va ? pick_b<EDGE, true>(p, s, tm, tn, vb, vc) : pick_b<EDGE, false>(p, s, tm, tn, vb, vc);
+    return va ? pick_b<CFG, EDGE, true>(p, s, tm, tn, vb, vc) : pick_b<CFG, EDGE, false>(p, s, tm, tn, vb, vc);
 }
 
+// Kernel names for every (edge, vec A, vec B, vec C) combination of one configuration.
+template <class CFG>
+struct Names {
+    char text[16][64];
+    const char *at[2][2][2][2];
+    Names() {
+        typedef Shape<CFG::TM, CFG::TN> S;
+        int n = 0;
+        for (int e = 0; e < 2; ++e)
+            for (int a = 0; a < 2; ++a)
+                for (int b = 0; b < 2; ++b)
+                    for (int c = 0; c < 2; ++c) {
+                        snprintf(text[n], sizeof text[n], "f32_regtile_%dx%dx%d_%dx%d%s%s%s%s", S::BM,
+                                 S::BN, CFG::BK, CFG::TM, CFG::TN, e ? "_edge" : "", a ? "_va" : "",
+                                 b ? "_vb" : "", c ? "_vc" : "");
+                        at[e][a][b][c] = text[n++];
+                    }
+    }
+};
+
+template <class CFG>
+hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name) {
+    typedef Shape<CFG::TM, CFG::TN> S;
+    const int tiles_m = (p.M + S::BM - 1) / S::BM, tiles_n = (p.N + S::BN - 1) / S::BN;
+    const bool edge = (p.M % S::BM) != 0 || (p.N % S::BN) != 0 || (p.K % CFG::BK) != 0;
+    const bool va = (p.lda % 4) == 0 && aligned16(p.A);
+    const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
+    const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
+    static const Names<CFG> names;  // thread-safe one-time initialisation
+    *name = names.at[edge][va][vb][vc];
+    return edge ? pick_a<CFG, true>(p, s, tiles_m, tiles_n, va, vb, vc)
+                : pick_a<CFG, false>(p, s, tiles_m, tiles_n, va, vb, vc);
+}
 
 }  // namespace
 
 hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name) {
-    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    const bool edge = (p.M % BM) != 0 || (p.N % BN) != 0 || (p.K % kBK) != 0;
-    const bool va = (p.lda % 4) == 0 && aligned16(p.A);
-    const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
-    const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
-    struct Names {
-        char text[16][64];
-        const char *at[2][2][2][2];
-        Names() {
-            int n = 0;
-            for (int e = 0; e < 2; ++e)
-                for (int a = 0; a < 2; ++a)
-                    for (int b = 0; b < 2; ++b)
-                        for (int c = 0; c < 2; ++c) {
-                            snprintf(text[n], sizeof text[n], "f32_regtile_%dx%dx%d_%dx%d%s%s%s%s",
-                                     BM, BN, kBK, TM, TN, e ? "_edge" : "", a ? "_va" : "", b ? "_vb" : "",
-                                     c ? "_vc" : "");
-                            at[e][a][b][c] = text[n++];
-                        }
-        }
-    };
-    static const Names names;  // thread-safe one-time initialisation
-    *name = names.at[edge][va][vb][vc];
-    return edge ? pick_a<true>(p, s, tiles_m, tiles_n, va, vb, vc)
-                : pick_a<false>(p, s, tiles_m, tiles_n, va, vb, vc);
+    return launch_cfg<SquareCfg>(p, s, name);
+}
+
+hipError_t launch_f32_regtile_small(const Problem &p, hipStream_t s, const char **name) {
+    return launch_cfg<SmallCfg>(p, s, name);
 }
 
 }  // namespace regtile

@@ -69,7 +69,7 @@ bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
 
 int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *A, int lda,
             const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
-    if (algo < REGTILE_F32_AUTO || algo > REGTILE_F32_SPLITK) return -1;
+    if (algo < REGTILE_F32_AUTO || algo > REGTILE_F32_REGTILE_SMALL) return -1;
     const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, false);
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
@@ -79,14 +79,17 @@ int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *
     const char *name = "none";
     hipError_t err;
     if (algo == REGTILE_F32_AUTO) {
-        // Fewer than two 128x128 tiles per CU leaves SIMDs idle: split K inside the workgroup.
+        // Fewer than two 128x128 tiles per CU leaves SIMDs idle: 64x64 tiles with 4x4 micro-tiles
+        // at 4 waves per SIMD (measured ahead of the split-K kernel on the tall-skinny and
+        // ragged shapes, and bitwise equal to the naive rung).
         const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-        algo = tiles < 2 * 256 ? REGTILE_F32_SPLITK : REGTILE_F32_REGTILE;
+        algo = tiles < 2 * 256 ? REGTILE_F32_REGTILE_SMALL : REGTILE_F32_REGTILE;
     }
     switch (algo) {
         case REGTILE_F32_NAIVE: err = regtile::launch_f32_naive(p, s, &name); break;
         case REGTILE_F32_LDS: err = regtile::launch_f32_lds(p, s, &name); break;
         case REGTILE_F32_SPLITK: err = regtile::launch_f32_splitk(p, s, &name); break;
+        case REGTILE_F32_REGTILE_SMALL: err = regtile::launch_f32_regtile_small(p, s, &name); break;
         default: err = regtile::launch_f32_regtile(p, s, &name); break;
     }
     return finish(err, name);

@@ -25,6 +25,7 @@ hipError_t launch_scale_c(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name);
+hipError_t launch_f32_regtile_small(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name);
 // MFMA kernels; `shape` 32 selects 32x32x16 fragments, 16 selects 16x16x32 (full aligned

@@ -90,7 +90,7 @@ def test_bf16_argument_validation(lib, args, expect):
 
 def test_unknown_algorithm_is_argument_one(lib):
     a = (4, 4, 4, 1.0, DUMMY, 4, DUMMY, 4, 0.0, DUMMY, 4, 0)
-    assert rt.regtile_gemm_f32_algo(5, *a) == -1
+    assert rt.regtile_gemm_f32_algo(6, *a) == -1
     assert rt.regtile_gemm_f32_algo(-1, *a) == -1
     assert rt.regtile_gemm_bf16_algo(4, *a) == -1
 
@@ -122,4 +122,6 @@ def test_kernels_have_no_scratch_and_stated_occupancy():
         assert r.get("ScratchSize [bytes/lane]", 0) == 0, (name, r)
     f32 = [r for n, r in res.items() if "f32_regtile_kernel" in n]
     assert f32 and all(r["Occupancy [waves/SIMD]"] >= 2 for r in f32)
+    small = [r for n, r in res.items() if "f32_regtile_kernel" in n and "SmallCfg" in n]
+    assert small and all(r["Occupancy [waves/SIMD]"] >= 4 for r in small)
     assert all(r["VGPRs"] + r.get("AGPRs", 0) <= 512 // r["Occupancy [waves/SIMD]"] for r in f32)

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS, rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK,
-             rt.ALGO_F32_AUTO]
+             rt.ALGO_F32_REGTILE_SMALL, rt.ALGO_F32_AUTO]
 BF16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16, rt.ALGO_BF16_AUTO]
 BF16_MFMA_ALGOS = [rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16]
 
@@ -63,7 +63,7 @@ def test_f32_tall_sampled():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
     announce("f32_tall default entry point")
     got = run(inp, torch).cpu().numpy()
-    assert "splitk" in rt.last_kernel()  # 128 tiles of 128x128: the split-K variant
+    assert "64x64x32_4x4" in rt.last_kernel()  # 128 tiles of 128x128: the small-tile kernel
     assert_parity_sampled(inp, got, "f32_tall")
 
 
@@ -97,7 +97,7 @@ EDGE_SHAPES = [(1, 1, 1), (1, 7, 3), (2, 3, 5), (3, 1, 2), (17, 33, 9), (127, 12
                (131, 293, 300), (64, 1024, 31), (1000, 8, 100), (8, 1000, 1000)]
 
 
-@pytest.mark.parametrize("algo", [rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK])
+@pytest.mark.parametrize("algo", [rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK, rt.ALGO_F32_REGTILE_SMALL])
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
 def test_f32_regtile_edges(shape, algo):
     M, N, K = shape
@@ -262,12 +262,13 @@ def test_runs_on_the_callers_stream_and_is_deterministic():
 
 
 def test_f32_ladder_rungs_agree_bitwise():
-    # rungs 0-2 accumulate every output with fmaf over k in natural order
+    # the SIMT rungs except split-K accumulate every output with fmaf over k in natural order
     inp = gi.make_inputs(333, 517, 1029, dist="normal", seed=9)
     announce("ladder bitwise agreement")
     outs = [run(inp, torch, a).cpu().numpy() for a in (rt.ALGO_F32_NAIVE, rt.ALGO_F32_LDS,
-                                                        rt.ALGO_F32_REGTILE)]
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+                                                        rt.ALGO_F32_REGTILE, rt.ALGO_F32_REGTILE_SMALL)]
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
 
 
 def test_f32_strided_views_every_register_tiled_kernel():
@@ -278,7 +279,7 @@ def test_f32_strided_views_every_register_tiled_kernel():
     big_b = torch.from_numpy(rng.standard_normal((K, N + 5), dtype=np.float32)).cuda()
     A, B = big_a[:, 1:K + 1], big_b[:, 3:N + 3]
     inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f32", False, A.cpu().numpy(), B.cpu().numpy(), None)
-    for algo in (rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK):
+    for algo in (rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK, rt.ALGO_F32_REGTILE_SMALL):
         announce(f"f32 strided algo={algo}")
         big_c = torch.zeros((M, N + 3), device="cuda")
         C = big_c[:, 1:N + 1]
