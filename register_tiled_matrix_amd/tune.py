@@ -134,7 +134,7 @@ def cmd_run(args) -> int:
         rungs = [("ladder:naive", rt.ALGO_F32_NAIVE), ("ladder:lds_1x1", rt.ALGO_F32_LDS),
                  ("ladder:regtile_default", rt.ALGO_F32_REGTILE), ("ladder:regtile_small", rt.ALGO_F32_REGTILE_SMALL),
                  ("ladder:splitk", rt.ALGO_F32_SPLITK)]
-        for label, algo in rungs:
+        for label, algo in ([] if args.no_rungs else rungs):
             def fn(algo=algo):
                 st = rt.regtile_gemm_f32_algo(algo, *call, C.data_ptr(), w.N, stream)
                 if st:
@@ -219,6 +219,9 @@ def main(argv=None) -> int:
     r.add_argument("--workloads", default="f32_4096,f32_tall")
     r.add_argument("--steps", type=int, default=10)
     r.add_argument("--warmup", type=int, default=3)
+    r.add_argument("--no-rungs", action="store_true",
+                   help="time only the variants (for counter runs, where the default library's "
+                        "kernels would share the variants' names)")
     rep = sub.add_parser("report")
     rep.add_argument("jsonl")
     rep.add_argument("--out", default="")
