@@ -1,6 +1,6 @@
 """Seeded synthetic GEMM inputs, shared by the CPU oracle tests and the HIP-path tests.
 
-This module only draws matrices and encodes fp32 draws as bf16 bit patterns. It holds
+This module only draws matrices and encodes fp32 draws as bf16 or fp16 bit patterns. It holds
 none of the product's arithmetic: no sums, no products, no tiling. Both sides of every
 parity check (the fp64 oracle under ``oracle/`` and the HIP library) receive the very
 same host arrays from here.
@@ -15,6 +15,8 @@ Draw order and layout
   ``rng.standard_normal(dtype=float32)``.
 * bf16 operands are the round-to-nearest-even encoding of the fp32 draw (NaN becomes the
   quiet NaN 0x7FC0). The pages fix no rounding mode; this is the plain reading.
+* fp16 operands (the pages' worked half-precision GEMM) are numpy's float32 -> float16
+  conversion of the draw: IEEE binary16, round to nearest even, overflow to infinity.
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ __all__ = [
     "workload",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "f32_to_f16_bits",
     "draw",
     "GemmInputs",
     "make_inputs",
@@ -43,7 +46,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str  # "f32" (fp32 in, fp32 out) or "bf16" (bf16 in, fp32 out)
+    dtype: str  # "f32" (fp32 in, fp32 out), "bf16" or "f16" (16-bit in, fp32 out)
     dist: str  # "uniform" (U[-1,1]) or "normal" (N(0,1))
     alpha: float = 1.0
     beta: float = 0.0
@@ -71,6 +74,9 @@ WORKLOADS = {
                           description="bf16 8192^3, A row-major, B column-major, N(0,1) rounded to bf16, fp32 C"),
     "f32_tall": Workload("f32_tall", 16384, 128, 4096, "f32", "uniform", 1.0, 0.0, 1005,
                          description="fp32 tall-skinny M=16384 N=128 K=4096, U[-1,1], alpha=1, beta=0"),
+    "f16_8192": Workload("f16_8192", 8192, 8192, 8192, "f16", "normal", 1.0, 0.0, 1006,
+                         b_col_major=True,
+                         description="fp16 8192^3, A row-major, B column-major, N(0,1) rounded to fp16, fp32 C"),
 }
 
 
@@ -88,6 +94,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
     return r
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest, ties to even); uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return x.astype(np.float16).view(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -111,7 +124,7 @@ class GemmInputs:
 
     A: M x K row-major (lda = K). B: K x N row-major (ldb = N), or for ``b_col_major``
     K x N column-major, stored as an N x K array (ldb = K). C: M x N row-major (ldc = N),
-    present only when beta != 0. For bf16 workloads A and B hold uint16 bit patterns.
+    present only when beta != 0. For bf16 and fp16 workloads A and B hold uint16 bit patterns.
     """
 
     M: int
@@ -141,10 +154,10 @@ class GemmInputs:
 def make_inputs(M: int, N: int, K: int, *, dtype: str = "f32", dist: str = "uniform",
                 alpha: float = 1.0, beta: float = 0.0, seed: int = 0,
                 b_col_major: Optional[bool] = None, with_c: Optional[bool] = None) -> GemmInputs:
-    """Draw one problem. ``b_col_major`` defaults to True for bf16 and False for fp32;
+    """Draw one problem. ``b_col_major`` defaults to True for bf16 / fp16 and False for fp32;
     C_in is drawn (same distribution) when beta != 0 or ``with_c`` is set."""
     if b_col_major is None:
-        b_col_major = dtype == "bf16"
+        b_col_major = dtype in ("bf16", "f16")
     if with_c is None:
         with_c = beta != 0.0
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -157,6 +170,9 @@ def make_inputs(M: int, N: int, K: int, *, dtype: str = "f32", dist: str = "unif
     if dtype == "bf16":
         a = f32_to_bf16_bits(a).reshape(a.shape)
         b = f32_to_bf16_bits(b).reshape(b.shape)
+    elif dtype == "f16":
+        a = f32_to_f16_bits(a).reshape(a.shape)
+        b = f32_to_f16_bits(b).reshape(b.shape)
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return GemmInputs(M, N, K, float(alpha), float(beta), dtype, bool(b_col_major), a, b, c)

@@ -9,7 +9,7 @@ The arithmetic lives in ``oracle_gemm.c`` (a plain fp64 triple loop, k summed in
 order, OpenMP over rows); this module only marshals numpy arrays into it. What is computed,
 and the pages it follows, is stated at the top of that file:
 
-    C_ref = alpha * (A @ B) + beta * C_in           (fp64, exact fp32 / bf16 inputs)
+    C_ref = alpha * (A @ B) + beta * C_in           (fp64, exact fp32 / bf16 / fp16 inputs)
     mag   = |alpha| * (|A| @ |B|) + |beta * C_in|   (elementwise magnitude)
 
 Parity bound (the stated numeric tolerance for fp32 accumulation): an element passes when
@@ -58,8 +58,10 @@ def _load():
         ent_f32 = [_L, _L, _L, _D, _fp, _L, _fp, _L, _D, _fp, _L, _L, _lp, _lp, _dp, _dp]
         ent_bf16 = [_L, _L, _L, _D, _u16p, _L, _u16p, _L, _D, _fp, _L, _L, _lp, _lp, _dp, _dp]
         for name, argt in (("oracle_gemm_f32", full_f32), ("oracle_gemm_bf16", full_bf16),
+                           ("oracle_gemm_f16", full_bf16),
                            ("oracle_gemm_f32_entries", ent_f32),
-                           ("oracle_gemm_bf16_entries", ent_bf16)):
+                           ("oracle_gemm_bf16_entries", ent_bf16),
+                           ("oracle_gemm_f16_entries", ent_bf16)):
             f = getattr(lib, name)
             f.argtypes = argt
             f.restype = ctypes.c_int
@@ -81,9 +83,9 @@ def _prep(A, B, C, dtype, M, N, K, b_col_major):
             raise ValueError("the fp32 oracle takes row-major B")
         A = np.ascontiguousarray(A, dtype=np.float32).reshape(M, K)
         B = np.ascontiguousarray(B, dtype=np.float32).reshape(K, N)
-    elif dtype == "bf16":
+    elif dtype in ("bf16", "f16"):
         if not b_col_major:
-            raise ValueError("the bf16 oracle takes column-major B (stored as N x K)")
+            raise ValueError(f"the {dtype} oracle takes column-major B (stored as N x K)")
         A = np.ascontiguousarray(A, dtype=np.uint16).reshape(M, K)
         B = np.ascontiguousarray(B, dtype=np.uint16).reshape(N, K)
     else:
@@ -95,10 +97,10 @@ def _prep(A, B, C, dtype, M, N, K, b_col_major):
 
 def gemm(A, B, C=None, *, alpha=1.0, beta=0.0, dtype="f32", b_col_major=None):
     """Full oracle product. A: M x K; B: K x N (fp32, row-major) or N x K storage of a
-    column-major K x N bf16 matrix; C: M x N or None (required when beta != 0).
-    Returns (ref, mag) as float64 M x N arrays."""
+    column-major K x N bf16 / fp16 matrix (16-bit patterns); C: M x N or None (required when
+    beta != 0). Returns (ref, mag) as float64 M x N arrays."""
     if b_col_major is None:
-        b_col_major = dtype == "bf16"
+        b_col_major = dtype in ("bf16", "f16")
     A = np.asarray(A)
     B = np.asarray(B)
     M, K = A.shape
@@ -117,10 +119,11 @@ def gemm(A, B, C=None, *, alpha=1.0, beta=0.0, dtype="f32", b_col_major=None):
                                  _ptr(C, ctypes.c_float), N, _ptr(out, ctypes.c_double),
                                  _ptr(mag, ctypes.c_double))
     else:
-        rc = lib.oracle_gemm_bf16(M, N, K, float(alpha), _ptr(A, ctypes.c_uint16), K,
-                                  _ptr(B, ctypes.c_uint16), K, float(beta),
-                                  _ptr(C, ctypes.c_float), N, _ptr(out, ctypes.c_double),
-                                  _ptr(mag, ctypes.c_double))
+        fn = lib.oracle_gemm_bf16 if dtype == "bf16" else lib.oracle_gemm_f16
+        rc = fn(M, N, K, float(alpha), _ptr(A, ctypes.c_uint16), K,
+                _ptr(B, ctypes.c_uint16), K, float(beta),
+                _ptr(C, ctypes.c_float), N, _ptr(out, ctypes.c_double),
+                _ptr(mag, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (rc={rc})")
     return out, mag
@@ -129,7 +132,7 @@ def gemm(A, B, C=None, *, alpha=1.0, beta=0.0, dtype="f32", b_col_major=None):
 def gemm_entries(A, B, C, I, J, *, alpha=1.0, beta=0.0, dtype="f32", b_col_major=None):
     """Oracle values at the sampled positions (I[e], J[e]); returns (ref, mag) of length n."""
     if b_col_major is None:
-        b_col_major = dtype == "bf16"
+        b_col_major = dtype in ("bf16", "f16")
     A = np.asarray(A)
     B = np.asarray(B)
     M, K = A.shape
@@ -145,7 +148,8 @@ def gemm_entries(A, B, C, I, J, *, alpha=1.0, beta=0.0, dtype="f32", b_col_major
     out = np.empty(n, np.float64)
     mag = np.empty(n, np.float64)
     lib = _load()
-    fn = lib.oracle_gemm_f32_entries if dtype == "f32" else lib.oracle_gemm_bf16_entries
+    fn = {"f32": lib.oracle_gemm_f32_entries, "bf16": lib.oracle_gemm_bf16_entries,
+          "f16": lib.oracle_gemm_f16_entries}[dtype]
     ct = ctypes.c_float if dtype == "f32" else ctypes.c_uint16
     rc = fn(M, N, K, float(alpha), _ptr(A, ct), K, _ptr(B, ct), K if b_col_major else N,
             float(beta), _ptr(C, ctypes.c_float), N, n, _ptr(I, ctypes.c_long),

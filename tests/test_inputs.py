@@ -50,7 +50,9 @@ def test_workload_table():
     assert b.dtype == "bf16" and b.b_col_major and b.K == 8192
     t = w["f32_tall"]
     assert (t.M, t.N, t.K) == (16384, 128, 4096)
-    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005]
+    h = w["f16_8192"]
+    assert h.dtype == "f16" and h.b_col_major and (h.M, h.N, h.K) == (8192, 8192, 8192)
+    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005, 1006]
 
 
 def test_determinism_and_layout():
@@ -107,3 +109,20 @@ def test_bf16_widening_roundtrip():
 def test_small_integers_are_bf16_exact(v):
     h = gi.f32_to_bf16_bits(np.array([v], np.float32))
     assert gi.bf16_bits_to_f32(h)[0] == v
+
+
+def test_f16_rne_against_python_half_packing():
+    # struct's 'e' format packs an IEEE binary16 with round-half-to-even, independently of numpy
+    import struct
+    rng = np.random.Generator(np.random.PCG64(12))
+    x = np.concatenate([rng.standard_normal(3000, dtype=np.float32),
+                        rng.uniform(-6e-5, 6e-5, 300).astype(np.float32),  # fp16 subnormal range
+                        rng.uniform(-65000, 65000, 300).astype(np.float32),
+                        # exact ties between neighbouring fp16 values (1 + 2^-11, 1 + 3*2^-11)
+                        np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, -(1 + 2 ** -11), 2 ** -25,
+                                  3 * 2 ** -25, 0.0, -0.0], np.float32)])
+    got = gi.f32_to_f16_bits(x)
+    want = np.array([struct.unpack("<H", struct.pack("<e", float(v)))[0] for v in x], np.uint16)
+    assert np.array_equal(got, want)
+    assert gi.f32_to_f16_bits(np.array([70000.0, -1e9], np.float32)).tolist() == [0x7C00, 0xFC00]
+

@@ -34,6 +34,10 @@ MUTANTS = {
     "bf16_drop_first_k": ("for (long k = 0; k < K; ++k) {\n                    double p = widen_bf16(arow[k])",
                           "for (long k = 1; k < K; ++k) {\n                    double p = widen_bf16(arow[k])"),
     "mag_without_abs": ("g[j] += fabs(p);", "g[j] += p;"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "f16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "f16_fraction_width": ("int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;",
+                           "int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x1FF;"),
 }
 
 PIN_TESTS = [
@@ -45,6 +49,10 @@ PIN_TESTS = [
     pins.test_identity_left_and_right,
     pins.test_permutation_reorders_rows_and_columns,
     lambda: pins.test_bf16_widening_follows_the_format(0x4049, 3.140625),
+    lambda: pins.test_bruteforce_every_tiny_shape("f16"),
+    lambda: pins.test_integer_matrices_exact_f16_column_major(70, 33, 129),
+    lambda: pins.test_f16_widening_follows_the_format(0x0001, 2.0 ** -24),
+    lambda: pins.test_f16_widening_follows_the_format(0x4248, 3.140625),
 ]
 
 
@@ -62,8 +70,8 @@ def _build_mutant(tmp_path, name, old, new):
 
 def _configure(lib):
     real = oracle._load()
-    for fname in ("oracle_gemm_f32", "oracle_gemm_bf16", "oracle_gemm_f32_entries",
-                  "oracle_gemm_bf16_entries", "oracle_num_threads"):
+    for fname in ("oracle_gemm_f32", "oracle_gemm_bf16", "oracle_gemm_f16", "oracle_gemm_f32_entries",
+                  "oracle_gemm_bf16_entries", "oracle_gemm_f16_entries", "oracle_num_threads"):
         f = getattr(lib, fname)
         g = getattr(real, fname)
         f.argtypes = g.argtypes

@@ -37,13 +37,19 @@ def _widen_bf16_independent(h: int) -> float:
     return struct.unpack(">f", struct.pack(">I", (int(h) & 0xFFFF) << 16))[0]
 
 
+def _widen_f16_independent(h: int) -> float:
+    """fp16 bits -> value via Python's own IEEE binary16 unpacking (struct format 'e')."""
+    return struct.unpack("<e", struct.pack("<H", int(h) & 0xFFFF))[0]
+
+
 def _exact_gemm(A, B, C, alpha, beta, dtype, b_col_major):
     """alpha*A*B + beta*C and |alpha|*|A||B| + |beta C| in exact rationals."""
     M, K = A.shape
     N = B.shape[0] if b_col_major else B.shape[1]
-    if dtype == "bf16":
-        fa = [[Fraction(_widen_bf16_independent(A[i, k])) for k in range(K)] for i in range(M)]
-        fb = [[Fraction(_widen_bf16_independent(B[j, k] if b_col_major else B[k, j]))
+    if dtype in ("bf16", "f16"):
+        w = _widen_bf16_independent if dtype == "bf16" else _widen_f16_independent
+        fa = [[Fraction(w(A[i, k])) for k in range(K)] for i in range(M)]
+        fb = [[Fraction(w(B[j, k] if b_col_major else B[k, j]))
                for j in range(N)] for k in range(K)]
     else:
         fa = [[_frac_f32(A[i, k]) for k in range(K)] for i in range(M)]
@@ -61,7 +67,7 @@ def _exact_gemm(A, B, C, alpha, beta, dtype, b_col_major):
     return ref, mag
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_bruteforce_every_tiny_shape(dtype):
     rng = np.random.Generator(np.random.PCG64(7))
     alphas = [1.0, -0.5, 1.5, 0.0, 3.0]
@@ -184,6 +190,18 @@ def test_integer_matrices_exact_bf16_column_major(M, N, K):
     assert np.array_equal(mag, np.abs(Ai) @ np.abs(Bi))
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 3, 2), (70, 33, 129), (31, 260, 400)])
+def test_integer_matrices_exact_f16_column_major(M, N, K):
+    rng = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
+    Ai = rng.integers(-16, 17, (M, K))
+    Bi = rng.integers(-16, 17, (K, N))
+    ha = gi.f32_to_f16_bits(Ai.astype(np.float32)).reshape(M, K)
+    hbT = gi.f32_to_f16_bits(np.ascontiguousarray(Bi.T).astype(np.float32)).reshape(N, K)
+    ref, mag = oracle.gemm(ha, hbT, dtype="f16")
+    assert np.array_equal(ref, (Ai @ Bi).astype(np.float64))
+    assert np.array_equal(mag, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+
+
 def test_against_library_fp64_matmul():
     rng = np.random.Generator(np.random.PCG64(12))
     M, N, K = 257, 129, 300
@@ -238,8 +256,21 @@ def test_bf16_widening_follows_the_format(bits, value):
     assert ref[0, 0] == value
 
 
+@pytest.mark.parametrize("bits,value", [
+    (0x3C00, 1.0), (0xBC00, -1.0), (0x4000, 2.0), (0x3800, 0.5), (0x4248, 3.140625),
+    (0x0001, 2.0 ** -24), (0x03FF, 1023 * 2.0 ** -24), (0x0400, 2.0 ** -14), (0x7BFF, 65504.0),
+    (0xD7B8, -123.5), (0x0000, 0.0), (0x8000, -0.0), (0x7C00, float("inf")),
+])
+def test_f16_widening_follows_the_format(bits, value):
+    # IEEE binary16 = sign, 5-bit exponent (bias 15), 10 fraction bits; exponent 0 holds the
+    # subnormals f * 2^-24: value read off the definition
+    one = np.array([[0x3C00]], np.uint16)
+    ref, _ = oracle.gemm(np.array([[bits]], np.uint16), one, dtype="f16")
+    assert ref[0, 0] == value
+
+
 def test_sampled_entries_match_full_product():
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32", "bf16", "f16"):
         inp = gi.make_inputs(67, 45, 129, dtype=dtype, dist="normal", alpha=1.5, beta=-0.5,
                              seed=21)
         ref, mag = oracle.gemm_inputs(inp)
