@@ -3,9 +3,9 @@
 
 One step = one call of the hot path on one batch of synthetic input: the fp32 register-tiled
 GEMM C = A @ B at M = N = K = 4096 (row-major, U[-1,1], alpha = 1, beta = 0), inputs
-resident in HBM before the timed region. The same JSON line also carries the bf16 MFMA path
-at 8192^3 (A row-major, B column-major, N(0,1) rounded to bf16) and the kernel ladder
-(naive -> LDS-tiled -> register-tiled -> MFMA), each timed the same way.
+resident in HBM before the timed region. The same JSON line also carries the bf16 and fp16
+MFMA paths at 8192^3 (A row-major, B column-major, N(0,1) rounded to the 16-bit type) and the
+kernel ladder (naive -> LDS-tiled -> register-tiled -> MFMA), each timed the same way.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-ladder] [--no-cpu]
 
@@ -42,11 +42,11 @@ def _parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-ladder", action="store_true", help="skip the naive/LDS rungs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 8192^3 leg")
+    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 and fp16 8192^3 legs")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
-    p.add_argument("--only", choices=["f32_4096", "bf16_8192", "f32_ragged", "f32_tall",
-                                      "f32_256", "copy"],
+    p.add_argument("--only", choices=["f32_4096", "bf16_8192", "f16_8192", "f32_ragged",
+                                      "f32_tall", "f32_256", "copy"],
                    help="profiler mode: run just this workload's kernel (warmup + steps) and "
                         "print one summary line; 'copy' runs a plain 1 GiB device copy used to "
                         "calibrate the HBM byte counters")
@@ -181,8 +181,9 @@ def _only(args, torch, gi, rt, dev):
     else:
         A = torch.from_numpy(inp.A.view(np.int16)).to(dev)
         B = torch.from_numpy(inp.B.view(np.int16)).to(dev)
-        fn = rt.gemm_bf16_raw if args.algo == 0 else (
-            lambda *a: rt.regtile_gemm_bf16_algo(args.algo, *a))
+        raw, algo_fn = ((rt.gemm_bf16_raw, rt.regtile_gemm_bf16_algo) if w.dtype == "bf16"
+                        else (rt.gemm_f16_raw, rt.regtile_gemm_f16_algo))
+        fn = raw if args.algo == 0 else (lambda *a: algo_fn(args.algo, *a))
     C = (torch.from_numpy(inp.C).to(dev) if inp.C is not None
          else torch.empty((w.M, w.N), dtype=torch.float32, device=dev))
     call = (w.M, w.N, w.K, w.alpha, A.data_ptr(), inp.lda, B.data_ptr(), inp.ldb, w.beta,
@@ -276,9 +277,9 @@ def main():
         },
     }
 
-    # ---- bf16 MFMA 8192^3 -------------------------------------------------------------------
-    if not args.no_bf16:
-        wb = gi.WORKLOADS["bf16_8192"]
+    # ---- bf16 and fp16 MFMA 8192^3 ------------------------------------------------------------
+    def leg_16b(wname, raw, algo_fn, label):
+        wb = gi.WORKLOADS[wname]
         ib = gi.workload_inputs(wb)
         Ab = torch.from_numpy(ib.A.view(np.int16)).to(dev)
         Bb = torch.from_numpy(ib.B.view(np.int16)).to(dev)
@@ -286,22 +287,21 @@ def main():
         bf_args = (wb.M, wb.N, wb.K, 1.0, Ab.data_ptr(), wb.K, Bb.data_ptr(), wb.K, 0.0,
                    Cb.data_ptr(), wb.N, stream)
 
-        def step_bf16():
-            st = rt.gemm_bf16_raw(*bf_args)
+        def step_16():
+            st = raw(*bf_args)
             if st:
                 raise rt.RegtileError(st, rt.strerror(st))
 
-        step_bf16()
+        step_16()
         kname = rt.last_kernel()
-        wms, kms, kmin = _time(torch, step_bf16, args.steps, args.warmup)
+        wms, kms, kmin = _time(torch, step_16, args.steps, args.warmup)
         v = wb.flop / (wms * 1e-3) / 1e12
         a = wb.flop / (kms * 1e-3) / 1e12
-        out["bf16_8192"] = {
+        res = {
             "value": round(v, 2), "unit": "TFLOP/s", "ms_per_step": round(wms, 4),
-            "dtype": "bf16 in, f32 accumulate",
-            "workload": "bf16_8192: M=N=K=8192, A row-major, B column-major, N(0,1) -> bf16 "
-                        "seed 1004, fp32 C, alpha=1, beta=0",
-            "percent_of_bf16_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
+            "dtype": f"{label} in, f32 accumulate",
+            "workload": f"{wname}: {wb.description}, seed {wb.seed}, alpha=1, beta=0",
+            "percent_of_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
             "roofline": {"bound": "mfma", "achieved": round(a, 2), "peak": acc.PEAK_BF16_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(a / acc.PEAK_BF16_MFMA_TFLOPS, 4),
                          "traffic": _traffic(kname),
@@ -311,18 +311,22 @@ def main():
         }
 
         # the same tiles and pipeline on 16x16x32 MFMA fragments (the fragment-shape rung)
-        def step_bf16_16():
-            st = rt.regtile_gemm_bf16_algo(rt.ALGO_BF16_MFMA_16X16, *bf_args)
+        def step_16x16():
+            st = algo_fn(rt.ALGO_BF16_MFMA_16X16, *bf_args)
             if st:
                 raise rt.RegtileError(st, rt.strerror(st))
 
-        step_bf16_16()
+        step_16x16()
         k16 = rt.last_kernel()
-        _, kms16, _ = _time(torch, step_bf16_16, args.steps, args.warmup)
-        out["bf16_8192"]["mfma_16x16x32"] = {
-            "kernel": k16, "kernel_ms_mean": round(kms16, 4),
-            "TFLOP/s": round(wb.flop / (kms16 * 1e-3) / 1e12, 2)}
+        _, kms16, _ = _time(torch, step_16x16, args.steps, args.warmup)
+        res["mfma_16x16x32"] = {"kernel": k16, "kernel_ms_mean": round(kms16, 4),
+                                "TFLOP/s": round(wb.flop / (kms16 * 1e-3) / 1e12, 2)}
         del Ab, Bb, Cb
+        return res
+
+    if not args.no_bf16:
+        out["bf16_8192"] = leg_16b("bf16_8192", rt.gemm_bf16_raw, rt.regtile_gemm_bf16_algo, "bf16")
+        out["f16_8192"] = leg_16b("f16_8192", rt.gemm_f16_raw, rt.regtile_gemm_f16_algo, "fp16")
 
     # ---- the ladder on the headline workload ------------------------------------------------
     if not args.no_ladder:
@@ -345,6 +349,9 @@ def main():
                 "kernel": out["bf16_8192"]["mfma_16x16x32"]["kernel"],
                 "kernel_ms": out["bf16_8192"]["mfma_16x16x32"]["kernel_ms_mean"],
                 "TFLOP/s": out["bf16_8192"]["mfma_16x16x32"]["TFLOP/s"]}
+            ladder["mfma_f16_8192"] = {"kernel": out["f16_8192"]["roofline"]["kernel"],
+                                       "kernel_ms": out["f16_8192"]["roofline"]["kernel_ms_mean"],
+                                       "TFLOP/s": out["f16_8192"]["roofline"]["achieved"]}
         out["ladder"] = ladder
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------

@@ -62,7 +62,7 @@ enum regtile_algo_f32 {
                                      per SIMD (shapes with few 128x256 tiles) */
 };
 
-/* Kernel ladder for the bf16 entry points. */
+/* Kernel ladder for the bf16 and fp16 entry points. */
 enum regtile_algo_bf16 {
     REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
     REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
@@ -103,15 +103,30 @@ int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, cons
               int ldb, float beta, float *C, int ldc, void *stream);
 
 /*
- * regtile_gemm_f32_algo / regtile_gemm_bf16_algo -- the same operations on an explicit rung of
- * the kernel ladder (arg 1: a regtile_algo_f32 / regtile_algo_bf16 value; -1 if unknown). The
- * remaining arguments are those of gemm_f32 / gemm_bf16, shifted by one position.
+ * gemm_f16 -- C = alpha*A*B + beta*C with IEEE fp16 (binary16) operands given as raw bit
+ * patterns, exact products and fp32 accumulation on the same MFMA kernels with
+ * v_mfma_f32_32x32x16_f16 fragments: the half-precision GEMM the second page works through
+ * ("寄存器Tiling跨架构解析" section 6: fp16 inputs, fp32 accumulation; section 3.2: MFMA
+ * fragments). Layouts, argument positions and rules exactly as for gemm_bf16 (A row-major,
+ * B column-major, C fp32 row-major).
+ */
+int gemm_f16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+             int ldb, float beta, float *C, int ldc, void *stream);
+
+/*
+ * regtile_gemm_f32_algo / regtile_gemm_bf16_algo / regtile_gemm_f16_algo -- the same
+ * operations on an explicit rung of
+ * the kernel ladder (arg 1: a regtile_algo_f32 value, or a regtile_algo_bf16 value for both
+ * 16-bit entry points; -1 if unknown). The remaining arguments are those of gemm_f32 /
+ * gemm_bf16 / gemm_f16, shifted by one position.
  */
 int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const float *A, int lda,
                           const float *B, int ldb, float beta, float *C, int ldc, void *stream);
 int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A,
                            int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
                            void *stream);
+int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                          const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream);
 
 /* Name of the kernel the calling thread launched last ("none" before the first launch,
  * "quick-return" when nothing was launched). Static storage; do not free. */

@@ -12,7 +12,10 @@ Entry points (same names as the C ABI):
 * ``gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO)``
   bf16 A (M x K, row-major) times bf16 B given as a K x N column-major view (for example
   ``Bt.t()`` for a contiguous N x K tensor ``Bt``), fp32 C.
-* ``gemm_f32_raw`` / ``gemm_bf16_raw`` take the C arguments verbatim (integers for pointers).
+* ``gemm_f16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO)`` the same with
+  float16 A and B (IEEE binary16); the algorithm values are the bf16 ones.
+* ``gemm_f32_raw`` / ``gemm_bf16_raw`` / ``gemm_f16_raw`` take the C arguments verbatim
+  (integers for pointers).
 * ``last_kernel()``, ``strerror(status)``, ``version()``.
 
 The library must be built (``python -m register_tiled_matrix_amd.build``); importing this
@@ -29,8 +32,8 @@ __all__ = [
     "ALGO_F32_REGTILE_SMALL",
     "ALGO_BF16_AUTO", "ALGO_BF16_NAIVE", "ALGO_BF16_MFMA", "ALGO_BF16_MFMA_16X16",
     "RegtileError", "RegtileLibraryMissing", "lib_path", "load",
-    "gemm_f32", "gemm_bf16", "gemm_f32_raw", "gemm_bf16_raw",
-    "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo",
+    "gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_raw", "gemm_bf16_raw", "gemm_f16_raw",
+    "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
     "last_kernel", "strerror", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -38,7 +41,8 @@ ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE, ALGO_F32_SPLITK =
 ALGO_F32_REGTILE_SMALL = 5
 ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA, ALGO_BF16_MFMA_16X16 = 0, 1, 2, 3
 
-EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo",
+EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "gemm_f16", "regtile_gemm_f32_algo",
+                    "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
                     "regtile_last_kernel", "regtile_strerror", "regtile_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,7 +77,8 @@ def load():
         lib = ctypes.CDLL(_LIB_PATH)
         I, F, P = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
         gemm = [I, I, I, F, P, I, P, I, F, P, I, P]
-        for name, args in (("gemm_f32", gemm), ("gemm_bf16", gemm),
+        for name, args in (("gemm_f32", gemm), ("gemm_bf16", gemm), ("gemm_f16", gemm),
+                           ("regtile_gemm_f16_algo", [I] + gemm),
                            ("regtile_gemm_f32_algo", [I] + gemm),
                            ("regtile_gemm_bf16_algo", [I] + gemm)):
             f = getattr(lib, name)
@@ -117,6 +122,15 @@ def gemm_bf16_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int
 
 def regtile_gemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
     return load().regtile_gemm_f32_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                        stream)
+
+
+def gemm_f16_raw(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def regtile_gemm_f16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().regtile_gemm_f16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                         stream)
 
 
@@ -189,15 +203,11 @@ def gemm_f32(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_F32_AUTO, stream=None)
     return C
 
 
-def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
-    """C = alpha*A@B + beta*C; A bf16 (M x K) row-major, B bf16 (K x N) column-major view,
-    C fp32 (M x N) row-major; returns C (allocated when None)."""
-    import torch
-
-    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
-        raise ValueError("gemm_bf16 takes bfloat16 A and B")
+def _gemm_16b(fn, want, label, A, B, C, alpha, beta, algo, stream):
+    if A.dtype != want or B.dtype != want:
+        raise ValueError(f"{label} takes {want} A and B")
     if not (A.is_cuda and B.is_cuda):
-        raise ValueError("gemm_bf16 takes device tensors")
+        raise ValueError(f"{label} takes device tensors")
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
@@ -206,8 +216,24 @@ def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=Non
         raise ValueError("beta != 0 needs C")
     C = _out(C, M, N, A)
     lda, ldb, ldc = _row_major_ld(A, "A"), _col_major_ld(B, "B"), _row_major_ld(C, "C")
-    st = regtile_gemm_bf16_algo(int(algo), M, N, K, float(alpha), A.data_ptr(), lda,
-                                B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
-                                _stream_handle(A, stream))
+    st = fn(int(algo), M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta),
+            C.data_ptr(), ldc, _stream_handle(A, stream))
     _check(st)
     return C
+
+
+def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
+    """C = alpha*A@B + beta*C; A bf16 (M x K) row-major, B bf16 (K x N) column-major view,
+    C fp32 (M x N) row-major; returns C (allocated when None)."""
+    import torch
+
+    return _gemm_16b(regtile_gemm_bf16_algo, torch.bfloat16, "gemm_bf16", A, B, C, alpha, beta,
+                     algo, stream)
+
+
+def gemm_f16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
+    """As gemm_bf16 with float16 (IEEE binary16) A and B."""
+    import torch
+
+    return _gemm_16b(regtile_gemm_f16_algo, torch.float16, "gemm_f16", A, B, C, alpha, beta,
+                     algo, stream)

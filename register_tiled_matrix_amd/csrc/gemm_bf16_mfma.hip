@@ -20,6 +20,7 @@
 // stored to the other stage after them, one barrier per slab (section 6.3's prefetch).
 // Tile order: workgroups are renumbered so each XCD gets a contiguous block of tiles, walked
 // in groups of 8 tile-rows (L2 reuse of A rows and B columns inside an XCD).
+#include "mfma_common.h"
 #include "regtile_internal.h"
 
 namespace regtile {
@@ -66,7 +67,7 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool
     return r;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VEC_C>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VEC_C, bool F16>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma::Frag<32, F16>::mfma(fa[i], fb[j], acc[i][j]);
         }
     };
 
@@ -185,44 +186,52 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     (void)VEC_C;
 }
 
-template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC>
+template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16>
 hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false>),
+    hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16>),
                        dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
                        (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,
                        p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, bool F16>
+hipError_t launch_pick(const Problem &p, hipStream_t s, bool edge, bool vec) {
+    if (edge) return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16>(p, s)
+                         : launch_cfg<BM, BN, WM, WN, true, false, F16>(p, s);
+    return vec ? launch_cfg<BM, BN, WM, WN, false, true, F16>(p, s)
+               : launch_cfg<BM, BN, WM, WN, false, false, F16>(p, s);
+}
+
+#define REGTILE_STAGED_NAMES(elt, tile)                                                        \
+    { elt "_mfma_" tile, elt "_mfma_" tile "_vec", elt "_mfma_" tile "_edge", elt "_mfma_" tile "_edge_vec" }
+// [f16][big][edge * 2 + vec]
+const char *const kStagedNames[2][2][4] = {
+    {REGTILE_STAGED_NAMES("bf16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("bf16", "256x256x64_w2x4")},
+    {REGTILE_STAGED_NAMES("f16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("f16", "256x256x64_w2x4")}};
+#undef REGTILE_STAGED_NAMES
 
 }  // namespace
 
-hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape) {
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
+                            bool f16) {
     // Full aligned 256x256 tiles, enough of them to fill the chip: the LDS-DMA kernel,
     // else the register-staged kernel below.
     if ((int64_t)(p.M / 256) * (p.N / 256) >= 128) {
-        const hipError_t e = launch_bf16_mfma_dma(p, s, name, shape);
+        const hipError_t e = launch_bf16_mfma_dma(p, s, name, shape, f16);
         if (e != hipErrorNotSupported) return e;
     }
     const bool vec = (p.lda % 8) == 0 && (p.ldb % 8) == 0 && aligned16(p.A) && aligned16(p.B);
     const bool big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
-    if (big) {
-        const bool edge = (p.M % 256) != 0 || (p.N % 256) != 0 || (p.K % BK) != 0;
-        *name = edge ? (vec ? "bf16_mfma_256x256x64_w2x4_edge_vec" : "bf16_mfma_256x256x64_w2x4_edge")
-                     : (vec ? "bf16_mfma_256x256x64_w2x4_vec" : "bf16_mfma_256x256x64_w2x4");
-        if (edge) return vec ? launch_cfg<256, 256, 2, 4, true, true>(p, s)
-                             : launch_cfg<256, 256, 2, 4, true, false>(p, s);
-        return vec ? launch_cfg<256, 256, 2, 4, false, true>(p, s)
-                   : launch_cfg<256, 256, 2, 4, false, false>(p, s);
-    }
-    const bool edge = (p.M % 128) != 0 || (p.N % 128) != 0 || (p.K % BK) != 0;
-    *name = edge ? (vec ? "bf16_mfma_128x128x64_w2x2_edge_vec" : "bf16_mfma_128x128x64_w2x2_edge")
-                 : (vec ? "bf16_mfma_128x128x64_w2x2_vec" : "bf16_mfma_128x128x64_w2x2");
-    if (edge) return vec ? launch_cfg<128, 128, 2, 2, true, true>(p, s)
-                         : launch_cfg<128, 128, 2, 2, true, false>(p, s);
-    return vec ? launch_cfg<128, 128, 2, 2, false, true>(p, s)
-               : launch_cfg<128, 128, 2, 2, false, false>(p, s);
+    const int tile = big ? 256 : 128;
+    const bool edge = (p.M % tile) != 0 || (p.N % tile) != 0 || (p.K % BK) != 0;
+    *name = kStagedNames[f16][big][edge * 2 + vec];
+    if (big)
+        return f16 ? launch_pick<256, 256, 2, 4, true>(p, s, edge, vec)
+                   : launch_pick<256, 256, 2, 4, false>(p, s, edge, vec);
+    return f16 ? launch_pick<128, 128, 2, 2, true>(p, s, edge, vec)
+               : launch_pick<128, 128, 2, 2, false>(p, s, edge, vec);
 }
 
 }  // namespace regtile

@@ -36,7 +36,7 @@ namespace regtile {
 namespace {
 using namespace mfma;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr int KCH = BK / 8;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    typedef Frag<MF> F;
+    typedef Frag<MF, F16> F;
     constexpr int MI = WTM / MF, NI = WTN / MF;
     constexpr int A_SLOTS = BM * KCH, B_SLOTS = BN * KCH;  // 16-byte slots per stage
     constexpr int STAGE_SLOTS = A_SLOTS + B_SLOTS;
@@ -268,10 +268,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER>
+template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -299,7 +299,8 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 
 // Returns hipErrorNotSupported (and launches nothing) unless the problem is made of full
 // tiles with 16-byte aligned, K-contiguous rows.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape) {
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
+                                bool f16) {
     const bool ok = p.M % DMA_BM == 0 && p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
                     p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
                     (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
@@ -307,15 +308,23 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
                     (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
                     (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128 && (shape == 32 || shape == 16);
     if (!ok) return hipErrorNotSupported;
-#define REGTILE_DMA_NAME(mf)                                                                   \
-    "bf16_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK) \
+#define REGTILE_DMA_NAME(elt, mf)                                                                  \
+    elt "_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)     \
         "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN)
-    if (shape == 16) {
-        *name = REGTILE_DMA_NAME("16x16x32");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16>(p, s);
+    if (f16) {
+        if (shape == 16) {
+            *name = REGTILE_DMA_NAME("f16", "16x16x32");
+            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, true>(p, s);
+        }
+        *name = REGTILE_DMA_NAME("f16", "32x32x16");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true>(p, s);
     }
-    *name = REGTILE_DMA_NAME("32x32x16");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32>(p, s);
+    if (shape == 16) {
+        *name = REGTILE_DMA_NAME("bf16", "16x16x32");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, false>(p, s);
+    }
+    *name = REGTILE_DMA_NAME("bf16", "32x32x16");
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false>(p, s);
 #undef REGTILE_DMA_NAME
 }
 

@@ -42,8 +42,12 @@ __device__ __forceinline__ float load_as_f32(const T *p);
 template <>
 __device__ __forceinline__ float load_as_f32<float>(const float *p) { return *p; }
 template <>
-__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p) {
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p) {  // bf16 bits
     return __uint_as_float(((uint32_t)(*p)) << 16);
+}
+template <>
+__device__ __forceinline__ float load_as_f32<_Float16>(const _Float16 *p) {  // fp16, exact
+    return (float)*p;
 }
 
 template <typename T, bool B_COL_MAJOR>
@@ -78,12 +82,19 @@ hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name) 
     return hipGetLastError();
 }
 
-hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name) {
+hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name, bool f16) {
     dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
-    hipLaunchKernelGGL((naive_kernel<uint16_t, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                       p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
-                       p.beta, p.C, p.ldc);
-    *name = "bf16_naive";
+    if (f16) {
+        hipLaunchKernelGGL((naive_kernel<_Float16, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, (const _Float16 *)p.A, p.lda, (const _Float16 *)p.B, p.ldb,
+                           p.beta, p.C, p.ldc);
+        *name = "f16_naive";
+    } else {
+        hipLaunchKernelGGL((naive_kernel<uint16_t, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
+                           p.beta, p.C, p.ldc);
+        *name = "bf16_naive";
+    }
     return hipGetLastError();
 }
 

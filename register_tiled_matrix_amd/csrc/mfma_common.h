@@ -1,6 +1,6 @@
-// mfma_common.h -- device helpers shared by the bf16 MFMA kernels that stage operands with
+// mfma_common.h -- device helpers shared by the 16-bit MFMA kernels that stage operands with
 // LDS DMA: fragment types, the slab swizzle, the DMA load, counter waits, a barrier that
-// waits on nothing, and the two gfx950 bf16 MFMA fragment shapes.
+// waits on nothing, and the two gfx950 MFMA fragment shapes for bf16 and fp16 operands.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,32 +100,44 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// The two gfx950 bf16 MFMA fragment shapes. Per lane: 8 bf16 of A (row lane % MF, k group
-// lane / MF), 8 bf16 of B (column lane % MF, same k group), and MF*MF/64 fp32 accumulators.
-//   MF = 32: v_mfma_f32_32x32x16_bf16, 16 k per instruction, accumulator v of lane l holds
-//            row (v/4)*8 + (l/32)*4 + v%4, column l%32;
-//   MF = 16: v_mfma_f32_16x16x32_bf16, 32 k per instruction, accumulator v holds row
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+
+// The two gfx950 MFMA fragment shapes for 16-bit operands (bf16 or fp16, fp32 accumulate).
+// Per lane: 8 values of A (row lane % MF, k group lane / MF), 8 values of B (column lane % MF,
+// same k group), and MF*MF/64 fp32 accumulators. Fragments are held as raw 16-bit patterns
+// (bf16x8) whichever the element type; the fp16 form reinterprets them at the instruction.
+//   MF = 32: v_mfma_f32_32x32x16_{bf16,f16}, 16 k per instruction, accumulator v of lane l
+//            holds row (v/4)*8 + (l/32)*4 + v%4, column l%32;
+//   MF = 16: v_mfma_f32_16x16x32_{bf16,f16}, 32 k per instruction, accumulator v holds row
 //            (l/16)*4 + v, column l%16.
 // The row splits into a per-lane part (row_lane) and a compile-time per-accumulator part
 // (row_acc), so the epilogue's address arithmetic stays constant offsets.
-template <int MF>
+template <int MF, bool F16 = false>
 struct Frag;
-template <>
-struct Frag<32> {
+template <bool F16>
+struct Frag<32, F16> {
     typedef f32x16 acc_t;
     static constexpr int KSTEP = 16, NACC = 16;
     __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+        if constexpr (F16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static int row_lane(int lane) { return (lane >> 5) * 4; }
     __device__ static constexpr int row_acc(int v) { return (v >> 2) * 8 + (v & 3); }
 };
-template <>
-struct Frag<16> {
+template <bool F16>
+struct Frag<16, F16> {
     typedef f32x4 acc_t;
     static constexpr int KSTEP = 32, NACC = 4;
     __device__ static acc_t mfma(bf16x8 a, bf16x8 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+        if constexpr (F16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static int row_lane(int lane) { return (lane >> 4) * 4; }
     __device__ static constexpr int row_acc(int v) { return v; }

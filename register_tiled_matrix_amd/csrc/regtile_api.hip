@@ -95,8 +95,8 @@ int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *
     return finish(err, name);
 }
 
-int run_bf16(int shift, int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
-             const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+int run_16b(bool f16, int shift, int algo, int M, int N, int K, float alpha, const uint16_t *A,
+            int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
     if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA_16X16) return -1;
     const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (v != REGTILE_OK) return v;
@@ -107,9 +107,9 @@ int run_bf16(int shift, int algo, int M, int N, int K, float alpha, const uint16
     const char *name = "none";
     hipError_t err;
     switch (algo) {
-        case REGTILE_BF16_NAIVE: err = regtile::launch_bf16_naive(p, s, &name); break;
-        case REGTILE_BF16_MFMA_16X16: err = regtile::launch_bf16_mfma(p, s, &name, 16); break;
-        default: err = regtile::launch_bf16_mfma(p, s, &name, 32); break;
+        case REGTILE_BF16_NAIVE: err = regtile::launch_bf16_naive(p, s, &name, f16); break;
+        case REGTILE_BF16_MFMA_16X16: err = regtile::launch_bf16_mfma(p, s, &name, 16, f16); break;
+        default: err = regtile::launch_bf16_mfma(p, s, &name, 32, f16); break;
     }
     return finish(err, name);
 }
@@ -125,7 +125,7 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
 
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
               int ldb, float beta, float *C, int ldc, void *stream) {
-    return run_bf16(0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(false, 0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const float *A, int lda,
@@ -136,7 +136,17 @@ int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const floa
 int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A,
                            int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
                            void *stream) {
-    return run_bf16(1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(false, 1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_f16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+             int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_16b(true, 0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                          const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_16b(true, 1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 const char *regtile_last_kernel(void) { return g_last_kernel; }

@@ -27,12 +27,15 @@ hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_regtile(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_regtile_small(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name);
-hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name);
+// 16-bit operand kernels: `f16` selects IEEE fp16 operands, otherwise bf16.
+hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name, bool f16);
 // MFMA kernels; `shape` 32 selects 32x32x16 fragments, 16 selects 16x16x32 (full aligned
 // tiles only, others keep the 32x32x16 register-staged kernel).
-hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape);
+hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
+                            bool f16);
 // Full aligned tiles only; return hipErrorNotSupported without launching otherwise.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape);
+hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
+                                bool f16);
 
 // Host-side launch checks.
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -18,13 +18,15 @@ def announce(msg: str) -> None:
 
 
 def device_operands(inp: gi.GemmInputs, torch, device="cuda"):
-    """(A, B, C) device tensors in the library's layouts; B is a column-major view for bf16."""
+    """(A, B, C) device tensors in the library's layouts; B is a column-major view for the
+    16-bit types (bf16, fp16)."""
     if inp.dtype == "f32":
         A = torch.from_numpy(np.ascontiguousarray(inp.A)).to(device)
         B = torch.from_numpy(np.ascontiguousarray(inp.B)).to(device)
     else:
-        A = torch.from_numpy(np.ascontiguousarray(inp.A).view(np.int16)).to(device).view(torch.bfloat16)
-        Bt = torch.from_numpy(np.ascontiguousarray(inp.B).view(np.int16)).to(device).view(torch.bfloat16)
+        tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float16
+        A = torch.from_numpy(np.ascontiguousarray(inp.A).view(np.int16)).to(device).view(tdt)
+        Bt = torch.from_numpy(np.ascontiguousarray(inp.B).view(np.int16)).to(device).view(tdt)
         B = Bt.t()
     if inp.C is not None:
         C = torch.from_numpy(np.ascontiguousarray(inp.C)).to(device)
@@ -38,10 +40,8 @@ def run(inp: gi.GemmInputs, torch, algo=0, C_init=None):
     A, B, C = device_operands(inp, torch)
     if C_init is not None:
         C.copy_(C_init)
-    if inp.dtype == "f32":
-        rt.gemm_f32(A, B, C, alpha=inp.alpha, beta=inp.beta, algo=algo)
-    else:
-        rt.gemm_bf16(A, B, C, alpha=inp.alpha, beta=inp.beta, algo=algo)
+    fn = {"f32": rt.gemm_f32, "bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[inp.dtype]
+    fn(A, B, C, alpha=inp.alpha, beta=inp.beta, algo=algo)
     torch.cuda.synchronize()
     return C
 

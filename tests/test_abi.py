@@ -86,6 +86,9 @@ def test_f32_argument_validation(lib, args, expect):
 def test_bf16_argument_validation(lib, args, expect):
     assert rt.gemm_bf16_raw(*args, 0) == expect
     assert rt.regtile_gemm_bf16_algo(rt.ALGO_BF16_MFMA, *args, 0) == expect - 1
+    # fp16 shares the 16-bit layout rules
+    assert rt.gemm_f16_raw(*args, 0) == expect
+    assert rt.regtile_gemm_f16_algo(rt.ALGO_BF16_MFMA, *args, 0) == expect - 1
 
 
 def test_unknown_algorithm_is_argument_one(lib):
@@ -93,6 +96,7 @@ def test_unknown_algorithm_is_argument_one(lib):
     assert rt.regtile_gemm_f32_algo(6, *a) == -1
     assert rt.regtile_gemm_f32_algo(-1, *a) == -1
     assert rt.regtile_gemm_bf16_algo(4, *a) == -1
+    assert rt.regtile_gemm_f16_algo(4, *a) == -1
 
 
 def test_null_operands_allowed_when_not_read(lib):
@@ -110,6 +114,8 @@ def test_binding_rejects_host_tensors_and_bad_layouts(lib):
         rt.gemm_f32(a, a)
     with pytest.raises(ValueError):
         rt.gemm_bf16(a.bfloat16(), a.bfloat16())
+    with pytest.raises(ValueError):
+        rt.gemm_f16(a.half(), a.half())
 
 
 def test_kernels_have_no_scratch_and_stated_occupancy():

@@ -175,8 +175,73 @@ def test_closed_forms_on_gpu():
     assert np.all(run(hones, torch).cpu().numpy() == 1000.0)
 
 
+# ---- fp16 operands (the pages' half-precision GEMM) on the same MFMA kernels -----------------
+F16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16, rt.ALGO_BF16_AUTO]
+
+
+@pytest.mark.parametrize("algo", [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16])
+def test_f16_8192_sampled(algo):
+    inp = gi.workload_inputs(gi.WORKLOADS["f16_8192"])
+    announce(f"f16_8192 algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    shape = "16x16x32" if algo == rt.ALGO_BF16_MFMA_16X16 else "32x32x16"
+    assert f"f16_mfma{shape}_dma" in rt.last_kernel()
+    assert_parity_sampled(inp, got, f"f16_8192 ({rt.last_kernel()})", n_random=30000)
+
+
+@pytest.mark.parametrize("algo", F16_ALGOS)
+@pytest.mark.parametrize("shape", [(512, 768, 1024), (300, 257, 777), (2048, 4096, 192)])
+def test_f16_full(algo, shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f16", dist="normal", alpha=1.5, beta=-0.5, seed=M + N + K + 1)
+    announce(f"f16 {shape} algo={algo}")
+    got = run(inp, torch, algo).cpu().numpy()
+    name = rt.last_kernel()
+    assert name.startswith("f16_")
+    if shape == (2048, 4096, 192) and algo != rt.ALGO_BF16_NAIVE:
+        assert "_dma_" in name
+    assert_parity_full(inp, got, f"f16 {shape} algo {algo} ({name})")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (17, 33, 9), (129, 127, 17), (257, 255, 65), (131, 293, 300)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f16_mfma_edges(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f16", dist="normal", alpha=-1.25, beta=0.75, seed=M * 5 + N + K)
+    announce(f"f16 edges {shape}")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    assert_parity_full(inp, got, f"f16 edges {shape}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 2048), (2048, 4096, 1024)])
+def test_f16_integer_inputs_are_bitwise_exact(M, N, K):
+    # integers in [-16, 16] are exact in fp16; every partial sum stays below 2^24
+    rng = np.random.Generator(np.random.PCG64(80 + M))
+    A = gi.f32_to_f16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_f16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f16", True, A, Bt, None)
+    announce(f"f16 integer bitwise {M}x{N}x{K}")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    I, J = sample_positions(M, N, n_random=50000, seed=4)
+    ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref)
+
+
+def test_f16_and_bf16_kernels_differ_only_in_the_element_type():
+    # the same 16-bit patterns read as fp16 and as bf16 give different products (a kernel that
+    # ignored the element type would pass one of the two parity checks only by accident)
+    inp16 = gi.make_inputs(256, 256, 512, dtype="f16", dist="normal", seed=31)
+    as_bf16 = gi.GemmInputs(256, 256, 512, 1.0, 0.0, "bf16", True, inp16.A, inp16.B, None)
+    announce("f16 vs bf16 element type")
+    g16 = run(inp16, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    g_bf = run(as_bf16, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
+    assert_parity_full(inp16, g16, "f16 reading")
+    assert_parity_full(as_bf16, g_bf, "bf16 reading of the same bits")
+    assert not np.allclose(g16, g_bf)
+
+
 # ---- epilogue conventions -----------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_beta_zero_never_reads_c(dtype):
     inp = gi.make_inputs(200, 300, 64, dtype=dtype, dist="normal", seed=3)
     announce(f"beta=0 NaN C {dtype}")
@@ -185,7 +250,7 @@ def test_beta_zero_never_reads_c(dtype):
     assert_parity_full(inp, got, "beta=0 with NaN C")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_alpha_zero_and_k_zero_scale_c(dtype):
     M, N = 70, 90
     rng = np.random.Generator(np.random.PCG64(5))
@@ -195,7 +260,7 @@ def test_alpha_zero_and_k_zero_scale_c(dtype):
     inp.C = C0
     A, B, C = device_operands(inp, torch)
     A.fill_(float("nan"))
-    fn = rt.gemm_f32 if dtype == "f32" else rt.gemm_bf16
+    fn = {"f32": rt.gemm_f32, "bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[dtype]
     fn(A, B, C, alpha=0.0, beta=-2.0)
     torch.cuda.synchronize()
     assert rt.last_kernel() == "scale_c"
