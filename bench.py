@@ -328,6 +328,42 @@ def main():
         out["bf16_8192"] = leg_16b("bf16_8192", rt.gemm_bf16_raw, rt.regtile_gemm_bf16_algo, "bf16")
         out["f16_8192"] = leg_16b("f16_8192", rt.gemm_f16_raw, rt.regtile_gemm_f16_algo, "fp16")
 
+    # ---- operand layouts (BLAS transpose flags over row-major storage) ----------------------
+    if not args.no_ladder:
+        lay = {}
+        for wname, ex in (("f32_4096", rt.regtile_gemm_f32_ex), ("bf16_8192", rt.regtile_gemm_bf16_ex)):
+            wl = gi.WORKLOADS[wname]
+            il = gi.workload_inputs(wl)
+            if wl.dtype == "f32":
+                Am = torch.from_numpy(il.A).to(dev)
+                Bm = torch.from_numpy(il.B).to(dev)
+            else:
+                Am = torch.from_numpy(il.A.view(np.int16)).to(dev)
+                Bm = torch.from_numpy(il.B.view(np.int16)).to(dev)
+            Cm = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+            for ta in (0, 1):
+                for tb in (0, 1):
+                    # the same values in the requested storage (square problems: the transposed
+                    # copy has the same leading dimension)
+                    A_ = Am.t().contiguous() if ta else Am
+                    B_ = Bm if (tb == 1) == (wl.dtype != "f32") else Bm.t().contiguous()
+                    call = (0, ta, tb, wl.M, wl.N, wl.K, 1.0, A_.data_ptr(), wl.K, B_.data_ptr(),
+                            wl.K, 0.0, Cm.data_ptr(), wl.N, stream)
+
+                    def step_l(call=call, ex=ex):
+                        st = ex(*call)
+                        if st:
+                            raise rt.RegtileError(st, rt.strerror(st))
+
+                    step_l()
+                    _, kms, _ = _time(torch, step_l, max(3, args.steps // 4), 2)
+                    code = ("n", "t")[ta] + ("n", "t")[tb]
+                    lay[f"{wname}_{code}"] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
+                                              "TFLOP/s": round(wl.flop / (kms * 1e-3) / 1e12, 2)}
+                    del A_, B_
+            del Am, Bm, Cm
+        out["layouts"] = lay
+
     # ---- the ladder on the headline workload ------------------------------------------------
     if not args.no_ladder:
         ladder = {}

@@ -128,6 +128,33 @@ int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uin
 int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
                           const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream);
 
+/*
+ * regtile_gemm_f32_ex / regtile_gemm_bf16_ex / regtile_gemm_f16_ex -- the same products with
+ * the storage of each operand chosen (BLAS transpose flags over row-major storage; a step to
+ * either side of the pages' row-major kernels):
+ *   algo     (arg 1) a regtile_algo_f32 value (fp32) or regtile_algo_bf16 value (16-bit);
+ *            -1 if unknown or if that rung stages row-major operands only (the fp32 LDS-tiled
+ *            and split-K rungs accept trans_a == trans_b == 0 only)
+ *   trans_a  (arg 2) 0: A stored M x K row-major, lda >= max(1,K);
+ *                    1: A stored K x M row-major (op(A) is its transpose), lda >= max(1,M)
+ *   trans_b  (arg 3) 0: B stored K x N row-major, ldb >= max(1,N);
+ *                    1: B stored N x K row-major (column-major K x N), ldb >= max(1,K)
+ *   the rest as gemm_f32 / gemm_bf16 / gemm_f16 at positions 4-15; -2 / -3 for a flag other
+ *   than 0 or 1. gemm_f32 is (AUTO, 0, 0) and gemm_bf16 / gemm_f16 are (AUTO, 0, 1).
+ * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit); only
+ * the 16-bit (0, 1) pair takes the LDS-DMA kernel, the others gather the M- or N-contiguous
+ * operand into K-contiguous LDS slabs with scalar loads.
+ */
+int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                        int ldc, void *stream);
+int regtile_gemm_bf16_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                         const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta,
+                         float *C, int ldc, void *stream);
+int regtile_gemm_f16_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta,
+                        float *C, int ldc, void *stream);
+
 /* Name of the kernel the calling thread launched last ("none" before the first launch,
  * "quick-return" when nothing was launched). Static storage; do not free. */
 const char *regtile_last_kernel(void);

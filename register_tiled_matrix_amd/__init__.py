@@ -10,8 +10,10 @@ Entry points (same names as the C ABI):
   fp32 ``C = alpha*A@B + beta*C``; A (M x K) and B (K x N) row-major fp32 CUDA tensors
   (row stride may exceed the width), C (M x N) row-major fp32.
 * ``gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO)``
-  bf16 A (M x K, row-major) times bf16 B given as a K x N column-major view (for example
-  ``Bt.t()`` for a contiguous N x K tensor ``Bt``), fp32 C.
+  bf16 A (M x K) times bf16 B (K x N), fp32 C; the fast path is row-major A with B given as a
+  column-major view (for example ``Bt.t()`` for a contiguous N x K tensor ``Bt``).
+* Every tensor entry point accepts A and B either row-major or as transposed (column-major)
+  views and passes the layout to the ``regtile_gemm_*_ex`` entry points.
 * ``gemm_f16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO)`` the same with
   float16 A and B (IEEE binary16); the algorithm values are the bf16 ones.
 * ``gemm_f32_raw`` / ``gemm_bf16_raw`` / ``gemm_f16_raw`` take the C arguments verbatim
@@ -34,6 +36,7 @@ __all__ = [
     "RegtileError", "RegtileLibraryMissing", "lib_path", "load",
     "gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_raw", "gemm_bf16_raw", "gemm_f16_raw",
     "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
+    "regtile_gemm_f32_ex", "regtile_gemm_bf16_ex", "regtile_gemm_f16_ex",
     "last_kernel", "strerror", "version", "EXPORTED_SYMBOLS",
 ]
 
@@ -42,7 +45,8 @@ ALGO_F32_REGTILE_SMALL = 5
 ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA, ALGO_BF16_MFMA_16X16 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "gemm_f16", "regtile_gemm_f32_algo",
-                    "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
+                    "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo", "regtile_gemm_f32_ex",
+                    "regtile_gemm_bf16_ex", "regtile_gemm_f16_ex",
                     "regtile_last_kernel", "regtile_strerror", "regtile_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +83,9 @@ def load():
         gemm = [I, I, I, F, P, I, P, I, F, P, I, P]
         for name, args in (("gemm_f32", gemm), ("gemm_bf16", gemm), ("gemm_f16", gemm),
                            ("regtile_gemm_f16_algo", [I] + gemm),
+                           ("regtile_gemm_f32_ex", [I, I, I] + gemm),
+                           ("regtile_gemm_bf16_ex", [I, I, I] + gemm),
+                           ("regtile_gemm_f16_ex", [I, I, I] + gemm),
                            ("regtile_gemm_f32_algo", [I] + gemm),
                            ("regtile_gemm_bf16_algo", [I] + gemm)):
             f = getattr(lib, name)
@@ -134,6 +141,24 @@ def regtile_gemm_f16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st
                                         stream)
 
 
+def regtile_gemm_f32_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        stream=0) -> int:
+    return load().regtile_gemm_f32_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                      beta, C, ldc, stream)
+
+
+def regtile_gemm_bf16_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=0) -> int:
+    return load().regtile_gemm_bf16_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                       beta, C, ldc, stream)
+
+
+def regtile_gemm_f16_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        stream=0) -> int:
+    return load().regtile_gemm_f16_ex(algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                      beta, C, ldc, stream)
+
+
 def regtile_gemm_bf16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
     return load().regtile_gemm_bf16_algo(algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                          stream)
@@ -160,14 +185,18 @@ def _row_major_ld(t, name):
     return max(int(t.stride(0)), int(t.shape[1]), 1)
 
 
-def _col_major_ld(t, name):
+def _layout(t, name):
+    """(trans, ld) of a 2-D operand: row-major storage (unit column stride) -> (0, row stride);
+    column-major storage (unit row stride), i.e. the transpose of a row-major matrix ->
+    (1, column stride). Anything else (overlapping or non-unit strides) is rejected."""
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.shape[0] > 1 and t.stride(0) != 1:
-        raise ValueError(f"{name} must be column-major (unit row stride), e.g. Bt.t()")
-    if t.shape[1] > 1 and t.stride(1) < t.shape[0]:
-        raise ValueError(f"{name} columns overlap (column stride below the height)")
-    return max(int(t.stride(1)), int(t.shape[0]), 1)
+    r, c = t.shape
+    if (c <= 1 or t.stride(1) == 1) and (r <= 1 or t.stride(0) >= c):
+        return 0, max(int(t.stride(0)), int(c), 1)
+    if (r <= 1 or t.stride(0) == 1) and (c <= 1 or t.stride(1) >= r):
+        return 1, max(int(t.stride(1)), int(r), 1)
+    raise ValueError(f"{name} must be row-major or column-major with non-overlapping rows")
 
 
 def _out(C, M, N, like):
@@ -180,30 +209,7 @@ def _out(C, M, N, like):
     return C
 
 
-def gemm_f32(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_F32_AUTO, stream=None):
-    """C = alpha*A@B + beta*C on fp32 CUDA tensors; returns C (allocated when None)."""
-    import torch
-
-    if A.dtype != torch.float32 or B.dtype != torch.float32:
-        raise ValueError("gemm_f32 takes float32 A and B")
-    if not (A.is_cuda and B.is_cuda):
-        raise ValueError("gemm_f32 takes device tensors")
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    if C is None and beta != 0.0:
-        raise ValueError("beta != 0 needs C")
-    C = _out(C, M, N, A)
-    lda, ldb, ldc = _row_major_ld(A, "A"), _row_major_ld(B, "B"), _row_major_ld(C, "C")
-    st = regtile_gemm_f32_algo(int(algo), M, N, K, float(alpha), A.data_ptr(), lda,
-                               B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
-                               _stream_handle(A, stream))
-    _check(st)
-    return C
-
-
-def _gemm_16b(fn, want, label, A, B, C, alpha, beta, algo, stream):
+def _gemm(fn, want, label, A, B, C, alpha, beta, algo, stream):
     if A.dtype != want or B.dtype != want:
         raise ValueError(f"{label} takes {want} A and B")
     if not (A.is_cuda and B.is_cuda):
@@ -215,25 +221,36 @@ def _gemm_16b(fn, want, label, A, B, C, alpha, beta, algo, stream):
     if C is None and beta != 0.0:
         raise ValueError("beta != 0 needs C")
     C = _out(C, M, N, A)
-    lda, ldb, ldc = _row_major_ld(A, "A"), _col_major_ld(B, "B"), _row_major_ld(C, "C")
-    st = fn(int(algo), M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta),
-            C.data_ptr(), ldc, _stream_handle(A, stream))
+    (ta, lda), (tb, ldb) = _layout(A, "A"), _layout(B, "B")
+    ldc = _row_major_ld(C, "C")
+    st = fn(int(algo), ta, tb, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+            float(beta), C.data_ptr(), ldc, _stream_handle(A, stream))
     _check(st)
     return C
 
 
-def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
-    """C = alpha*A@B + beta*C; A bf16 (M x K) row-major, B bf16 (K x N) column-major view,
-    C fp32 (M x N) row-major; returns C (allocated when None)."""
+def gemm_f32(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_F32_AUTO, stream=None):
+    """C = alpha*A@B + beta*C on fp32 CUDA tensors; returns C (allocated when None). A and B
+    may each be row-major or a transposed (column-major) view; C is row-major."""
     import torch
 
-    return _gemm_16b(regtile_gemm_bf16_algo, torch.bfloat16, "gemm_bf16", A, B, C, alpha, beta,
-                     algo, stream)
+    return _gemm(regtile_gemm_f32_ex, torch.float32, "gemm_f32", A, B, C, alpha, beta, algo,
+                 stream)
+
+
+def gemm_bf16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
+    """C = alpha*A@B + beta*C; bf16 A (M x K) and B (K x N), each row-major or a transposed
+    view (the fast path is row-major A with column-major B, e.g. ``Bt.t()``), fp32 C row-major;
+    returns C (allocated when None)."""
+    import torch
+
+    return _gemm(regtile_gemm_bf16_ex, torch.bfloat16, "gemm_bf16", A, B, C, alpha, beta, algo,
+                 stream)
 
 
 def gemm_f16(A, B, C=None, alpha=1.0, beta=0.0, algo=ALGO_BF16_AUTO, stream=None):
     """As gemm_bf16 with float16 (IEEE binary16) A and B."""
     import torch
 
-    return _gemm_16b(regtile_gemm_f16_algo, torch.float16, "gemm_f16", A, B, C, alpha, beta,
-                     algo, stream)
+    return _gemm(regtile_gemm_f16_ex, torch.float16, "gemm_f16", A, B, C, alpha, beta, algo,
+                 stream)

@@ -67,7 +67,26 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool
     return r;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VEC_C, bool F16>
+// 8 consecutive k values of one M (or N) index from an operand stored K-major-outer (element
+// (r, k) at p[k * ld] relative to the chunk's first one): 8 scalar loads, zero outside.
+__device__ __forceinline__ uint4 load_chunk_mn(const uint16_t *__restrict__ p, int64_t ld,
+                                               bool row_ok, int k_left) {
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (row_ok && e < k_left) ? p[e * ld] : (uint16_t)0;
+    uint4 r;
+    r.x = v[0] | ((uint32_t)v[1] << 16);
+    r.y = v[2] | ((uint32_t)v[3] << 16);
+    r.z = v[4] | ((uint32_t)v[5] << 16);
+    r.w = v[6] | ((uint32_t)v[7] << 16);
+    return r;
+}
+
+// A_MN: A stored K x M (M-contiguous); B_MN: B stored K x N (N-contiguous). The LDS slab is
+// K-contiguous either way; an MN-contiguous operand is gathered with scalar loads that are
+// coalesced across lanes (consecutive lanes take consecutive M / N indices).
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VEC_C, bool F16,
+          bool A_MN = false, bool B_MN = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -100,24 +119,49 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     const int64_t a_pass = (int64_t)ROWS_PER_PASS * lda;
     const int64_t b_pass = (int64_t)ROWS_PER_PASS * ldb;
 
+    // MN-contiguous staging: slot e = tid + NT*i is row e % BM (or BN), chunk e / BM.
+    static_assert(!A_MN || NT % BM == 0, "whole rows per pass");
+    static_assert(!B_MN || NT % BN == 0, "whole rows per pass");
+    constexpr int A_MN_CPP = A_MN ? NT / BM : 1, B_MN_CPP = B_MN ? NT / BN : 1;  // chunks per pass
+    const int amn_row = tid % BM, amn_chunk = tid / BM;
+    const int bmn_row = tid % BN, bmn_chunk = tid / BN;
+
     uint4 ra[A_CH], rb[B_CH];
     auto load_slab = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            ra[i] = load_chunk<EDGE, VEC>(a_src + i * a_pass + k0,
-                                          m0 + ld_row + i * ROWS_PER_PASS < M,
-                                          K - k0 - ld_chunk * 8);
+        for (int i = 0; i < A_CH; ++i) {
+            if (A_MN) {
+                const int kc = k0 + (amn_chunk + i * A_MN_CPP) * 8;
+                ra[i] = load_chunk_mn(A + (int64_t)kc * lda + m0 + amn_row, lda, m0 + amn_row < M, K - kc);
+            } else {
+                ra[i] = load_chunk<EDGE, VEC>(a_src + i * a_pass + k0,
+                                              m0 + ld_row + i * ROWS_PER_PASS < M,
+                                              K - k0 - ld_chunk * 8);
+            }
+        }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            rb[i] = load_chunk<EDGE, VEC>(b_src + i * b_pass + k0,
-                                          n0 + ld_row + i * ROWS_PER_PASS < N,
-                                          K - k0 - ld_chunk * 8);
+        for (int i = 0; i < B_CH; ++i) {
+            if (B_MN) {
+                const int kc = k0 + (bmn_chunk + i * B_MN_CPP) * 8;
+                rb[i] = load_chunk_mn(B + (int64_t)kc * ldb + n0 + bmn_row, ldb, n0 + bmn_row < N, K - kc);
+            } else {
+                rb[i] = load_chunk<EDGE, VEC>(b_src + i * b_pass + k0,
+                                              n0 + ld_row + i * ROWS_PER_PASS < N,
+                                              K - k0 - ld_chunk * 8);
+            }
+        }
     };
     auto store_slab = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) sA[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = ra[i];
+        for (int i = 0; i < A_CH; ++i) {
+            if (A_MN) sA[buf][swz(amn_row, amn_chunk + i * A_MN_CPP)] = ra[i];
+            else sA[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = ra[i];
+        }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) sB[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = rb[i];
+        for (int i = 0; i < B_CH; ++i) {
+            if (B_MN) sB[buf][swz(bmn_row, bmn_chunk + i * B_MN_CPP)] = rb[i];
+            else sB[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = rb[i];
+        }
     };
 
     f32x16 acc[MI][NI];
@@ -186,10 +230,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     (void)VEC_C;
 }
 
-template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16>
+template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16, bool A_MN = false,
+          bool B_MN = false>
 hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16>),
+    hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16, A_MN, B_MN>),
                        dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
                        (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,
                        p.ldc, tiles_m, tiles_n);
@@ -204,6 +249,20 @@ hipError_t launch_pick(const Problem &p, hipStream_t s, bool edge, bool vec) {
                : launch_cfg<BM, BN, WM, WN, false, false, F16>(p, s);
 }
 
+// Operands other than K-contiguous A and B: 128x128 tiles, edge-predicated kernel; `vec` only
+// matters for a K-contiguous operand.
+template <bool F16>
+hipError_t launch_layout(const Problem &p, hipStream_t s, bool vec) {
+    const bool a_mn = p.ta, b_mn = !p.tb;
+    if (a_mn && b_mn)
+        return launch_cfg<128, 128, 2, 2, true, false, F16, true, true>(p, s);
+    if (a_mn)
+        return vec ? launch_cfg<128, 128, 2, 2, true, true, F16, true, false>(p, s)
+                   : launch_cfg<128, 128, 2, 2, true, false, F16, true, false>(p, s);
+    return vec ? launch_cfg<128, 128, 2, 2, true, true, F16, false, true>(p, s)
+               : launch_cfg<128, 128, 2, 2, true, false, F16, false, true>(p, s);
+}
+
 #define REGTILE_STAGED_NAMES(elt, tile)                                                        \
     { elt "_mfma_" tile, elt "_mfma_" tile "_vec", elt "_mfma_" tile "_edge", elt "_mfma_" tile "_edge_vec" }
 // [f16][big][edge * 2 + vec]
@@ -211,11 +270,24 @@ const char *const kStagedNames[2][2][4] = {
     {REGTILE_STAGED_NAMES("bf16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("bf16", "256x256x64_w2x4")},
     {REGTILE_STAGED_NAMES("f16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("f16", "256x256x64_w2x4")}};
 #undef REGTILE_STAGED_NAMES
+// [f16][layout code: 0 = "tt", 1 = "tn", 2 = "nn"][vec], BLAS letters of op(A), op(B) storage
+#define REGTILE_LAYOUT_NAMES(elt, lay)                                                          \
+    { elt "_mfma_128x128x64_w2x2_" lay "_edge", elt "_mfma_128x128x64_w2x2_" lay "_edge_vec" }
+const char *const kLayoutNames[2][3][2] = {
+    {REGTILE_LAYOUT_NAMES("bf16", "tt"), REGTILE_LAYOUT_NAMES("bf16", "tn"), REGTILE_LAYOUT_NAMES("bf16", "nn")},
+    {REGTILE_LAYOUT_NAMES("f16", "tt"), REGTILE_LAYOUT_NAMES("f16", "tn"), REGTILE_LAYOUT_NAMES("f16", "nn")}};
+#undef REGTILE_LAYOUT_NAMES
 
 }  // namespace
 
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16) {
+    if (p.ta || !p.tb) {  // not the native K-contiguous pair
+        const bool vec = (p.ta ? (p.ldb % 8) == 0 && aligned16(p.B) : (p.lda % 8) == 0 && aligned16(p.A));
+        const int lay = (p.ta && p.tb) ? 0 : p.ta ? 1 : 2;  // tt: A K x M, B N x K; tn; nn
+        *name = kLayoutNames[f16][lay][vec && !(p.ta && !p.tb)];
+        return f16 ? launch_layout<true>(p, s, vec) : launch_layout<false>(p, s, vec);
+    }
     // Full aligned 256x256 tiles, enough of them to fill the chip: the LDS-DMA kernel,
     // else the register-staged kernel below.
     if ((int64_t)(p.M / 256) * (p.N / 256) >= 128) {

@@ -66,10 +66,11 @@ struct Shape {
     static constexpr int MG = TM / 4, NG = TN / 4, BM = 16 * TM, BN = 16 * TN;
 };
 
-template <int BM, int BN, int BK>
+// B rows get the same padding when B is staged by transposed stores (B stored N x K).
+template <int BM, int BN, int BK, int BPAD>
 struct alignas(16) Smem {
     float a[2][BK][BM + APAD];
-    float b[2][BK][BN];
+    float b[2][BK][BN + BPAD];
 };
 
 // Global -> register staging of one slab. A: BM x BK as BK/4 float4 chunks per row;
@@ -97,7 +98,8 @@ __device__ __forceinline__ float4 load4_rowwise(const float *__restrict__ p, int
     return v;
 }
 
-template <class CFG, bool EDGE, bool VEC_A, bool VEC_B, bool VEC_C>
+// TA: A is stored K x M row-major (op(A) = A^T of the storage); TB: B is stored N x K.
+template <class CFG, bool TA, bool TB, bool EDGE, bool VEC_A, bool VEC_B, bool VEC_C>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, CFG::WAVES))) void f32_regtile_kernel(int M, int N, int K, float alpha,
                                                          const float *__restrict__ A, int64_t lda,
                                                          const float *__restrict__ B, int64_t ldb,
@@ -108,11 +110,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
     constexpr int MG = S::MG, NG = S::NG, BM = S::BM, BN = S::BN;
     static_assert(BK % 4 == 0 && (BM * BK) % (4 * NT) == 0 && (BN * BK) % (4 * NT) == 0,
                   "every thread stages whole float4 chunks");
-    constexpr int CH = BM * BK / (4 * NT);  // A float4 chunks per thread per slab
-    constexpr int A_CPR = BK / 4;           // A chunks per tile row
-    constexpr int B_CPR = BN / 4;           // B chunks per slab row
+    constexpr int CH = BM * BK / (4 * NT);   // A float4 chunks per thread per slab
     constexpr int CHB = BK * BN / (4 * NT);  // B float4 chunks per thread per slab
-    __shared__ Smem<BM, BN, BK> sm;
+    constexpr int BPAD = TB ? APAD : 0;
+    constexpr int BLD = BN + BPAD;           // LDS row stride of the B slab
+    __shared__ Smem<BM, BN, BK, BPAD> sm;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -123,50 +125,84 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
     grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // This thread's staging chunks: A chunk q = tid + NT*i -> (row q / A_CPR, k (q % A_CPR)*4);
-    // B chunk q -> (k q / B_CPR, col (q % B_CPR)*4).
-    int a_row[CH], a_k[CH], b_k[CHB], b_col[CHB];
+    // Staging chunks: float4 chunk q = tid + NT*i of a slab, read along the operand's
+    // contiguous dimension. A (BM x BK): stored M x K -> (m, k) = (q / (BK/4), 4 (q % (BK/4)));
+    // stored K x M -> (k, m) = (q / (BM/4), 4 (q % (BM/4))). B (BK x BN): stored K x N ->
+    // (k, n) = (q / (BN/4), 4 (q % (BN/4))); stored N x K -> (n, k) = (q / (BK/4), 4 (q % (BK/4))).
+    // a_m/a_k (b_k/b_n) name the first element of the chunk in the tile.
+    int a_m[CH], a_k[CH], b_k[CHB], b_n[CHB];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int q = tid + NT * i;
-        a_row[i] = q / A_CPR;
-        a_k[i] = (q % A_CPR) * 4;
+        if (TA) {
+            a_k[i] = q / (BM / 4);
+            a_m[i] = (q % (BM / 4)) * 4;
+        } else {
+            a_m[i] = q / (BK / 4);
+            a_k[i] = (q % (BK / 4)) * 4;
+        }
     }
 #pragma unroll
     for (int i = 0; i < CHB; ++i) {
         const int q = tid + NT * i;
-        b_k[i] = q / B_CPR;
-        b_col[i] = (q % B_CPR) * 4;
+        if (TB) {
+            b_n[i] = q / (BK / 4);
+            b_k[i] = (q % (BK / 4)) * 4;
+        } else {
+            b_k[i] = q / (BN / 4);
+            b_n[i] = (q % (BN / 4)) * 4;
+        }
     }
     const float *a_ptr[CH];
     const float *b_ptr[CHB];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) a_ptr[i] = A + (int64_t)(m0 + a_row[i]) * lda + a_k[i];
+    for (int i = 0; i < CH; ++i)
+        a_ptr[i] = TA ? A + (int64_t)a_k[i] * lda + m0 + a_m[i] : A + (int64_t)(m0 + a_m[i]) * lda + a_k[i];
 #pragma unroll
-    for (int i = 0; i < CHB; ++i) b_ptr[i] = B + (int64_t)b_k[i] * ldb + n0 + b_col[i];
+    for (int i = 0; i < CHB; ++i)
+        b_ptr[i] = TB ? B + (int64_t)(n0 + b_n[i]) * ldb + b_k[i] : B + (int64_t)b_k[i] * ldb + n0 + b_n[i];
 
     float4 ra[CH], rb[CHB];
     auto load_slab = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            ra[i] = load4_rowwise<EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_row[i]),
-                                                   K - (k0 + a_k[i]));
+            ra[i] = TA ? load4_rowwise<EDGE, VEC_A>(a_ptr[i] + (int64_t)k0 * lda, K - (k0 + a_k[i]),
+                                                    M - (m0 + a_m[i]))
+                       : load4_rowwise<EDGE, VEC_A>(a_ptr[i] + k0, M - (m0 + a_m[i]),
+                                                    K - (k0 + a_k[i]));
 #pragma unroll
         for (int i = 0; i < CHB; ++i)
-            rb[i] = load4_rowwise<EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
-                                                   K - (k0 + b_k[i]), N - (n0 + b_col[i]));
+            rb[i] = TB ? load4_rowwise<EDGE, VEC_B>(b_ptr[i] + k0, N - (n0 + b_n[i]),
+                                                    K - (k0 + b_k[i]))
+                       : load4_rowwise<EDGE, VEC_B>(b_ptr[i] + (int64_t)k0 * ldb,
+                                                    K - (k0 + b_k[i]), N - (n0 + b_n[i]));
     };
+    // LDS images: A k-major (sm.a[k][m]) and B k-major (sm.b[k][n]) whatever the storage; a
+    // chunk read along k is written as 4 scalars down a column, one read along m or n as one
+    // float4 along a row.
     auto store_slab = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            sm.a[buf][a_k[i] + 0][a_row[i]] = ra[i].x;
-            sm.a[buf][a_k[i] + 1][a_row[i]] = ra[i].y;
-            sm.a[buf][a_k[i] + 2][a_row[i]] = ra[i].z;
-            sm.a[buf][a_k[i] + 3][a_row[i]] = ra[i].w;
+            if (TA) {
+                *reinterpret_cast<float4 *>(&sm.a[buf][a_k[i]][a_m[i]]) = ra[i];
+            } else {
+                sm.a[buf][a_k[i] + 0][a_m[i]] = ra[i].x;
+                sm.a[buf][a_k[i] + 1][a_m[i]] = ra[i].y;
+                sm.a[buf][a_k[i] + 2][a_m[i]] = ra[i].z;
+                sm.a[buf][a_k[i] + 3][a_m[i]] = ra[i].w;
+            }
         }
 #pragma unroll
-        for (int i = 0; i < CHB; ++i)
-            *reinterpret_cast<float4 *>(&sm.b[buf][b_k[i]][b_col[i]]) = rb[i];
+        for (int i = 0; i < CHB; ++i) {
+            if (TB) {
+                sm.b[buf][b_k[i] + 0][b_n[i]] = rb[i].x;
+                sm.b[buf][b_k[i] + 1][b_n[i]] = rb[i].y;
+                sm.b[buf][b_k[i] + 2][b_n[i]] = rb[i].z;
+                sm.b[buf][b_k[i] + 3][b_n[i]] = rb[i].w;
+            } else {
+                *reinterpret_cast<float4 *>(&sm.b[buf][b_k[i]][b_n[i]]) = rb[i];
+            }
+        }
     };
 
     float acc[TM][TN];
@@ -196,7 +232,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
                     fa[nb][g] = *reinterpret_cast<const float4 *>(sa + (k + 1) * (BM + APAD) + g * 32);
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
-                    fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BN + g * 32);
+                    fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BLD + g * 32);
             }
             float ra_[TM], rb_[TN];
 #pragma unroll
@@ -270,9 +306,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
     }
 }
 
-template <class CFG, bool EDGE, bool VA, bool VB, bool VC>
+template <class CFG, bool TA, bool TB, bool EDGE, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tiles_n) {
-    hipLaunchKernelGGL((f32_regtile_kernel<CFG, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((f32_regtile_kernel<CFG, TA, TB, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
                        dim3(NT), 0, s, p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda,
                        (const float *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -280,8 +316,8 @@ hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tile
 
 template <class CFG, bool EDGE, bool VA, bool VB>
 hipError_t pick_c(const Problem &p, hipStream_t s, int tm, int tn, bool vc) {
-    return vc ? launch_variant<CFG, EDGE, VA, VB, true>(p, s, tm, tn)
-              : launch_variant<CFG, EDGE, VA, VB, false>(p, s, tm, tn);
+    return vc ? launch_variant<CFG, false, false, EDGE, VA, VB, true>(p, s, tm, tn)
+              : launch_variant<CFG, false, false, EDGE, VA, VB, false>(p, s, tm, tn);
 }
 template <class CFG, bool EDGE, bool VA>
 hipError_t pick_b(const Problem &p, hipStream_t s, int tm, int tn, bool vb, bool vc) {
@@ -291,12 +327,21 @@ template <class CFG, bool EDGE>
 hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, bool va, bool vb, bool vc) {
     return va ? pick_b<CFG, EDGE, true>(p, s, tm, tn, vb, vc) : pick_b<CFG, EDGE, false>(p, s, tm, tn, vb, vc);
 }
+// Transposed storage of A and/or B: the general (edge-predicated) kernel, vector loads and
+// stores only when every operand allows them.
+template <class CFG, bool TA, bool TB>
+hipError_t pick_t(const Problem &p, hipStream_t s, int tm, int tn, bool vec) {
+    return vec ? launch_variant<CFG, TA, TB, true, true, true, true>(p, s, tm, tn)
+               : launch_variant<CFG, TA, TB, true, false, false, false>(p, s, tm, tn);
+}
 
-// Kernel names for every (edge, vec A, vec B, vec C) combination of one configuration.
+// Kernel names: [edge][vec A][vec B][vec C] for row-major operands, and [layout - 1][vec]
+// for B stored N x K ("_nt", layout 1), A stored K x M ("_tn", 2) or both ("_tt", 3).
 template <class CFG>
 struct Names {
-    char text[16][64];
+    char text[22][72];
     const char *at[2][2][2][2];
+    const char *tr[3][2];
     Names() {
         typedef Shape<CFG::TM, CFG::TN> S;
         int n = 0;
@@ -309,6 +354,13 @@ struct Names {
                                  b ? "_vb" : "", c ? "_vc" : "");
                         at[e][a][b][c] = text[n++];
                     }
+        const char *lay[3] = {"_nt", "_tn", "_tt"};  // BLAS letters of op(A), op(B) storage
+        for (int l = 0; l < 3; ++l)
+            for (int v = 0; v < 2; ++v) {
+                snprintf(text[n], sizeof text[n], "f32_regtile_%dx%dx%d_%dx%d%s%s", S::BM, S::BN,
+                         CFG::BK, CFG::TM, CFG::TN, lay[l], v ? "_vec" : "");
+                tr[l][v] = text[n++];
+            }
     }
 };
 
@@ -321,6 +373,16 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name) {
     const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
     const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
     static const Names<CFG> names;  // thread-safe one-time initialisation
+    const int layout = (p.ta ? 2 : 0) + (p.tb ? 1 : 0);
+    if (layout != 0) {
+        const bool vec = va && vb && vc;
+        *name = names.tr[layout - 1][vec];
+        switch (layout) {
+            case 1: return pick_t<CFG, false, true>(p, s, tiles_m, tiles_n, vec);
+            case 2: return pick_t<CFG, true, false>(p, s, tiles_m, tiles_n, vec);
+            default: return pick_t<CFG, true, true>(p, s, tiles_m, tiles_n, vec);
+        }
+    }
     *name = names.at[edge][va][vb][vc];
     return edge ? pick_a<CFG, true>(p, s, tiles_m, tiles_n, va, vb, vc)
                 : pick_a<CFG, false>(p, s, tiles_m, tiles_n, va, vb, vc);

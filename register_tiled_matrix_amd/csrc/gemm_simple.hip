@@ -50,7 +50,9 @@ __device__ __forceinline__ float load_as_f32<_Float16>(const _Float16 *p) {  // 
     return (float)*p;
 }
 
-template <typename T, bool B_COL_MAJOR>
+// TA: A stored K x M (element (i, k) at A[k*lda + i]); TB: B stored N x K (element (k, j) at
+// B[j*ldb + k]). Otherwise row-major M x K and K x N.
+template <typename T, bool TA, bool TB>
 __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float alpha,
                                                     const T *__restrict__ A, int64_t lda,
                                                     const T *__restrict__ B, int64_t ldb,
@@ -59,43 +61,44 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
     const int col = blockIdx.x * 64 + (threadIdx.x & 63);
     const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (row >= M || col >= N) return;
-    const T *a = A + (int64_t)row * lda;
+    const T *a = TA ? A + row : A + (int64_t)row * lda;
+    const int64_t a_step = TA ? lda : 1;
+    const T *b = TB ? B + (int64_t)col * ldb : B + col;
+    const int64_t b_step = TB ? 1 : ldb;
     float acc = 0.0f;
-    if (B_COL_MAJOR) {
-        const T *b = B + (int64_t)col * ldb;
-        for (int k = 0; k < K; ++k) acc = fmaf(load_as_f32(a + k), load_as_f32(b + k), acc);
-    } else {
-        const T *b = B + col;
-        for (int k = 0; k < K; ++k)
-            acc = fmaf(load_as_f32(a + k), load_as_f32(b + (int64_t)k * ldb), acc);
-    }
+    for (int k = 0; k < K; ++k)
+        acc = fmaf(load_as_f32(a + k * a_step), load_as_f32(b + k * b_step), acc);
     float *c = C + (int64_t)row * ldc + col;
     *c = epilogue_value(acc, alpha, beta, c);
 }
 
-hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name) {
+template <typename T>
+hipError_t launch_naive(const Problem &p, hipStream_t s) {
     dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
-    hipLaunchKernelGGL((naive_kernel<float, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                       p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb, p.beta,
-                       p.C, p.ldc);
-    *name = "f32_naive";
+    const T *A = (const T *)p.A, *B = (const T *)p.B;
+    if (p.ta && p.tb)
+        hipLaunchKernelGGL((naive_kernel<T, true, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+    else if (p.ta)
+        hipLaunchKernelGGL((naive_kernel<T, true, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+    else if (p.tb)
+        hipLaunchKernelGGL((naive_kernel<T, false, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+    else
+        hipLaunchKernelGGL((naive_kernel<T, false, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
     return hipGetLastError();
 }
 
+hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name) {
+    *name = "f32_naive";
+    return launch_naive<float>(p, s);
+}
+
 hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name, bool f16) {
-    dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
-    if (f16) {
-        hipLaunchKernelGGL((naive_kernel<_Float16, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, (const _Float16 *)p.A, p.lda, (const _Float16 *)p.B, p.ldb,
-                           p.beta, p.C, p.ldc);
-        *name = "f16_naive";
-    } else {
-        hipLaunchKernelGGL((naive_kernel<uint16_t, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
-                           p.beta, p.C, p.ldc);
-        *name = "bf16_naive";
-    }
-    return hipGetLastError();
+    *name = f16 ? "f16_naive" : "bf16_naive";
+    return f16 ? launch_naive<_Float16>(p, s) : launch_naive<uint16_t>(p, s);
 }
 
 // ---------------------------------------------------------------------------------------

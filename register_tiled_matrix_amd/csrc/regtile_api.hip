@@ -11,20 +11,22 @@ namespace {
 
 thread_local const char *g_last_kernel = "none";
 
-// LAPACK-style validation. `shift` is 1 for the *_algo entry points (their first argument is
-// the algorithm), so the returned -i always names the position in the called function.
-// b_col_major selects the ldb rule (>= K instead of >= N).
+// LAPACK-style validation. `shift` counts the arguments before M (1 for the *_algo entry
+// points, 3 for the *_ex ones), so the returned -i always names the position in the called
+// function. ta / tb select the leading-dimension rules of transposed storage (A stored K x M:
+// lda >= M; B stored N x K: ldb >= K).
 int validate(int shift, int M, int N, int K, float alpha, const void *A, int lda, const void *B,
-             int ldb, float *C, int ldc, bool b_col_major) {
+             int ldb, float *C, int ldc, bool ta, bool tb) {
     if (M < 0) return -(1 + shift);
     if (N < 0) return -(2 + shift);
     if (K < 0) return -(3 + shift);
     const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
     if (reads_ab && A == nullptr) return -(5 + shift);
-    if (lda < (K > 1 ? K : 1)) return -(6 + shift);
+    const int lda_min = ta ? M : K;
+    if (lda < (lda_min > 1 ? lda_min : 1)) return -(6 + shift);
     if (reads_ab && B == nullptr) return -(7 + shift);
-    const int ldb_min = b_col_major ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
-    if (ldb < ldb_min) return -(8 + shift);
+    const int ldb_min = tb ? K : N;
+    if (ldb < (ldb_min > 1 ? ldb_min : 1)) return -(8 + shift);
     if (M > 0 && N > 0 && C == nullptr) return -(10 + shift);
     if (ldc < (N > 1 ? N : 1)) return -(11 + shift);
     return REGTILE_OK;
@@ -36,8 +38,11 @@ int finish(hipError_t err, const char *name) {
 }
 
 regtile::Problem make_problem(int M, int N, int K, float alpha, const void *A, int lda,
-                              const void *B, int ldb, float beta, float *C, int ldc) {
+                              const void *B, int ldb, float beta, float *C, int ldc, bool ta,
+                              bool tb) {
     regtile::Problem p;
+    p.ta = ta;
+    p.tb = tb;
     p.M = M;
     p.N = N;
     p.K = K;
@@ -67,12 +72,17 @@ bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
     return false;
 }
 
-int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *A, int lda,
-            const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+bool bad_flag(int f) { return f != 0 && f != 1; }
+
+int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float alpha,
+            const float *A, int lda, const float *B, int ldb, float beta, float *C, int ldc,
+            void *stream) {
     if (algo < REGTILE_F32_AUTO || algo > REGTILE_F32_REGTILE_SMALL) return -1;
-    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, false);
+    // the LDS-tiled and split-K rungs stage row-major operands only
+    if ((ta || tb) && (algo == REGTILE_F32_LDS || algo == REGTILE_F32_SPLITK)) return -1;
+    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, ta, tb);
     if (v != REGTILE_OK) return v;
-    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int status;
     if (quick_return(p, s, &status)) return status;
@@ -95,12 +105,13 @@ int run_f32(int shift, int algo, int M, int N, int K, float alpha, const float *
     return finish(err, name);
 }
 
-int run_16b(bool f16, int shift, int algo, int M, int N, int K, float alpha, const uint16_t *A,
-            int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
+int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K, float alpha,
+            const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
+            void *stream) {
     if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA_16X16) return -1;
-    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, ta, tb);
     if (v != REGTILE_OK) return v;
-    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int status;
     if (quick_return(p, s, &status)) return status;
@@ -120,33 +131,62 @@ extern "C" {
 
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream) {
-    return run_f32(0, REGTILE_F32_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_f32(0, REGTILE_F32_AUTO, false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   stream);
 }
 
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
               int ldb, float beta, float *C, int ldc, void *stream) {
-    return run_16b(false, 0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(false, 0, REGTILE_BF16_AUTO, false, true, M, N, K, alpha, A, lda, B, ldb, beta,
+                   C, ldc, stream);
 }
 
 int regtile_gemm_f32_algo(int algo, int M, int N, int K, float alpha, const float *A, int lda,
                           const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
-    return run_f32(1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_f32(1, algo, false, false, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int regtile_gemm_bf16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A,
                            int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
                            void *stream) {
-    return run_16b(false, 1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(false, 1, algo, false, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_f16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
              int ldb, float beta, float *C, int ldc, void *stream) {
-    return run_16b(true, 0, REGTILE_BF16_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(true, 0, REGTILE_BF16_AUTO, false, true, M, N, K, alpha, A, lda, B, ldb, beta,
+                   C, ldc, stream);
 }
 
 int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint16_t *A, int lda,
                           const uint16_t *B, int ldb, float beta, float *C, int ldc, void *stream) {
-    return run_16b(true, 1, algo, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_16b(true, 1, algo, false, true, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                        int ldc, void *stream) {
+    if (bad_flag(trans_a)) return -2;
+    if (bad_flag(trans_b)) return -3;
+    return run_f32(3, algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int regtile_gemm_bf16_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                         const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta,
+                         float *C, int ldc, void *stream) {
+    if (bad_flag(trans_a)) return -2;
+    if (bad_flag(trans_b)) return -3;
+    return run_16b(false, 3, algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   stream);
+}
+
+int regtile_gemm_f16_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta,
+                        float *C, int ldc, void *stream) {
+    if (bad_flag(trans_a)) return -2;
+    if (bad_flag(trans_b)) return -3;
+    return run_16b(true, 3, algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                   stream);
 }
 
 const char *regtile_last_kernel(void) { return g_last_kernel; }

@@ -18,6 +18,9 @@ struct Problem {
     int64_t ldb;
     float *C;
     int64_t ldc;
+    // Storage of the operands (row-major throughout): ta -> A is stored K x M (op(A) is its
+    // transpose), tb -> B is stored N x K. The 16-bit entry points' native B is tb.
+    bool ta = false, tb = false;
 };
 
 // A launch reports the kernel it chose through `name` (static storage).

@@ -77,7 +77,7 @@ def build_variant(name: str) -> dict:
 def variant_resources(name: str) -> dict:
     """VGPRs, scratch, occupancy and LDS of the variant's fully aligned interior kernel."""
     res = _build.resource_usage(os.path.join(VARIANT_DIR, name))
-    key = [k for k in res if "f32_regtile_kernel" in k and "SquareCfg" in k and "ELb0ELb1ELb1ELb1EE" in k]
+    key = [k for k in res if "SquareCfgELb0ELb0ELb0ELb1ELb1ELb1EE" in k]
     r = res[key[0]] if key else {}
     return {"vgprs": r.get("VGPRs"), "agprs": r.get("AGPRs"), "scratch_bytes": r.get("ScratchSize [bytes/lane]"),
             "waves_per_simd": r.get("Occupancy [waves/SIMD]"), "lds_bytes": r.get("LDS Size [bytes/block]")}

@@ -131,3 +131,33 @@ def test_kernels_have_no_scratch_and_stated_occupancy():
     small = [r for n, r in res.items() if "f32_regtile_kernel" in n and "SmallCfg" in n]
     assert small and all(r["Occupancy [waves/SIMD]"] >= 4 for r in small)
     assert all(r["VGPRs"] + r.get("AGPRs", 0) <= 512 // r["Occupancy [waves/SIMD]"] for r in f32)
+
+
+@pytest.mark.parametrize("fn", ["regtile_gemm_f32_ex", "regtile_gemm_bf16_ex", "regtile_gemm_f16_ex"])
+def test_layout_entry_points_validate_flags_and_leading_dimensions(lib, fn):
+    f = getattr(rt, fn)
+    # algo, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream
+    base = dict(algo=0, ta=0, tb=0, M=4, N=5, K=6, lda=6, ldb=5, ldc=5)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return f(a["algo"], a["ta"], a["tb"], a["M"], a["N"], a["K"], 1.0, DUMMY, a["lda"], DUMMY,
+                 a["ldb"], 0.0, DUMMY, a["ldc"], 0)
+
+    assert call(ta=2) == -2 and call(tb=-1) == -3
+    assert call(M=-1) == -4 and call(N=-1) == -5 and call(K=-1) == -6
+    assert call(lda=5) == -9            # A stored M x K: lda >= K
+    assert call(ta=1, lda=3) == -9      # A stored K x M: lda >= M
+    assert call(ldb=4) == -11           # B stored K x N: ldb >= N
+    assert call(tb=1, ldb=5) == -11     # B stored N x K: ldb >= K
+    assert call(ldc=4) == -14
+    assert call(algo=9) == -1
+    assert call(M=0) == 0 and rt.last_kernel() == "quick-return"
+
+
+def test_row_major_only_rungs_reject_transposed_layouts(lib):
+    a = (4, 4, 4, 1.0, DUMMY, 4, DUMMY, 4, 0.0, DUMMY, 4, 0)
+    for algo in (rt.ALGO_F32_LDS, rt.ALGO_F32_SPLITK):
+        assert rt.regtile_gemm_f32_ex(algo, 1, 0, *a) == -1
+        assert rt.regtile_gemm_f32_ex(algo, 0, 1, *a) == -1
+

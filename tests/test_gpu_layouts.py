@@ -1,0 +1,134 @@
+"""GPU parity of the operand layouts (BLAS transpose flags over row-major storage).
+
+Every problem is drawn in the oracle's layout (row-major A; row-major B for fp32, column-major
+B for bf16/fp16); the device copies are then stored the other way where a test asks for it,
+and passed as transposed views. The oracle sees the same values either way.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+import register_tiled_matrix_amd as rt
+from gpu_util import announce, assert_parity_full, assert_parity_sampled, sample_positions
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+LAYOUTS = [(0, 0), (0, 1), (1, 0), (1, 1)]  # (trans_a, trans_b): A stored K x M, B stored N x K
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rt.load()
+    yield
+
+
+def _as(arr, torch_dtype):
+    arr = np.ascontiguousarray(arr)
+    if torch_dtype == torch.float32:
+        return torch.from_numpy(arr).cuda()
+    return torch.from_numpy(arr.view(np.int16)).cuda().view(torch_dtype)
+
+
+def _operands(inp, ta, tb):
+    """Device A (M x K) and B (K x N) views with the requested storage; C (row-major)."""
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[inp.dtype]
+    A = _as(inp.A.T, tdt).t() if ta else _as(inp.A, tdt)
+    # inp.B is K x N row-major for fp32, N x K (column-major K x N) for the 16-bit types
+    if inp.b_col_major:
+        B = _as(inp.B, tdt).t() if tb else _as(inp.B.T, tdt)
+    else:
+        B = _as(inp.B.T, tdt).t() if tb else _as(inp.B, tdt)
+    C = (torch.from_numpy(np.ascontiguousarray(inp.C)).cuda() if inp.C is not None
+         else torch.empty((inp.M, inp.N), dtype=torch.float32, device="cuda"))
+    return A, B, C
+
+
+def _run(inp, ta, tb, algo=0):
+    A, B, C = _operands(inp, ta, tb)
+    assert rt._layout(A, "A")[0] == ta and rt._layout(B, "B")[0] == tb
+    fn = {"f32": rt.gemm_f32, "bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[inp.dtype]
+    fn(A, B, C, alpha=inp.alpha, beta=inp.beta, algo=algo)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), rt.last_kernel()
+
+
+F32_ALGOS = [rt.ALGO_F32_NAIVE, rt.ALGO_F32_REGTILE, rt.ALGO_F32_REGTILE_SMALL, rt.ALGO_F32_AUTO]
+
+
+@pytest.mark.parametrize("algo", F32_ALGOS)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(1000, 1500, 777), (256, 512, 64), (33, 17, 129)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_f32_layouts_full(shape, ta, tb, algo):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=1.5, beta=-0.5, seed=M + 3 * N + K)
+    announce(f"f32 layout {ta}{tb} {shape} algo={algo}")
+    got, name = _run(inp, ta, tb, algo)
+    assert_parity_full(inp, got, f"f32 layout ({ta},{tb}) {shape} ({name})")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_f32_layouts_agree_bitwise_with_the_naive_rung(ta, tb):
+    # the register-tiled kernels keep fmaf over k in natural order whatever the storage
+    inp = gi.make_inputs(300, 260, 333, dtype="f32", dist="normal", seed=41)
+    announce(f"f32 layout bitwise {ta}{tb}")
+    ref, _ = _run(inp, ta, tb, rt.ALGO_F32_NAIVE)
+    for algo in (rt.ALGO_F32_REGTILE, rt.ALGO_F32_REGTILE_SMALL):
+        got, name = _run(inp, ta, tb, algo)
+        assert np.array_equal(got, ref), name
+    nn, _ = _run(inp, 0, 0, rt.ALGO_F32_NAIVE)
+    assert np.array_equal(nn, ref)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_f32_layouts_4096_sampled(ta, tb):
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_4096"])
+    announce(f"f32_4096 layout {ta}{tb}")
+    got, name = _run(inp, ta, tb)
+    assert "regtile" in name
+    assert_parity_sampled(inp, got, f"f32_4096 layout ({ta},{tb}) ({name})")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("algo", [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_AUTO])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(300, 257, 777), (512, 256, 128), (2048, 4096, 192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_16bit_layouts_full(shape, ta, tb, algo, dtype):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.25, beta=0.5, seed=M + N + 7 * K)
+    announce(f"{dtype} layout {ta}{tb} {shape} algo={algo}")
+    got, name = _run(inp, ta, tb, algo)
+    assert name.startswith(dtype + "_")
+    if (ta, tb) == (0, 1) and shape == (2048, 4096, 192) and algo != rt.ALGO_BF16_NAIVE:
+        assert "_dma_" in name
+    assert_parity_full(inp, got, f"{dtype} layout ({ta},{tb}) {shape} ({name})")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_16bit_layouts_integer_bitwise(ta, tb):
+    rng = np.random.Generator(np.random.PCG64(90 + 2 * ta + tb))
+    M, N, K = 384, 256, 2048
+    A = gi.f32_to_bf16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_bf16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, A, Bt, None)
+    announce(f"bf16 layout integer bitwise {ta}{tb}")
+    got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA)
+    I, J = sample_positions(M, N, n_random=20000, seed=6)
+    ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref), name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (1, 1)])
+def test_16bit_layouts_8192_sampled(ta, tb, dtype):
+    inp = gi.workload_inputs(gi.WORKLOADS[f"{dtype}_8192"])
+    announce(f"{dtype}_8192 layout {ta}{tb}")
+    got, name = _run(inp, ta, tb)
+    assert_parity_sampled(inp, got, f"{dtype}_8192 layout ({ta},{tb}) ({name})", n_random=10000)
