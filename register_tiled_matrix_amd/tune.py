@@ -11,6 +11,7 @@ ladder (algorithm 2).
     python -m register_tiled_matrix_amd.tune build            # CPU: compile every variant
     python -m register_tiled_matrix_amd.tune run  > sweep.jsonl   # GPU: time every variant
     python -m register_tiled_matrix_amd.tune report sweep.jsonl  # markdown summary
+    python -m register_tiled_matrix_amd.tune ladder > ladder.jsonl   # GPU: every rung, every config
 
 Correctness of each variant is checked bitwise against the naive rung of the default library:
 every fp32 rung accumulates each output with fmaf over k in natural order, so any micro-tile
@@ -174,8 +175,104 @@ def cmd_run(args) -> int:
     return 0
 
 
+# every rung of the ladder, per element type: (label, algorithm value, kernel-name prefix in
+# the compiler's resource report)
+F32_RUNGS = [("naive", 1, "naive_kernelIfLb0ELb0E"), ("lds_32x32", 2, "f32_lds_kernel"),
+             ("regtile_8x16", 3, "SquareCfgELb0ELb0E"), ("regtile_small_4x4", 5, "SmallCfgELb0ELb0E"),
+             ("splitk_8x8", 4, "f32_splitk_kernel")]
+R16_RUNGS = [("naive", 1, "naive_kernelI{T}Lb0ELb1E"), ("mfma_32x32x16", 2, "ELi32ELi1ELi1ELb{F}E"),
+             ("mfma_16x16x32", 3, "ELi16ELi1ELi0ELb{F}E")]
+
+
+def _kernel_resources(prefix: str) -> dict:
+    """Largest VGPR count, occupancy and LDS among the in-tree kernels whose mangled name
+    contains `prefix` (all vector/edge variants of one rung)."""
+    res = _build.resource_usage()
+    hits = [r for k, r in res.items() if prefix in k]
+    if not hits:
+        return {}
+    r = max(hits, key=lambda r: r.get("VGPRs", 0) + r.get("AGPRs", 0))
+    return {"vgprs": r.get("VGPRs"), "agprs": r.get("AGPRs"), "scratch_bytes": r.get("ScratchSize [bytes/lane]"),
+            "waves_per_simd": r.get("Occupancy [waves/SIMD]"), "lds_bytes": r.get("LDS Size [bytes/block]")}
+
+
+def cmd_ladder(args) -> int:
+    """Every rung on every workload: TFLOP/s plus the compiler's VGPRs / occupancy / LDS."""
+    import numpy as np
+    import torch
+
+    import gemm_inputs as gi
+    import register_tiled_matrix_amd as rt
+
+    if not torch.cuda.is_available():
+        print("tune ladder needs a GPU", file=sys.stderr)
+        return 2
+    rt.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    for wl in args.workloads.split(","):
+        w = gi.WORKLOADS[wl]
+        inp = gi.workload_inputs(w)
+        if w.dtype == "f32":
+            A = torch.from_numpy(inp.A).cuda()
+            B = torch.from_numpy(inp.B).cuda()
+            rungs, fn = F32_RUNGS, rt.regtile_gemm_f32_algo
+        else:
+            A = torch.from_numpy(inp.A.view(np.int16)).cuda()
+            B = torch.from_numpy(inp.B.view(np.int16)).cuda()
+            T, F = ("DF16_", "1") if w.dtype == "f16" else ("t", "0")
+            rungs = [(l, a, p.format(T=T, F=F)) for l, a, p in R16_RUNGS]
+            fn = rt.regtile_gemm_bf16_algo if w.dtype == "bf16" else rt.regtile_gemm_f16_algo
+        C = (torch.from_numpy(inp.C).cuda() if inp.C is not None
+             else torch.empty((w.M, w.N), dtype=torch.float32, device="cuda"))
+        for label, algo, prefix in rungs:
+            call = (algo, w.M, w.N, w.K, w.alpha, A.data_ptr(), inp.lda, B.data_ptr(), inp.ldb, w.beta,
+                    C.data_ptr(), w.N, stream)
+            slow = label in ("naive", "lds_32x32") and w.flop > 1e11
+            steps = 3 if slow else args.steps
+            for _ in range(1 if slow else args.warmup):
+                assert fn(*call) == 0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record()
+                fn(*call)
+                b.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            print(json.dumps({"workload": wl, "rung": label, "kernel": rt.last_kernel(),
+                              "ms_median": round(ms, 4), "tflops": round(w.flop / (ms * 1e-3) / 1e12, 3),
+                              **_kernel_resources(prefix)}), flush=True)
+        del A, B, C
+    return 0
+
+
+def _ladder_report(rows) -> str:
+    out = ["# Kernel ladder on every configuration", "",
+           "Command (repository root, one MI355X):", "", "```",
+           "python -m register_tiled_matrix_amd.tune ladder > gpurun_out/ladder.jsonl",
+           "python -m register_tiled_matrix_amd.tune report gpurun_out/ladder.jsonl", "```", "",
+           "Median of 10 timed launches (3 for the naive and LDS rungs on the large problems), "
+           "operands resident on the device. VGPRs / occupancy / LDS: the compiler's resource "
+           "report for the rung's kernels (largest variant).", "",
+           "| workload | rung | kernel | median ms | TFLOP/s | VGPRs | AGPRs | waves/SIMD | LDS bytes |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['workload']} | {r['rung']} | `{r['kernel']}` | {r['ms_median']} | {r['tflops']} | "
+                   f"{r.get('vgprs', '-')} | {r.get('agprs', '-')} | {r.get('waves_per_simd', '-')} | "
+                   f"{r.get('lds_bytes', '-')} |")
+    return "\n".join(out) + "\n"
+
+
 def cmd_report(args) -> int:
     rows = [json.loads(l) for l in open(args.jsonl) if l.strip().startswith("{")]
+    if rows and "rung" in rows[0]:
+        text = _ladder_report(rows)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        else:
+            sys.stdout.write(text)
+        return 0
     out = ["# fp32 micro-tile / occupancy sweep", "",
            "Commands (repository root; the variants are built on the CPU first):", "", "```",
            "python -m register_tiled_matrix_amd.tune build",
@@ -222,6 +319,10 @@ def main(argv=None) -> int:
     r.add_argument("--no-rungs", action="store_true",
                    help="time only the variants (for counter runs, where the default library's "
                         "kernels would share the variants' names)")
+    lad = sub.add_parser("ladder")
+    lad.add_argument("--workloads", default="f32_256,f32_4096,f32_ragged,f32_tall,bf16_8192,f16_8192")
+    lad.add_argument("--steps", type=int, default=10)
+    lad.add_argument("--warmup", type=int, default=3)
     rep = sub.add_parser("report")
     rep.add_argument("jsonl")
     rep.add_argument("--out", default="")
@@ -230,7 +331,7 @@ def main(argv=None) -> int:
     if root not in sys.path:
         sys.path.insert(0, root)
     t0 = time.time()
-    rc = {"build": cmd_build, "run": cmd_run, "report": cmd_report}[args.cmd](args)
+    rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report}[args.cmd](args)
     print(f"# {args.cmd} done in {time.time() - t0:.1f} s", file=sys.stderr)
     return rc
 
