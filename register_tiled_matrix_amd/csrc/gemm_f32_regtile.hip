@@ -233,7 +233,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * BLD + g * 32);
+                // One wait for all of step k's fragments (only step k+1's reads may still be
+                // in flight; no other LDS access is outstanding inside a slab). Left to
+                // itself the compiler waits fragment by fragment, and at two waves per SIMD
+                // every extra instruction a wave issues is a lost FMA issue slot.
+                wait_lgkmcnt<MG + NG>();
+            } else {
+                wait_lgkmcnt<0>();
             }
+            __builtin_amdgcn_sched_barrier(0);  // no FMA is hoisted above the wait
             float ra_[TM], rb_[TN];
 #pragma unroll
             for (int g = 0; g < MG; ++g) {

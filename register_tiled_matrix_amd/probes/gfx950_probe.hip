@@ -1,0 +1,253 @@
+// gfx950_probe.hip -- small measurements of the gfx950 facts the kernels are designed around.
+// Not part of the library: `python -m register_tiled_matrix_amd.tune probe` builds this file
+// with the library's compiler flags and runs it.
+//
+//   valu  FP32 FMA issue rate (non-packed v_fmac_f32, VGPR operands) at 1, 2 and 4 waves per
+//         SIMD, and the effect of VGPR banks (register number mod 4): accumulator and src0 in
+//         one bank, accumulator and src1 in one bank, neither, all three operands in even
+//         banks. Each wave also reports its own
+//         shader-clock cycles (s_memtime) against the constant-rate wall clock, which gives
+//         the clock the SIMD ran at and the cycles one wave64 FMA took per SIMD.
+//   mfma  v_mfma_f32_32x32x16_bf16 with 8 independent accumulators per wave: the attainable
+//         matrix rate on this machine.
+//   lds   one kernel per LDS address pattern (16 bytes per lane); run under
+//         `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES` for the
+//         cycles and conflict cycles per instruction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#define CHECK(x)                                                                          \
+    do {                                                                                  \
+        hipError_t e_ = (x);                                                              \
+        if (e_ != hipSuccess) {                                                           \
+            printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);          \
+            return 1;                                                                     \
+        }                                                                                 \
+    } while (0)
+
+// ---- valu ---------------------------------------------------------------------------------
+// 16 FMAs into accumulators v32, v36, ..., v92 (all in bank 0) with the given sources.
+#define FMA1(D, S0, S1) "v_fmac_f32 " D ", " S0 ", " S1 "\n"
+#define FMA16(S0, S1)                                                                      \
+    FMA1("v32", S0, S1) FMA1("v36", S0, S1) FMA1("v40", S0, S1) FMA1("v44", S0, S1)       \
+    FMA1("v48", S0, S1) FMA1("v52", S0, S1) FMA1("v56", S0, S1) FMA1("v60", S0, S1)       \
+    FMA1("v64", S0, S1) FMA1("v68", S0, S1) FMA1("v72", S0, S1) FMA1("v76", S0, S1)       \
+    FMA1("v80", S0, S1) FMA1("v84", S0, S1) FMA1("v88", S0, S1) FMA1("v92", S0, S1)
+#define VALU_CLOBBERS                                                                      \
+    "v1", "v2", "v4", "v32", "v36", "v40", "v44", "v48", "v52", "v56", "v60", "v64", "v68", \
+        "v72", "v76", "v80", "v84", "v88", "v92"
+#define VALU_INIT                                                                          \
+    "v_mov_b32 v1, 1.0\nv_mov_b32 v2, 1.0\nv_mov_b32 v4, 1.0\n"                            \
+    "v_mov_b32 v32, 0\nv_mov_b32 v36, 0\nv_mov_b32 v40, 0\nv_mov_b32 v44, 0\n"             \
+    "v_mov_b32 v48, 0\nv_mov_b32 v52, 0\nv_mov_b32 v56, 0\nv_mov_b32 v60, 0\n"             \
+    "v_mov_b32 v64, 0\nv_mov_b32 v68, 0\nv_mov_b32 v72, 0\nv_mov_b32 v76, 0\n"             \
+    "v_mov_b32 v80, 0\nv_mov_b32 v84, 0\nv_mov_b32 v88, 0\nv_mov_b32 v92, 0\n"
+
+constexpr int kValuIters = 2000, kValuFmaPerIter = 64;
+
+// P = 0: src0 v1, src1 v2 (no operand shares the accumulators' bank)
+// P = 1: src0 v4, src1 v1 (accumulator and src0 in bank 0)
+// P = 2: src0 v1, src1 v4 (accumulator and src1 in bank 0)
+// P = 3: src0 v4, src1 v2 (accumulator, src0 and src1 all in even banks)
+template <int P>
+__global__ __launch_bounds__(256) void valu_kernel(uint64_t *out, int iters) {
+    asm volatile(VALU_INIT ::: VALU_CLOBBERS);
+    const uint64_t t0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+        if (P == 0) asm volatile(FMA16("v1", "v2") FMA16("v1", "v2") FMA16("v1", "v2") FMA16("v1", "v2") ::: VALU_CLOBBERS);
+        if (P == 1) asm volatile(FMA16("v4", "v1") FMA16("v4", "v1") FMA16("v4", "v1") FMA16("v4", "v1") ::: VALU_CLOBBERS);
+        if (P == 2) asm volatile(FMA16("v1", "v4") FMA16("v1", "v4") FMA16("v1", "v4") FMA16("v1", "v4") ::: VALU_CLOBBERS);
+        if (P == 3) asm volatile(FMA16("v4", "v2") FMA16("v4", "v2") FMA16("v4", "v2") FMA16("v4", "v2") ::: VALU_CLOBBERS);
+    }
+    const uint64_t t1 = clock64(), w1 = wall_clock64();
+    if ((threadIdx.x & 63) == 0) {
+        const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+        out[2 * w] = t1 - t0;
+        out[2 * w + 1] = w1 - w0;
+    }
+}
+
+int run_valu() {
+    const int max_blocks = 256 * 4;
+    uint64_t *d;
+    CHECK(hipMalloc(&d, sizeof(uint64_t) * 2 * 4 * max_blocks));
+    static uint64_t h[2 * 4 * 256 * 4];
+    int wall_khz = 0;
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    typedef void (*kfn)(uint64_t *, int);
+    const struct { const char *name; kfn fn; } pats[] = {
+        {"no shared bank", valu_kernel<0>}, {"acc + src0 bank", valu_kernel<1>}, {"acc + src1 bank", valu_kernel<2>},
+        {"all three in even banks", valu_kernel<3>}};
+    printf("| operands | waves/SIMD | SIMD cycles per wave64 FMA | clock GHz | TFLOP/s |\n|---|---|---|---|---|\n");
+    for (int per_simd = 1; per_simd <= 4; per_simd *= 2)
+        for (const auto &p : pats) {
+            const int blocks = 256 * per_simd;  // 256 threads = one wave per SIMD of a CU
+            hipLaunchKernelGGL(p.fn, dim3(blocks), dim3(256), 0, 0, d, kValuIters);
+            CHECK(hipGetLastError());
+            CHECK(hipEventRecord(e0));
+            hipLaunchKernelGGL(p.fn, dim3(blocks), dim3(256), 0, 0, d, kValuIters);
+            CHECK(hipEventRecord(e1));
+            CHECK(hipEventSynchronize(e1));
+            float ms;
+            CHECK(hipEventElapsedTime(&ms, e0, e1));
+            CHECK(hipMemcpy(h, d, sizeof(uint64_t) * 2 * 4 * blocks, hipMemcpyDeviceToHost));
+            double cyc = 0, wall = 0;
+            for (int i = 0; i < 4 * blocks; ++i) {
+                cyc += (double)h[2 * i];
+                wall += (double)h[2 * i + 1];
+            }
+            cyc /= 4 * blocks;
+            wall /= 4 * blocks;
+            const double fmas = (double)kValuIters * kValuFmaPerIter;
+            const double ghz = cyc / (wall / (wall_khz * 1e3)) / 1e9;
+            const double tflops = 2.0 * fmas * 64 * 4 * blocks / (ms * 1e-3) / 1e12;
+            printf("| %s | %d | %.2f | %.2f | %.1f |\n", p.name, per_simd, cyc / fmas / per_simd, ghz, tflops);
+        }
+    return 0;
+}
+
+// ---- mfma ---------------------------------------------------------------------------------
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+__global__ __launch_bounds__(256) void mfma_kernel(float *out, uint64_t *clk, int iters) {
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (short)(0x3f80 + (threadIdx.x & 7));  // bf16 values near 1
+        b[i] = (short)(0x3c00 + i);                  // small bf16 values
+    }
+    f32x16 acc[8];
+    for (int j = 0; j < 8; ++j)
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+    const uint64_t t0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    const uint64_t t1 = clock64(), w1 = wall_clock64();
+    if ((threadIdx.x & 63) == 0) {
+        const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = w1 - w0;
+    }
+    float s = 0.0f;
+    for (int j = 0; j < 8; ++j)
+        for (int v = 0; v < 16; ++v) s += acc[j][v];
+    out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+int run_mfma() {
+    const int blocks = 256, iters = 4000;
+    float *d;
+    uint64_t *clk;
+    CHECK(hipMalloc(&d, sizeof(float) * blocks * 256));
+    CHECK(hipMalloc(&clk, sizeof(uint64_t) * 2 * 4 * blocks));
+    static uint64_t h[2 * 4 * 256];
+    int wall_khz = 0;
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, 0, d, clk, iters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, 0, d, clk, iters);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    CHECK(hipMemcpy(h, clk, sizeof(uint64_t) * 2 * 4 * blocks, hipMemcpyDeviceToHost));
+    double cyc = 0, wall = 0;
+    for (int i = 0; i < 4 * blocks; ++i) {
+        cyc += (double)h[2 * i];
+        wall += (double)h[2 * i + 1];
+    }
+    cyc /= 4 * blocks;
+    wall /= 4 * blocks;
+    const double mfmas = 8.0 * iters;
+    const double flop = 2.0 * 32 * 32 * 16 * mfmas * 4 * blocks;
+    printf("| v_mfma_f32_32x32x16_bf16, one wave per SIMD, 8 accumulators | %.2f cycles per MFMA | "
+           "%.2f GHz | %.0f TFLOP/s |\n",
+           cyc / mfmas, cyc / (wall / (wall_khz * 1e3)) / 1e9, flop / (ms * 1e-3) / 1e12);
+    return 0;
+}
+
+// ---- lds ----------------------------------------------------------------------------------
+__device__ __forceinline__ int key_row7(int row, int c) { return row * 128 + ((c ^ (row & 7)) * 16); }
+__device__ __forceinline__ int key_row7_row8(int row, int c) {
+    return row * 128 + ((c ^ ((row & 7) ^ ((row >> 3) & 1))) * 16);
+}
+
+template <int P>
+__device__ __forceinline__ int lds_pattern(int lane) {
+    switch (P) {
+        case 0: return lane * 16;                                 // 1 KiB contiguous
+        case 1: return key_row7(lane & 31, 2 + (lane >> 5));      // 32 rows of 128 B, chunk ^ (row & 7)
+        case 2: return key_row7_row8(lane & 31, 2 + (lane >> 5)); // chunk ^ ((row & 7) ^ (row >> 3 & 1))
+        case 3: return (lane & 31) * 128 + (lane >> 5) * 16;      // 32 rows of 128 B, no swizzle
+        case 4: return (lane >> 3) * 16;                          // 8 distinct addresses, rest broadcast
+        case 5: return (lane & 1) * 256 + (lane >> 1) * 16;       // lane pairs 256 B apart
+        default: return key_row7_row8(lane >> 3, lane & 7);       // 8 lanes per 128-byte row
+    }
+}
+
+template <int P, bool WRITE>
+__global__ __launch_bounds__(256) void lds_kernel(uint32_t *out, int iters) {
+    __shared__ uint4 lds[4096];  // 64 KiB, 16 KiB per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 4096; i += 256) lds[i] = make_uint4(i, i + 1, i + 2, i + 3);
+    __syncthreads();
+    int off = lds_pattern<P>(lane) + wave * 16384;  // every pattern stays below 16 KiB
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(off));
+        if (WRITE) {
+            *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(lds) + off) = make_uint4(it, it, it, it);
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(lds) + off);
+            acc.x ^= v.x;
+            acc.y ^= v.y;
+            acc.z ^= v.z;
+            acc.w ^= v.w;
+        }
+    }
+    __syncthreads();
+    out[blockIdx.x * 256 + threadIdx.x] = acc.x + acc.y + acc.z + acc.w + lds[threadIdx.x].x;
+}
+
+template <int P, bool WRITE>
+int lds_one(uint32_t *d, const char *what) {
+    hipLaunchKernelGGL((lds_kernel<P, WRITE>), dim3(256), dim3(256), 0, 0, d, 1024);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    printf("lds pattern %d (%s) done\n", P, what);
+    return 0;
+}
+
+int run_lds() {
+    uint32_t *d;
+    CHECK(hipMalloc(&d, sizeof(uint32_t) * 256 * 256));
+    int rc = 0;
+    rc |= lds_one<0, false>(d, "ds_read_b128, 1 KiB contiguous");
+    rc |= lds_one<1, false>(d, "ds_read_b128, 128-byte rows, chunk ^ (row & 7)");
+    rc |= lds_one<2, false>(d, "ds_read_b128, 128-byte rows, chunk ^ ((row & 7) ^ (row >> 3 & 1))");
+    rc |= lds_one<3, false>(d, "ds_read_b128, 128-byte rows, no swizzle");
+    rc |= lds_one<4, false>(d, "ds_read_b128, 8 distinct addresses");
+    rc |= lds_one<5, false>(d, "ds_read_b128, lane pairs 256 B apart");
+    rc |= lds_one<0, true>(d, "ds_write_b128, 1 KiB contiguous");
+    rc |= lds_one<6, true>(d, "ds_write_b128, 8 lanes per 128-byte row");
+    return rc;
+}
+
+int main(int argc, char **argv) {
+    const char *what = argc > 1 ? argv[1] : "all";
+    int rc = 0;
+    if (!strcmp(what, "valu") || !strcmp(what, "all")) rc |= run_valu();
+    if (!strcmp(what, "mfma") || !strcmp(what, "all")) rc |= run_mfma();
+    if (!strcmp(what, "lds")) rc |= run_lds();
+    return rc;
+}

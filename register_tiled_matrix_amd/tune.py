@@ -12,6 +12,8 @@ ladder (algorithm 2).
     python -m register_tiled_matrix_amd.tune run  > sweep.jsonl   # GPU: time every variant
     python -m register_tiled_matrix_amd.tune report sweep.jsonl  # markdown summary
     python -m register_tiled_matrix_amd.tune ladder > ladder.jsonl   # GPU: every rung, every config
+    python -m register_tiled_matrix_amd.tune probe --build none   # CPU: build the gfx950 probes
+    python -m register_tiled_matrix_amd.tune probe valu           # GPU: FMA issue rate, VGPR banks
 
 Correctness of each variant is checked bitwise against the naive rung of the default library:
 every fp32 rung accumulates each output with fmaf over k in natural order, so any micro-tile
@@ -306,6 +308,31 @@ def cmd_report(args) -> int:
     return 0
 
 
+PROBE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "gfx950_probe.hip")
+PROBE_BIN = os.path.join(_build.BUILD_DIR, "probes", "gfx950_probe")
+
+
+def build_probe() -> None:
+    """Compile the gfx950 probe program with the library's flags (raises on failure)."""
+    os.makedirs(os.path.dirname(PROBE_BIN), exist_ok=True)
+    flags = [f for f in _build.COMMON_FLAGS if f != "-fPIC"]
+    res = subprocess.run([_build._hipcc(), *flags, PROBE_SRC, "-o", PROBE_BIN],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{res.stderr}")
+    print(f"# built {PROBE_BIN}", file=sys.stderr)
+
+
+def cmd_probe(args) -> int:
+    """Build (on the CPU, with the library's flags) and/or run the gfx950 probe program."""
+    if args.build or not os.path.exists(PROBE_BIN):
+        build_probe()
+    if args.what == "none":
+        return 0
+    sys.stdout.flush()
+    return subprocess.run([PROBE_BIN, args.what]).returncode
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -323,6 +350,10 @@ def main(argv=None) -> int:
     lad.add_argument("--workloads", default="f32_256,f32_4096,f32_ragged,f32_tall,bf16_8192,f16_8192")
     lad.add_argument("--steps", type=int, default=10)
     lad.add_argument("--warmup", type=int, default=3)
+    pr = sub.add_parser("probe", help="gfx950 facts: FP32 FMA issue rate and VGPR banks, "
+                                       "MFMA rate, LDS access patterns")
+    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "mfma", "lds", "none"])
+    pr.add_argument("--build", action="store_true", help="recompile the probe program first")
     rep = sub.add_parser("report")
     rep.add_argument("jsonl")
     rep.add_argument("--out", default="")
@@ -331,7 +362,8 @@ def main(argv=None) -> int:
     if root not in sys.path:
         sys.path.insert(0, root)
     t0 = time.time()
-    rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report}[args.cmd](args)
+    rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report,
+          "probe": cmd_probe}[args.cmd](args)
     print(f"# {args.cmd} done in {time.time() - t0:.1f} s", file=sys.stderr)
     return rc
 
