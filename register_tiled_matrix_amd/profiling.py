@@ -1,0 +1,244 @@
+"""rocprofv3 evidence for the benchmark's kernels: collect on the GPU, summarise on the CPU.
+
+    python -m register_tiled_matrix_amd.profiling collect gpurun_out/prof    # GPU machine
+    python -m register_tiled_matrix_amd.profiling summarize gpurun_out/prof  # writes profiles/
+
+`collect` runs each profiler pass as a child process (rocprofv3 starts the program itself;
+this process never touches the GPU), one pass at a time, each under its own time limit, and
+stops at the first pass that fails. The passes:
+
+  trace      --kernel-trace --stats over `bench.py --no-cpu` (per-kernel durations);
+  pmc_*      FETCH_SIZE, then WRITE_SIZE, one counter per run, over `bench.py --only <workload>`
+             for the fp32 4096^3, bf16 8192^3 and fp32 16384x128x4096 kernels and for a plain
+             1 GiB device copy (the calibration: bytes moved / counter bytes);
+  sq_*       LDS, VALU and MFMA instruction and cycle counters per kernel.
+
+`summarize` turns the CSV files into the short tables under profiles/ and writes
+profiles/pmc_traffic.json, from which bench.py reports `roofline.traffic` (HBM bytes per
+launch), stamped with a digest of the kernel's sources so a changed kernel reports null.
+"""
+from __future__ import annotations
+
+import csv
+import collections
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "register_tiled_matrix_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_MFMA "
+               "SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES")
+COPY_BYTES = 1 << 30
+
+# workload -> (kernel label as regtile_last_kernel() names it, substring of the kernel's symbol,
+#              sources whose digest stamps the record, algorithmic HBM bytes per launch)
+KERNELS = {
+    "f32_4096": ("f32_regtile_128x256x16_8x16_va_vb_vc", "f32_regtile_kernel<regtile::(anonymous namespace)::SquareCfg",
+                 ["gemm_f32_regtile.hip", "regtile_internal.h"], 3 * 4096 * 4096 * 4),
+    "bf16_8192": ("bf16_mfma32x32x16_dma_256x256x64_w2x2", "bf16_mfma_dma_kernel<256, 256, 64, 2, 2, 32",
+                  ["gemm_bf16_mfma_dma.hip", "mfma_common.h", "regtile_internal.h"],
+                  2 * 8192 * 8192 * 2 + 8192 * 8192 * 4),
+    "f32_tall": ("f32_regtile_64x64x32_4x4_va_vb_vc", "f32_regtile_kernel<regtile::(anonymous namespace)::SmallCfg",
+                 ["gemm_f32_regtile.hip", "regtile_internal.h"], (16384 * 4096 + 4096 * 128 + 16384 * 128) * 4),
+}
+PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "copy"]
+SQ_WORKLOADS = ["f32_4096", "bf16_8192"]
+
+
+def _bench_cmd(*extra):
+    return ["python3", os.path.join(ROOT, "bench.py"), *extra]
+
+
+def passes(out):
+    """(name, rocprofv3 argv, seconds allowed) for every pass, in order."""
+    p = [("trace", ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out, "trace"), "-o", "trace",
+                    "--output-format", "csv", "--", *_bench_cmd("--no-cpu", "--steps", "20", "--warmup", "5")], 420)]
+    for w in PMC_WORKLOADS:
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            p.append((f"pmc_{c}_{w}", ["rocprofv3", "--pmc", c, "-d", os.path.join(out, f"pmc_{c}_{w}"), "-o", "pmc",
+                                       "--output-format", "csv", "--",
+                                       *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    for w in SQ_WORKLOADS:
+        p.append((f"sq_{w}", ["rocprofv3", "--pmc", *SQ_COUNTERS.split(), "-d", os.path.join(out, f"sq_{w}"), "-o", "sq",
+                              "--output-format", "csv", "--",
+                              *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    return p
+
+
+def _display(argv, prof):
+    """A pass's command as the profiles print it: output under gpurun_out/prof, other paths
+    relative to the repository root."""
+    return " ".join(argv).replace(prof, "gpurun_out/prof").replace(ROOT + os.sep, "")
+
+
+def collect(out, only=None) -> int:
+    out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT)
+    for name, argv, limit in passes(out):
+        if only and name not in only:
+            continue
+        print(f"== {name}", flush=True)
+        t0 = time.time()
+        with open(os.path.join(out, name + ".out"), "w") as log:
+            try:
+                rc = subprocess.run(argv, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT,
+                                    timeout=limit).returncode
+            except subprocess.TimeoutExpired:
+                print(f"{name}: time limit {limit} s reached; stopping", flush=True)
+                return 124
+        print(f"{name}: rc={rc} in {time.time() - t0:.1f} s", flush=True)
+        if rc != 0:
+            return rc
+    return 0
+
+
+# ---- summaries ------------------------------------------------------------------------------
+
+def _digest(files):
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc(path):
+    agg = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _mean_for(prof, dirname, prefix, sub):
+    d = _pmc(os.path.join(prof, dirname, prefix + "_counter_collection.csv"))
+    vals = [v for (k, _), vs in d.items() if sub in k for v in vs]
+    if not vals:
+        raise KeyError(f"no dispatch of '{sub}' in {dirname}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _cmd_block(cmds):
+    return ["Commands (repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```", *cmds, "```", ""]
+
+
+def summarize_trace(prof, out_md):
+    with open(os.path.join(prof, "trace", "trace_kernel_stats.csv")) as f:
+        rows = list(csv.DictReader(f))
+    lines = ["# Kernel trace: fp32 4096^3 and bf16 8192^3 bench run (rocprofv3 --kernel-trace --stats)", ""]
+    lines += _cmd_block([_display(passes(prof)[0][1], prof)])
+    lines += ["| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} % |")
+    bench_line = None
+    with open(os.path.join(prof, "trace.out")) as f:
+        for line in f:
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    if bench_line:
+        lines += ["", "The same run's bench line (HIP events around each launch on the launch stream):", ""]
+        r = bench_line["roofline"]
+        lines.append(f"- fp32 4096^3 `{r['kernel']}`: event mean {r['kernel_ms_mean'] * 1e3:.1f} us, "
+                     f"achieved {r['achieved']} TFLOP/s")
+        if "bf16_8192" in bench_line:
+            r2 = bench_line["bf16_8192"]["roofline"]
+            lines.append(f"- bf16 8192^3 `{r2['kernel']}`: event mean {r2['kernel_ms_mean'] * 1e3:.1f} us, "
+                         f"achieved {r2['achieved']} TFLOP/s")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_traffic(prof, out_json, out_md):
+    cf, _ = _mean_for(prof, "pmc_FETCH_SIZE_copy", "pmc", "copyBuffer")
+    cw, _ = _mean_for(prof, "pmc_WRITE_SIZE_copy", "pmc", "copyBuffer")
+    fs, ws = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    res = {"about": "HBM-side bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, "
+                    "KiB per dispatch), each scaled by the reading of the same counter for a plain 1 GiB "
+                    "device copy (copy bytes / counter bytes).",
+           "calibration": {"kernel": "__amd_rocclr_copyBuffer", "bytes_each_way": COPY_BYTES,
+                           "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw, "fetch_scale": fs, "write_scale": ws},
+           "kernels": {}}
+    cmds = [_display(a, prof) for n, a, _ in passes(prof) if n.startswith("pmc_")]
+    md = ["# HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", ""] + _cmd_block(cmds)
+    md += [f"Calibration: a 1 GiB copy reads FETCH_SIZE = {cf:.0f} KiB and WRITE_SIZE = {cw:.0f} KiB, so fetch "
+           f"counts are scaled by {fs:.3f} and write counts by {ws:.3f}.", "",
+           "| workload | kernel | FETCH_SIZE KiB (mean of dispatches) | WRITE_SIZE KiB | HBM bytes per launch "
+           "(scaled) | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+    for w, (label, sub, sources, alg) in KERNELS.items():
+        f, nf = _mean_for(prof, f"pmc_FETCH_SIZE_{w}", "pmc", sub)
+        wr, nw = _mean_for(prof, f"pmc_WRITE_SIZE_{w}", "pmc", sub)
+        tb = f * 1024 * fs + wr * 1024 * ws
+        res["kernels"][label] = {"workload": w, "sources": sources, "sources_digest": _digest(sources),
+                                 "FETCH_SIZE_KiB": f, "WRITE_SIZE_KiB": wr, "hbm_bytes_per_launch": int(tb),
+                                 "algorithmic_bytes": alg, "dispatches": [nf, nw]}
+        md.append(f"| {w} | `{label}` | {f:.0f} | {wr:.0f} | {tb / 1e6:.1f} MB | {alg / 1e6:.1f} MB | {tb / alg:.2f} |")
+    md += ["", "Traffic above the algorithmic bytes is operand panels fetched again by different XCDs (each has "
+               "its own L2) and re-fetched after eviction; the MALL (Infinity Cache) serves part of it."]
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+def summarize_sq(prof, out_md):
+    cmds = [_display(a, prof) for n, a, _ in passes(prof) if n.startswith("sq_")]
+    md = ["# SQ counters: LDS instructions, bank conflicts, VALU/MFMA instructions", ""] + _cmd_block(cmds)
+    for w in SQ_WORKLOADS:
+        label, sub = KERNELS[w][0], KERNELS[w][1]
+        d = _pmc(os.path.join(prof, f"sq_{w}", "sq_counter_collection.csv"))
+        vals = collections.defaultdict(list)
+        for (k, c), vs in d.items():
+            if sub in k:
+                vals[c].extend(vs)
+        m = {c: sum(vs) / len(vs) for c, vs in vals.items()}
+        md += [f"## {w} (`{label}`), mean per dispatch", ""]
+        md += [f"- {c}: {m[c]:.0f}" for c in sorted(m)]
+        waves = m.get("SQ_WAVES", 0)
+        if waves:
+            md.append(f"- per wave: {m['SQ_INSTS_LDS'] / waves:.0f} LDS instructions, "
+                      f"{m['SQ_INSTS_VALU'] / waves:.0f} VALU instructions, "
+                      f"{m.get('SQ_INSTS_MFMA', 0) / waves:.0f} MFMA instructions")
+        if m.get("SQ_LDS_IDX_ACTIVE"):
+            md.append(f"- bank-conflict rate SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = "
+                      f"{100 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.1f} %")
+        md.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+def summarize(prof) -> int:
+    prof = os.path.abspath(prof)
+    summarize_trace(prof, os.path.join(PROFILES, "kernel_trace_f32_4096_bf16_8192.md"))
+    summarize_traffic(prof, os.path.join(PROFILES, "pmc_traffic.json"),
+                      os.path.join(PROFILES, "hbm_traffic_f32_4096_bf16_8192.md"))
+    summarize_sq(prof, os.path.join(PROFILES, "sq_counters_f32_4096_bf16_8192.md"))
+    return 0
+
+
+def main(argv=None) -> int:
+    import argparse
+
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("cmd", choices=["collect", "summarize", "commands"])
+    p.add_argument("dir", help="directory for (collect) or of (summarize) the rocprofv3 output")
+    p.add_argument("--only", default="", help="collect: comma-separated pass names")
+    a = p.parse_args(argv)
+    if a.cmd == "collect":
+        return collect(a.dir, [s for s in a.only.split(",") if s])
+    if a.cmd == "commands":
+        for name, argv_, limit in passes(os.path.abspath(a.dir)):
+            print(f"{name} ({limit} s): {' '.join(argv_)}")
+        return 0
+    return summarize(a.dir)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
