@@ -33,13 +33,10 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 constexpr int BK = 64;   // bf16 per slab row
 constexpr int KCH = 8;   // 16-byte chunks per slab row
 
-// Slot of 16-byte chunk `chunk` of slab row `row` (rows of 8 chunks = 128 bytes). gfx950 serves
-// 128-bit LDS reads 16 lanes at a time over 64 banks (256 bytes): a fragment read touches 16
-// consecutive rows at one chunk, i.e. 8 even rows in banks 0-31 and 8 odd rows in banks 32-63,
-// so each parity class must land on 8 distinct slots. row & 7 alone repeats every 8 rows
-// (2-way conflict); folding in bit 3 makes every aligned group of 16 rows conflict-free.
-__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * KCH + (chunk ^ swz_key(row)); }
+// Slot of 16-byte chunk `chunk` of slab row `row` (rows of 8 chunks = 128 bytes): the same
+// swizzle as the DMA kernel's 32x32x16 slabs (mfma::slab_key), under which the fragment reads
+// are free of LDS bank conflicts.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * KCH + (chunk ^ mfma::slab_key<KCH>(row)); }
 
 template <bool EDGE, bool VEC>
 __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool row_ok,

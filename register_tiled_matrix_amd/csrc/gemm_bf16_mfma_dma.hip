@@ -12,11 +12,11 @@
 //    belongs in LDS slot (base + l): the permutation is applied to the global addresses.
 //  * Slab layout: a tile row (an A row, or a B column: both operands are K-contiguous) of
 //    BK bf16 is KCH = BK/8 chunks of 16 bytes; chunk c of row r sits in slot c ^ key(r).
-//    128-bit LDS reads are served 16 lanes at a time over 64 banks (256 bytes). A fragment
-//    read covers 16 consecutive rows at one chunk, and the key makes those 16 reads hit 16
-//    distinct 16-byte bank groups:
-//      KCH = 8 (128-byte rows): key(r) = (r & 7) ^ ((r >> 3) & 1)
-//      KCH = 4 ( 64-byte rows): key(r) = (r >> 2) & 3
+//    The key is chosen per fragment shape by measurement (LDS bank-conflict counters on the
+//    fragment read patterns; mfma_common.h) so that the fragment reads are conflict-free:
+//      KCH = 8, MF = 32: key(r) = (r & 7) ^ ((r >> 3) & 1)
+//      KCH = 8, MF = 16: key(r) = ((r >> 1) & 7) ^ ((r & 1) << 2)
+//      KCH = 4 (64-byte rows): key(r) = (r >> 2) & 3
 //  * Two LDS stages and one barrier per slab, placed inside the slab's last k step: the
 //    next slab is loaded while the current one is consumed, and its first fragments are
 //    read before the current slab's last MFMAs (section 6.3: prefetch of the next k slice
@@ -82,10 +82,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int pa = (wave * JA + j) * 64 + lane;
-        const int ra = pa / KCH, ca = (pa % KCH) ^ slab_key<KCH>(ra);
+        const int ra = pa / KCH, ca = (pa % KCH) ^ slab_key<KCH, MF>(ra);
         a_voff[j] = (uint32_t)(ra * lda + ca * 8) * 2u;
         const int pb = (wave * JB + j) * 64 + lane;
-        const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH>(rb);
+        const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH, MF>(rb);
         b_voff[j] = (uint32_t)(rb * ldb + cb * 8) * 2u;
     }
     const uint32_t a_step = (uint32_t)(ROWS_PER_INSTR * lda) * 2u;  // bytes per instruction
@@ -119,12 +119,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int row = wm * WTM + i * MF + frag_r;
-            fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH>(row))]);
+            fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int row = wn * WTN + j * MF + frag_r;
-            fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH>(row))]);
+            fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
         }
     };
     // One slab is KSTEPS k steps. Each starts by waiting for its own fragments (read during

@@ -182,8 +182,31 @@ __device__ __forceinline__ int key_row7_row8(int row, int c) {
     return row * 128 + ((c ^ ((row & 7) ^ ((row >> 3) & 1))) * 16);
 }
 
+// Candidate keys for 128-byte slab rows (8 chunks of 16 bytes): chunk c of row r sits at
+// c ^ key(r). Candidate 0 is the one the MFMA kernels use.
+__device__ __forceinline__ int cand_key(int cand, int r) {
+    const int lo = r & 7, b3 = (r >> 3) & 1;
+    switch (cand) {
+        case 0: return lo ^ b3;
+        case 1: return lo ^ (b3 << 1);
+        case 2: return lo ^ (b3 << 2);
+        case 3: return lo ^ (b3 * 3);
+        case 4: return ((r >> 1) & 7) ^ ((r & 1) << 2);
+        default: return ((r >> 1) & 3) ^ ((r & 1) << 2) ^ (b3 << 1);
+    }
+}
+
 template <int P>
 __device__ __forceinline__ int lds_pattern(int lane) {
+    if (P >= 100) {  // candidate key (P - 100) / 2; even P: 32x32x16 fragment read, odd: 16x16x32
+        const int cand = (P - 100) / 2;
+        if ((P & 1) == 0) {
+            const int r = lane & 31, c = 2 + (lane >> 5);
+            return r * 128 + ((c ^ cand_key(cand, r)) * 16);
+        }
+        const int r = lane & 15, c = 4 + (lane >> 4);
+        return r * 128 + ((c ^ cand_key(cand, r)) * 16);
+    }
     switch (P) {
         case 0: return lane * 16;                                 // 1 KiB contiguous
         case 1: return key_row7(lane & 31, 2 + (lane >> 5));      // 32 rows of 128 B, chunk ^ (row & 7)
@@ -191,6 +214,8 @@ __device__ __forceinline__ int lds_pattern(int lane) {
         case 3: return (lane & 31) * 128 + (lane >> 5) * 16;      // 32 rows of 128 B, no swizzle
         case 4: return (lane >> 3) * 16;                          // 8 distinct addresses, rest broadcast
         case 5: return (lane & 1) * 256 + (lane >> 1) * 16;       // lane pairs 256 B apart
+        case 7: return key_row7_row8(lane & 15, 2 + (lane >> 4)); // 16 rows x 4 chunks (16x16x32 fragment)
+        case 8: return (lane & 15) * 128 + (2 + (lane >> 4)) * 16; // same, no swizzle
         default: return key_row7_row8(lane >> 3, lane & 7);       // 8 lanes per 128-byte row
     }
 }
@@ -238,6 +263,20 @@ int run_lds() {
     rc |= lds_one<3, false>(d, "ds_read_b128, 128-byte rows, no swizzle");
     rc |= lds_one<4, false>(d, "ds_read_b128, 8 distinct addresses");
     rc |= lds_one<5, false>(d, "ds_read_b128, lane pairs 256 B apart");
+    rc |= lds_one<7, false>(d, "ds_read_b128, 16 rows x 4 chunks, chunk ^ ((row & 7) ^ (row >> 3 & 1))");
+    rc |= lds_one<8, false>(d, "ds_read_b128, 16 rows x 4 chunks, no swizzle");
+    rc |= lds_one<100, false>(d, "key candidate 0, 32x32x16 fragment");
+    rc |= lds_one<101, false>(d, "key candidate 0, 16x16x32 fragment");
+    rc |= lds_one<102, false>(d, "key candidate 1, 32x32x16 fragment");
+    rc |= lds_one<103, false>(d, "key candidate 1, 16x16x32 fragment");
+    rc |= lds_one<104, false>(d, "key candidate 2, 32x32x16 fragment");
+    rc |= lds_one<105, false>(d, "key candidate 2, 16x16x32 fragment");
+    rc |= lds_one<106, false>(d, "key candidate 3, 32x32x16 fragment");
+    rc |= lds_one<107, false>(d, "key candidate 3, 16x16x32 fragment");
+    rc |= lds_one<108, false>(d, "key candidate 4, 32x32x16 fragment");
+    rc |= lds_one<109, false>(d, "key candidate 4, 16x16x32 fragment");
+    rc |= lds_one<110, false>(d, "key candidate 5, 32x32x16 fragment");
+    rc |= lds_one<111, false>(d, "key candidate 5, 16x16x32 fragment");
     rc |= lds_one<0, true>(d, "ds_write_b128, 1 KiB contiguous");
     rc |= lds_one<6, true>(d, "ds_write_b128, 8 lanes per 128-byte row");
     return rc;
