@@ -64,19 +64,41 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool
     return r;
 }
 
-// 8 consecutive k values of one M (or N) index from an operand stored K-major-outer (element
-// (r, k) at p[k * ld] relative to the chunk's first one): 8 scalar loads, zero outside.
-__device__ __forceinline__ uint4 load_chunk_mn(const uint16_t *__restrict__ p, int64_t ld,
-                                               bool row_ok, int k_left) {
-    uint16_t v[8];
+// A 4 x 8 block of an operand stored K-major-outer (element (r, k) at p[k * ld + r] relative
+// to the block's first element, r < 4 along the contiguous M or N dimension, k < 8): read as
+// 8 runs of 4 elements (one 8-byte load per k when `vec`, else predicated 2-byte loads; zero
+// outside r_left x k_left) and transposed in registers into 4 chunks of 8 consecutive k, the
+// K-contiguous form the fragment reads expect. out[j] holds row r = j.
+template <bool EDGE>
+__device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, int64_t ld, bool vec,
+                                              int r_left, int k_left, uint4 out[4]) {
+    uint32_t lo[8], hi[8];  // k = kk: rows 0, 1 in lo (low half = row 0), rows 2, 3 in hi
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (row_ok && e < k_left) ? p[e * ld] : (uint16_t)0;
-    uint4 r;
-    r.x = v[0] | ((uint32_t)v[1] << 16);
-    r.y = v[2] | ((uint32_t)v[3] << 16);
-    r.z = v[4] | ((uint32_t)v[5] << 16);
-    r.w = v[6] | ((uint32_t)v[7] << 16);
-    return r;
+    for (int kk = 0; kk < 8; ++kk) {
+        const uint16_t *q = p + kk * ld;
+        if (vec && (!EDGE || (kk < k_left && r_left >= 4))) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(q);
+            lo[kk] = v.x;
+            hi[kk] = v.y;
+        } else {
+            uint32_t e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (!EDGE || (kk < k_left && j < r_left)) ? q[j] : 0u;
+            lo[kk] = e[0] | (e[1] << 16);
+            hi[kk] = e[2] | (e[3] << 16);
+        }
+    }
+    // out[j] dword d = (k = 2d in the low half, k = 2d + 1 in the high half) of row j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t *src = j < 2 ? lo : hi;
+        uint32_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            d[q] = (j & 1) ? (src[2 * q] >> 16) | (src[2 * q + 1] & 0xFFFF0000u)
+                           : (src[2 * q] & 0xFFFFu) | (src[2 * q + 1] << 16);
+        out[j] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
 }
 
 // A_MN: A stored K x M (M-contiguous); B_MN: B stored K x N (N-contiguous). The LDS slab is
@@ -87,7 +109,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VE
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, int mn_vec) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int MI = WTM / 32, NI = WTN / 32;
@@ -116,47 +138,50 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     const int64_t a_pass = (int64_t)ROWS_PER_PASS * lda;
     const int64_t b_pass = (int64_t)ROWS_PER_PASS * ldb;
 
-    // MN-contiguous staging: slot e = tid + NT*i is row e % BM (or BN), chunk e / BM.
-    static_assert(!A_MN || NT % BM == 0, "whole rows per pass");
-    static_assert(!B_MN || NT % BN == 0, "whole rows per pass");
-    constexpr int A_MN_CPP = A_MN ? NT / BM : 1, B_MN_CPP = B_MN ? NT / BN : 1;  // chunks per pass
-    const int amn_row = tid % BM, amn_chunk = tid / BM;
-    const int bmn_row = tid % BN, bmn_chunk = tid / BN;
+    // MN-contiguous staging: thread t owns the 4 x 8 block at rows 4 (t % (B/4)), chunk
+    // t / (B/4) of the slab (B = BM or BN): consecutive lanes read consecutive 8-byte runs
+    // along the contiguous dimension at one k. `mn_vec` (uniform) says the runs are 8-byte
+    // aligned (leading dimension a multiple of 4, operand 8-byte aligned).
+    static_assert(!A_MN || BM * BK == 32 * NT, "one 4 x 8 block of A per thread");
+    static_assert(!B_MN || BN * BK == 32 * NT, "one 4 x 8 block of B per thread");
+    const int amn_row = (tid % (BM / 4)) * 4, amn_chunk = tid / (BM / 4);
+    const int bmn_row = (tid % (BN / 4)) * 4, bmn_chunk = tid / (BN / 4);
+    const bool vec_mn = mn_vec != 0;
 
     uint4 ra[A_CH], rb[B_CH];
     auto load_slab = [&](int k0) {
+        if (A_MN) {
+            const int kc = k0 + amn_chunk * 8;
+            load_block_mn<EDGE>(A + (int64_t)kc * lda + m0 + amn_row, lda, vec_mn, M - (m0 + amn_row),
+                                K - kc, ra);
+        } else {
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            if (A_MN) {
-                const int kc = k0 + (amn_chunk + i * A_MN_CPP) * 8;
-                ra[i] = load_chunk_mn(A + (int64_t)kc * lda + m0 + amn_row, lda, m0 + amn_row < M, K - kc);
-            } else {
+            for (int i = 0; i < A_CH; ++i)
                 ra[i] = load_chunk<EDGE, VEC>(a_src + i * a_pass + k0,
                                               m0 + ld_row + i * ROWS_PER_PASS < M,
                                               K - k0 - ld_chunk * 8);
-            }
         }
+        if (B_MN) {
+            const int kc = k0 + bmn_chunk * 8;
+            load_block_mn<EDGE>(B + (int64_t)kc * ldb + n0 + bmn_row, ldb, vec_mn, N - (n0 + bmn_row),
+                                K - kc, rb);
+        } else {
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            if (B_MN) {
-                const int kc = k0 + (bmn_chunk + i * B_MN_CPP) * 8;
-                rb[i] = load_chunk_mn(B + (int64_t)kc * ldb + n0 + bmn_row, ldb, n0 + bmn_row < N, K - kc);
-            } else {
+            for (int i = 0; i < B_CH; ++i)
                 rb[i] = load_chunk<EDGE, VEC>(b_src + i * b_pass + k0,
                                               n0 + ld_row + i * ROWS_PER_PASS < N,
                                               K - k0 - ld_chunk * 8);
-            }
         }
     };
     auto store_slab = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
-            if (A_MN) sA[buf][swz(amn_row, amn_chunk + i * A_MN_CPP)] = ra[i];
+            if (A_MN) sA[buf][swz(amn_row + i, amn_chunk)] = ra[i];
             else sA[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
-            if (B_MN) sB[buf][swz(bmn_row, bmn_chunk + i * B_MN_CPP)] = rb[i];
+            if (B_MN) sB[buf][swz(bmn_row + i, bmn_chunk)] = rb[i];
             else sB[buf][swz(ld_row + i * ROWS_PER_PASS, ld_chunk)] = rb[i];
         }
     };
@@ -229,12 +254,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
 
 template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16, bool A_MN = false,
           bool B_MN = false>
-hipError_t launch_cfg(const Problem &p, hipStream_t s) {
+hipError_t launch_cfg(const Problem &p, hipStream_t s, bool mn_vec = false) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16, A_MN, B_MN>),
                        dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
                        (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,
-                       p.ldc, tiles_m, tiles_n);
+                       p.ldc, tiles_m, tiles_n, mn_vec ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -248,16 +273,28 @@ hipError_t launch_pick(const Problem &p, hipStream_t s, bool edge, bool vec) {
 
 // Operands other than K-contiguous A and B: 128x128 tiles, edge-predicated kernel; `vec` only
 // matters for a K-contiguous operand.
-template <bool F16>
-hipError_t launch_layout(const Problem &p, hipStream_t s, bool vec) {
+template <int BM, int BN, int WM, int WN, bool F16>
+hipError_t launch_layout_tile(const Problem &p, hipStream_t s, bool vec, bool mn_vec) {
     const bool a_mn = p.ta, b_mn = !p.tb;
     if (a_mn && b_mn)
-        return launch_cfg<128, 128, 2, 2, true, false, F16, true, true>(p, s);
+        return launch_cfg<BM, BN, WM, WN, true, false, F16, true, true>(p, s, mn_vec);
     if (a_mn)
-        return vec ? launch_cfg<128, 128, 2, 2, true, true, F16, true, false>(p, s)
-                   : launch_cfg<128, 128, 2, 2, true, false, F16, true, false>(p, s);
-    return vec ? launch_cfg<128, 128, 2, 2, true, true, F16, false, true>(p, s)
-               : launch_cfg<128, 128, 2, 2, true, false, F16, false, true>(p, s);
+        return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, true, false>(p, s, mn_vec)
+                   : launch_cfg<BM, BN, WM, WN, true, false, F16, true, false>(p, s, mn_vec);
+    return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, false, true>(p, s, mn_vec)
+               : launch_cfg<BM, BN, WM, WN, true, false, F16, false, true>(p, s, mn_vec);
+}
+
+// 256x256 tiles of eight waves when there are enough of them to fill the chip, else 128x128.
+template <bool F16>
+hipError_t launch_layout(const Problem &p, hipStream_t s, bool vec, bool big) {
+    const bool a_mn = p.ta, b_mn = !p.tb;
+    // 8-byte runs along M / N: leading dimension a multiple of 4 and an 8-byte aligned base
+    // for every MN-contiguous operand
+    const bool mn_vec = (!a_mn || ((p.lda % 4) == 0 && aligned8(p.A))) &&
+                        (!b_mn || ((p.ldb % 4) == 0 && aligned8(p.B)));
+    return big ? launch_layout_tile<256, 256, 2, 4, F16>(p, s, vec, mn_vec)
+               : launch_layout_tile<128, 128, 2, 2, F16>(p, s, vec, mn_vec);
 }
 
 #define REGTILE_STAGED_NAMES(elt, tile)                                                        \
@@ -267,12 +304,17 @@ const char *const kStagedNames[2][2][4] = {
     {REGTILE_STAGED_NAMES("bf16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("bf16", "256x256x64_w2x4")},
     {REGTILE_STAGED_NAMES("f16", "128x128x64_w2x2"), REGTILE_STAGED_NAMES("f16", "256x256x64_w2x4")}};
 #undef REGTILE_STAGED_NAMES
-// [f16][layout code: 0 = "tt", 1 = "tn", 2 = "nn"][vec], BLAS letters of op(A), op(B) storage
-#define REGTILE_LAYOUT_NAMES(elt, lay)                                                          \
-    { elt "_mfma_128x128x64_w2x2_" lay "_edge", elt "_mfma_128x128x64_w2x2_" lay "_edge_vec" }
-const char *const kLayoutNames[2][3][2] = {
-    {REGTILE_LAYOUT_NAMES("bf16", "tt"), REGTILE_LAYOUT_NAMES("bf16", "tn"), REGTILE_LAYOUT_NAMES("bf16", "nn")},
-    {REGTILE_LAYOUT_NAMES("f16", "tt"), REGTILE_LAYOUT_NAMES("f16", "tn"), REGTILE_LAYOUT_NAMES("f16", "nn")}};
+// [f16][big][layout code: 0 = "tt", 1 = "tn", 2 = "nn"][vec], BLAS letters of op(A), op(B)
+// storage
+#define REGTILE_LAYOUT_NAMES(elt, tile, lay) \
+    { elt "_mfma_" tile "_" lay "_edge", elt "_mfma_" tile "_" lay "_edge_vec" }
+#define REGTILE_LAYOUT_ROW(elt, tile)                                                       \
+    { REGTILE_LAYOUT_NAMES(elt, tile, "tt"), REGTILE_LAYOUT_NAMES(elt, tile, "tn"),          \
+      REGTILE_LAYOUT_NAMES(elt, tile, "nn") }
+const char *const kLayoutNames[2][2][3][2] = {
+    {REGTILE_LAYOUT_ROW("bf16", "128x128x64_w2x2"), REGTILE_LAYOUT_ROW("bf16", "256x256x64_w2x4")},
+    {REGTILE_LAYOUT_ROW("f16", "128x128x64_w2x2"), REGTILE_LAYOUT_ROW("f16", "256x256x64_w2x4")}};
+#undef REGTILE_LAYOUT_ROW
 #undef REGTILE_LAYOUT_NAMES
 
 }  // namespace
@@ -282,8 +324,9 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
     if (p.ta || !p.tb) {  // not the native K-contiguous pair
         const bool vec = (p.ta ? (p.ldb % 8) == 0 && aligned16(p.B) : (p.lda % 8) == 0 && aligned16(p.A));
         const int lay = (p.ta && p.tb) ? 0 : p.ta ? 1 : 2;  // tt: A K x M, B N x K; tn; nn
-        *name = kLayoutNames[f16][lay][vec && !(p.ta && !p.tb)];
-        return f16 ? launch_layout<true>(p, s, vec) : launch_layout<false>(p, s, vec);
+        const bool big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
+        *name = kLayoutNames[f16][big][lay][vec && !(p.ta && !p.tb)];
+        return f16 ? launch_layout<true>(p, s, vec, big) : launch_layout<false>(p, s, vec, big);
     }
     // Full aligned 256x256 tiles, enough of them to fill the chip: the LDS-DMA kernel,
     // else the register-staged kernel below.

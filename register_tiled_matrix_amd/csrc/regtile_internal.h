@@ -42,6 +42,7 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 
 // Host-side launch checks.
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // s_waitcnt lgkmcnt(N) with no wait on the vector-memory or export counters (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).

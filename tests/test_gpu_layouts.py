@@ -132,3 +132,18 @@ def test_16bit_layouts_8192_sampled(ta, tb, dtype):
     announce(f"{dtype}_8192 layout {ta}{tb}")
     got, name = _run(inp, ta, tb)
     assert_parity_sampled(inp, got, f"{dtype}_8192 layout ({ta},{tb}) ({name})", n_random=10000)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("shape", [(4000, 4100, 200), (4001, 4099, 136)], ids=lambda s: "x".join(map(str, s)))
+def test_16bit_gathered_layouts_large_ragged(shape, ta, tb, dtype):
+    # enough 256x256 tiles for the eight-wave gathered kernel, ragged on every side; the second
+    # shape's odd leading dimensions (lda = M for A stored K x M, ldb = N for B stored K x N)
+    # take the 2-byte gather instead of the 8-byte runs
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=0.75, beta=0.5, seed=M + N + K + 2 * ta + tb)
+    announce(f"{dtype} gathered layout {ta}{tb} {shape}")
+    got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA)
+    assert "256x256x64_w2x4" in name, name
+    assert_parity_sampled(inp, got, f"{dtype} layout ({ta},{tb}) {shape} ({name})", n_random=50000)
