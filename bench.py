@@ -56,8 +56,9 @@ def _parse():
     return p.parse_args()
 
 
-def _time(torch, fn, steps, warmup):
-    """(wall ms per step, mean per-launch kernel ms from event pairs)."""
+def _kernel_times(torch, fn, steps, warmup):
+    """(wall ms per step, per-launch kernel ms from event pairs around each launch on the
+    current stream, which is the stream every launch here goes to)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -70,8 +71,50 @@ def _time(torch, fn, steps, warmup):
         ends[i].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def _time(torch, fn, steps, warmup):
+    """(wall ms per step, mean per-launch kernel ms from event pairs, fastest launch ms)."""
+    wall_ms, kern = _kernel_times(torch, fn, steps, warmup)
     return wall_ms, float(np.mean(kern)), float(np.min(kern))
+
+
+def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
+    """Every configuration through the default entry points: 5 warm-up and 30 timed launches,
+    TFLOP/s from the median event time, and the fraction of the peak that bounds it."""
+    res = {}
+    names = ["f32_256", "f32_4096", "f32_ragged", "f32_tall"] + (["bf16_8192"] if with_16bit else [])
+    for wname in names:
+        wc = gi.WORKLOADS[wname]
+        ic = gi.workload_inputs(wc)
+        if wc.dtype == "f32":
+            A = torch.from_numpy(ic.A).to(dev)
+            B = torch.from_numpy(ic.B).to(dev)
+            raw, ldb, peak = rt.gemm_f32_raw, wc.N, acc.PEAK_FP32_VECTOR_TFLOPS
+        else:
+            A = torch.from_numpy(ic.A.view(np.int16)).to(dev)
+            B = torch.from_numpy(ic.B.view(np.int16)).to(dev)
+            raw, ldb, peak = rt.gemm_bf16_raw, wc.K, acc.PEAK_BF16_MFMA_TFLOPS
+        C = (torch.from_numpy(ic.C).to(dev) if ic.C is not None
+             else torch.empty((wc.M, wc.N), dtype=torch.float32, device=dev))
+        call = (wc.M, wc.N, wc.K, wc.alpha, A.data_ptr(), wc.K, B.data_ptr(), ldb, wc.beta,
+                C.data_ptr(), wc.N, stream)
+
+        def step(call=call, raw=raw):
+            st = raw(*call)
+            if st:
+                raise rt.RegtileError(st, rt.strerror(st))
+
+        step()
+        kname = rt.last_kernel()
+        _, kern = _kernel_times(torch, step, 30, 5)
+        med = float(np.median(kern))
+        tf = wc.flop / (med * 1e-3) / 1e12
+        res[wname] = {"shape": [wc.M, wc.N, wc.K], "kernel": kname, "kernel_ms_median": round(med, 4),
+                      "TFLOP/s": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4)}
+        del A, B, C
+    return res
 
 
 def _sources_digest(files):
@@ -389,6 +432,9 @@ def main():
                                        "kernel_ms": out["f16_8192"]["roofline"]["kernel_ms_mean"],
                                        "TFLOP/s": out["f16_8192"]["roofline"]["achieved"]}
         out["ladder"] = ladder
+
+    # ---- every configuration, median of 30 launches ------------------------------------------
+    out["configs"] = _configs(torch, gi, rt, acc, dev, stream, not args.no_bf16)
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------
     if not args.no_cpu:
