@@ -36,7 +36,8 @@ namespace regtile {
 namespace {
 using namespace mfma;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16,
+          int RING = 2>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -54,8 +55,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     static_assert(WTM % MF == 0 && WTN % MF == 0 && BK % F::KSTEP == 0, "fragment shapes");
     static_assert(PER_SLAB < 64, "vmcnt range");
     constexpr int STAGES = 2;
+    static_assert(RING == 2 || (RING == 5 && A_SLOTS == B_SLOTS), "two stages, or a ring of five halves");
 
-    __shared__ uint4 smem[STAGES * STAGE_SLOTS];
+    __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
 
     const int tid = threadIdx.x;
     // wave-uniform by construction; readfirstlane tells the compiler so (scalar registers
@@ -98,6 +100,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         else
             dma16_buf(b_rsrc, b_voff[(q - JA) & 1], (uint32_t)((q - JA) & ~1) * b_step + (uint32_t)k0 * 2u,
                       sb + (wave * JB + (q - JA)) * 64);
+    };
+
+    // One DMA instruction q of the A part (B part) of the slab starting at k0 into the half
+    // (A or B area) at `dst`.
+    auto dma_a = [&](int q, int k0, uint4 *dst) {
+        dma16_buf(a_rsrc, a_voff[q & 1], (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u, dst + (wave * JA + q) * 64);
+    };
+    auto dma_b = [&](int q, int k0, uint4 *dst) {
+        dma16_buf(b_rsrc, b_voff[q & 1], (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
     };
 
     typename F::acc_t acc[MI][NI];
@@ -187,11 +198,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // Past the end, requests are clamped to the last slab: they refill a stage nobody reads
     // again with valid data and keep every iteration identical (same counts at every wait).
     const int nslabs = K / BK;
+    if constexpr (RING == 2) {
 #pragma unroll
-    for (int q = 0; q < PER_SLAB; ++q) dma_q(q, 0, smem, smem + A_SLOTS);
-    wait_vmcnt<0>();
-    lds_barrier();
-    read_frags(smem, smem + A_SLOTS, 0, 0);
+        for (int q = 0; q < PER_SLAB; ++q) dma_q(q, 0, smem, smem + A_SLOTS);
+        wait_vmcnt<0>();
+        lds_barrier();
+        read_frags(smem, smem + A_SLOTS, 0, 0);
+    }
 
     // DMA windows sit at positions of the k-step sequence: position 0 is the last k step of
     // a slab (after its barrier), position p >= 1 is k step p-1 of the next slab. Window w of
@@ -228,10 +241,78 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             }
         }
     };
-    if (STAGGER && wave >= NWAVES / 2)
-        main_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
-    else
-        main_loop(std::integral_constant<int, 0>{});
+    // Ring of five half-stages (RING == 5): all of LDS as five 32 KB halves, slab t's A part
+    // in half (2t) % 5 and its B part in half (2t + 1) % 5. While slab s is consumed, slab
+    // s+1 is in two more halves and slab s+2's A part in the fifth, so after the barrier that
+    // frees slab s's two halves a wave loads B of slab s+2 and A of slab s+3 into them. A
+    // parts thus get about two slabs to land, and the barrier before slab s+1's last k step
+    // waits only for B of slab s+2 (the A loads issued after it may stay in flight).
+    auto ring_window = [&](int win, int slab_b, int h_b, int slab_a, int h_a) {
+        const int kb = min(slab_b, nslabs - 1) * BK, ka = min(slab_a, nslabs - 1) * BK;
+#pragma unroll
+        for (int d = 0; d < DMA_PER_WIN; ++d) {
+            const int q = win * DMA_PER_WIN + d;  // B instructions first, then A
+            if (q < JB)
+                dma_b(q, kb, smem + h_b * A_SLOTS);
+            else if (q < PER_SLAB)
+                dma_a(q - JB, ka, smem + h_a * A_SLOTS);
+        }
+    };
+    auto wrap5 = [](int h) { return h >= 5 ? h - 5 : h; };
+    auto ring_loop = [&](auto shift_tag) {
+        constexpr int SH = decltype(shift_tag)::value;
+        static_assert(SH + NWIN <= KSTEPS, "every window lands at least one k step before its barrier");
+        // prologue: A and B of slab 0, A of slab 1, and (unshifted waves) the first window of
+        // the set a barrier before slab 0 would have issued: B of slab 1, A of slab 2
+#pragma unroll
+        for (int q = 0; q < JA; ++q) dma_a(q, 0, smem);
+#pragma unroll
+        for (int q = 0; q < JB; ++q) dma_b(q, 0, smem + A_SLOTS);
+#pragma unroll
+        for (int q = 0; q < JA; ++q) dma_a(q, min(1, nslabs - 1) * BK, smem + 2 * A_SLOTS);
+        if (SH == 0) ring_window(0, 1, 3, 2, 4);
+        wait_vmcnt<JA + (SH == 0 ? dmas_in(0) : 0)>();  // A and B of slab 0 have landed
+        lds_barrier();
+        read_frags(smem, smem + A_SLOTS, 0, 0);
+        int ha = 0;  // half of slab s's A part; its B part is in ha + 1
+        for (int s = 0; s < nslabs; ++s) {
+            const int hb = wrap5(ha + 1), hna = wrap5(ha + 2), hnb = wrap5(ha + 3), hfa = wrap5(ha + 4);
+            const uint4 *sa = smem + ha * A_SLOTS, *sb = smem + hb * A_SLOTS;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const int cb = kk & 1;
+                wait_lgkmcnt0();
+                if (kk + 1 < KSTEPS) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_frags(sa, sb, kk + 1, cb ^ 1);
+                    // windows of the set issued after the previous slab's barrier:
+                    // B of slab s+1 (half hnb) and A of slab s+2 (half hfa)
+                    const int win = kk + 1 - SH;
+                    const bool has = win >= 0 && win < NWIN;
+                    if (has) ring_window(win, s + 1, hnb, s + 2, hfa);
+                    mfma_woven(cb, NREAD, has ? dmas_in(win) : 0);
+                } else {
+                    wait_vmcnt<JA>();  // B of slab s+1 landed (A of slab s+2 may be in flight)
+                    lds_barrier();     // slab s+1 published; slab s's halves read by nobody
+                    read_frags(smem + hna * A_SLOTS, smem + hnb * A_SLOTS, 0, cb ^ 1);
+                    if (SH == 0) ring_window(0, s + 2, ha, s + 3, hb);
+                    mfma_woven(cb, NREAD, SH == 0 ? dmas_in(0) : 0);
+                }
+            }
+            ha = wrap5(ha + 2);
+        }
+    };
+    if constexpr (RING == 5) {
+        if (STAGGER && wave >= NWAVES / 2)
+            ring_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
+        else
+            ring_loop(std::integral_constant<int, 0>{});
+    } else {
+        if (STAGGER && wave >= NWAVES / 2)
+            main_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
+        else
+            main_loop(std::integral_constant<int, 0>{});
+    }
     wait_vmcnt<0>();  // no LDS DMA may still be in flight when the workgroup retires
 
     // Epilogue: accumulator v of a fragment lands at (row_lane + row_acc(v), lane % MF) of
@@ -268,10 +349,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16>
+template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -294,6 +375,15 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 #define DMA_WIN16 1
 #define DMA_STAG16 0
 #endif
+// LDS layout per fragment shape: a ring of five half-stages for 32x32x16 (+3.5% at 8192^3
+// against two stages, same box and run), two stages for 16x16x32 (the ring measured 5.7%
+// slower there)
+#ifndef DMA_RING32
+#define DMA_RING32 5
+#endif
+#ifndef DMA_RING16
+#define DMA_RING16 2
+#endif
 
 }  // namespace
 
@@ -314,17 +404,17 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
     if (f16) {
         if (shape == 16) {
             *name = REGTILE_DMA_NAME("f16", "16x16x32");
-            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, true>(p, s);
+            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, true, DMA_RING16>(p, s);
         }
         *name = REGTILE_DMA_NAME("f16", "32x32x16");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true>(p, s);
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, DMA_RING32>(p, s);
     }
     if (shape == 16) {
         *name = REGTILE_DMA_NAME("bf16", "16x16x32");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, false>(p, s);
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, false, DMA_RING16>(p, s);
     }
     *name = REGTILE_DMA_NAME("bf16", "32x32x16");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false>(p, s);
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, DMA_RING32>(p, s);
 #undef REGTILE_DMA_NAME
 }
 
