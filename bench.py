@@ -399,7 +399,7 @@ def main():
                             raise rt.RegtileError(st, rt.strerror(st))
 
                     step_l()
-                    _, kms, _ = _time(torch, step_l, max(3, args.steps // 4), 2)
+                    _, kms, _ = _time(torch, step_l, max(10, args.steps // 2), 3)
                     code = ("n", "t")[ta] + ("n", "t")[tb]
                     lay[f"{wname}_{code}"] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
                                               "TFLOP/s": round(wl.flop / (kms * 1e-3) / 1e12, 2)}

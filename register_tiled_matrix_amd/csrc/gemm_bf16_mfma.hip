@@ -88,7 +88,9 @@ __device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, in
             hi[kk] = e[2] | (e[3] << 16);
         }
     }
-    // out[j] dword d = (k = 2d in the low half, k = 2d + 1 in the high half) of row j
+    // out[j] dword d = (k = 2d in the low half, k = 2d + 1 in the high half) of row j (written
+    // out here rather than through mfma::transpose_4x8: the shared helper compiles to a
+    // different, measurably slower schedule in this kernel)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t *src = j < 2 ? lo : hi;
@@ -321,6 +323,10 @@ const char *const kLayoutNames[2][2][3][2] = {
 
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16) {
+    if (!p.ta && !p.tb && shape == 32) {  // both row-major: the LDS-DMA kernel with B rows
+        const hipError_t e = launch_bf16_mfma_dma_nn(p, s, name, f16);
+        if (e != hipErrorNotSupported) return e;
+    }
     if (p.ta || !p.tb) {  // not the native K-contiguous pair
         const bool vec = (p.ta ? (p.ldb % 8) == 0 && aligned16(p.B) : (p.lda % 8) == 0 && aligned16(p.A));
         const int lay = (p.ta && p.tb) ? 0 : p.ta ? 1 : 2;  // tt: A K x M, B N x K; tn; nn

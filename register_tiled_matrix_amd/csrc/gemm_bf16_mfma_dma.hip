@@ -37,7 +37,7 @@ namespace {
 using namespace mfma;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16,
-          int RING = 2>
+          int RING = 2, bool B_ROW = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     static_assert(PER_SLAB < 64, "vmcnt range");
     constexpr int STAGES = 2;
     static_assert(RING == 2 || (RING == 5 && A_SLOTS == B_SLOTS), "two stages, or a ring of five halves");
+    static_assert(!B_ROW || RING == 5, "row-major B goes through the ring");
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
 
@@ -111,6 +112,48 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         dma16_buf(b_rsrc, b_voff[q & 1], (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
     };
 
+    // B stored K x N row-major (B_ROW): no DMA for B. Each thread owns two 4 x 8 blocks of the
+    // slab (4 consecutive n, 8 consecutive k), reads them as 8-byte runs along n (consecutive
+    // lanes take consecutive runs of one k row), and after the half they go to is free writes
+    // them transposed (8 k per 16-byte chunk, mfma_common.h) into the swizzled slab.
+    constexpr int NT = NWAVES * 64;
+    constexpr int B_BLOCKS = B_ROW ? 2 : 1;
+    static_assert(!B_ROW || (BN / 4) * KCH == B_BLOCKS * NT, "two 4 x 8 blocks of B per thread");
+    constexpr int NBL = B_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
+    uint32_t bl[B_BLOCKS][8], bh[B_BLOCKS][8];
+    int brow_n[B_BLOCKS], brow_kc[B_BLOCKS];
+    const uint16_t *brow_src[B_BLOCKS];
+#pragma unroll
+    for (int i = 0; i < B_BLOCKS; ++i) {
+        const int b = tid + NT * i;
+        brow_n[i] = (b % (BN / 4)) * 4;
+        brow_kc[i] = b / (BN / 4);
+        brow_src[i] = B + (int64_t)(brow_kc[i] * 8) * ldb + n0 + brow_n[i];
+    }
+    auto load_brow = [&](int slab) {
+        const int64_t k0 = (int64_t)min(slab, K / BK - 1) * BK;
+#pragma unroll
+        for (int i = 0; i < B_BLOCKS; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(brow_src[i] + (k0 + kk) * ldb);
+                bl[i][kk] = v.x;
+                bh[i][kk] = v.y;
+            }
+    };
+    auto write_brow = [&](uint4 *dst) {
+#pragma unroll
+        for (int i = 0; i < B_BLOCKS; ++i) {
+            uint4 out[4];
+            transpose_4x8(bl[i], bh[i], out);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = brow_n[i] + j;
+                dst[row * KCH + (brow_kc[i] ^ slab_key<KCH, MF>(row))] = out[j];
+            }
+        }
+    };
+
     typename F::acc_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -155,7 +198,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int NMFMA = MI * NI;
     constexpr int NREAD = MI + NI;
     constexpr int NWIN = KSTEPS - 1 < WINDOWS ? KSTEPS - 1 : WINDOWS;
-    constexpr int DMA_PER_WIN = (PER_SLAB + NWIN - 1) / NWIN;
+    constexpr int PER_SET = B_ROW ? JA : PER_SLAB;  // DMA instructions per wave and slab
+    constexpr int DMA_PER_WIN = (PER_SET + NWIN - 1) / NWIN;
     static_assert(KSTEPS % 2 == 0 && NWIN >= 1, "even number of k steps per slab");
     static_assert(NREAD <= NMFMA && DMA_PER_WIN <= NMFMA, "one extra instruction per MFMA slot");
 
@@ -170,7 +214,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         }
     };
     auto dmas_in = [](int win) {
-        const int left = PER_SLAB - win * DMA_PER_WIN;
+        const int left = PER_SET - win * DMA_PER_WIN;
         return left <= 0 ? 0 : (left < DMA_PER_WIN ? left : DMA_PER_WIN);
     };
     // MFMAs of buffer cb; every MFMA is followed by at most one fragment read or one DMA.
@@ -191,6 +235,37 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 --r_left;
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The same MFMAs with several kinds of other instructions spread evenly over the MFMA
+    // slots: vector-memory loads, LDS reads, VALU (the B transposes) and LDS writes (at most
+    // 2, 2, 4 and 2 per slot).
+    auto mfma_spread = [&](int cb, int reads, int vmem, int valu, int dsw) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+#pragma unroll
+        for (int g = 0; g < NMFMA; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            const int nv = ((g + 1) * vmem) / NMFMA - (g * vmem) / NMFMA;
+            const int nr = ((g + 1) * reads) / NMFMA - (g * reads) / NMFMA;
+            const int na = ((g + 1) * valu) / NMFMA - (g * valu) / NMFMA;
+            const int nw = ((g + 1) * dsw) / NMFMA - (g * dsw) / NMFMA;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (t < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (t < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (t < na) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (t < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -252,10 +327,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
         for (int d = 0; d < DMA_PER_WIN; ++d) {
             const int q = win * DMA_PER_WIN + d;  // B instructions first, then A
-            if (q < JB)
+            if constexpr (B_ROW) {  // B arrives as rows through registers
+                if (q < JA) dma_a(q, ka, smem + h_a * A_SLOTS);
+            } else if (q < JB) {
                 dma_b(q, kb, smem + h_b * A_SLOTS);
-            else if (q < PER_SLAB)
+            } else if (q < PER_SLAB) {
                 dma_a(q - JB, ka, smem + h_a * A_SLOTS);
+            }
         }
     };
     auto wrap5 = [](int h) { return h >= 5 ? h - 5 : h; };
@@ -302,7 +380,71 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             ha = wrap5(ha + 2);
         }
     };
-    if constexpr (RING == 5) {
+    // Ring with B row-major (B_ROW): in k step 2 of slab s a wave writes the B rows of slab s+1
+    // (read into registers one slab earlier), transposed, into their half (freed by slab s-1's
+    // barrier), then reads slab s+2's rows into the same registers: four k steps to land. A
+    // keeps its DMA and its early half. The vector-memory order per wave is ... rows (s+1),
+    // A (s+2), rows (s+2), A (s+3) ..., so waiting for the rows of slab s+1 leaves JA
+    // operations in flight, and the barrier needs no vector-memory wait at all (A of slab s+1
+    // precedes those rows).
+    auto ring_loop_brow = [&](auto shift_tag) {
+        constexpr int SH = decltype(shift_tag)::value;
+        static_assert(SH + NWIN <= KSTEPS && KSTEPS >= 3, "k step 2 carries the B rows");
+        constexpr int NVALU_T = B_BLOCKS * 16;  // dword selects of the transposes
+        load_brow(0);
+#pragma unroll
+        for (int q = 0; q < JA; ++q) dma_a(q, 0, smem);
+#pragma unroll
+        for (int q = 0; q < JA; ++q) dma_a(q, min(1, nslabs - 1) * BK, smem + 2 * A_SLOTS);
+        wait_vmcnt<2 * JA>();  // rows of slab 0
+        write_brow(smem + A_SLOTS);
+        load_brow(1);
+        if (SH == 0) ring_window(0, 1, 3, 2, 4);  // A of slab 2 (the B part is rows)
+        wait_vmcnt<JA + NBL + (SH == 0 ? JA : 0)>();  // A of slab 0
+        wait_lgkmcnt0();
+        lds_barrier();
+        read_frags(smem, smem + A_SLOTS, 0, 0);
+        int ha = 0;
+        for (int s = 0; s < nslabs; ++s) {
+            const int hb = wrap5(ha + 1), hna = wrap5(ha + 2), hnb = wrap5(ha + 3), hfa = wrap5(ha + 4);
+            const uint4 *sa = smem + ha * A_SLOTS, *sb = smem + hb * A_SLOTS;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const int cb = kk & 1;
+                wait_lgkmcnt0();
+                if (kk + 1 < KSTEPS) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_frags(sa, sb, kk + 1, cb ^ 1);
+                    const int win = kk + 1 - SH;
+                    const bool has = win >= 0 && win < NWIN;
+                    if (has) ring_window(win, s + 1, hnb, s + 2, hfa);
+                    const int dmas = has ? dmas_in(win) : 0;
+                    if (kk == 2) {
+                        // one register buffer: slab s+1's rows go to LDS before the same
+                        // registers take slab s+2's
+                        wait_vmcnt<JA>();  // rows of slab s+1 (only A of slab s+2 after them)
+                        write_brow(smem + hnb * A_SLOTS);
+                        load_brow(s + 2);
+                        mfma_spread(cb, NREAD, dmas + NBL, NVALU_T, B_BLOCKS * 4);
+                    } else {
+                        mfma_woven(cb, NREAD, dmas);
+                    }
+                } else {
+                    lds_barrier();  // slab s+1 published (its rows were written and waited for)
+                    read_frags(smem + hna * A_SLOTS, smem + hnb * A_SLOTS, 0, cb ^ 1);
+                    if (SH == 0) ring_window(0, s + 2, ha, s + 3, hb);
+                    mfma_woven(cb, NREAD, SH == 0 ? dmas_in(0) : 0);
+                }
+            }
+            ha = wrap5(ha + 2);
+        }
+    };
+    if constexpr (RING == 5 && B_ROW) {
+        if (STAGGER && wave >= NWAVES / 2)
+            ring_loop_brow(std::integral_constant<int, STAGGER ? 1 : 0>{});
+        else
+            ring_loop_brow(std::integral_constant<int, 0>{});
+    } else if constexpr (RING == 5) {
         if (STAGGER && wave >= NWAVES / 2)
             ring_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
         else
@@ -349,10 +491,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING>
+template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING,
+          bool B_ROW = false>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, B_ROW>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -416,6 +559,30 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
     *name = REGTILE_DMA_NAME("bf16", "32x32x16");
     return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, DMA_RING32>(p, s);
 #undef REGTILE_DMA_NAME
+}
+
+// Both operands row-major (B stored K x N): A over LDS DMA, B as 8-byte row runs through
+// registers, transposed into the slab. Returns hipErrorNotSupported (launching nothing) unless
+// the problem is made of full tiles, A rows are 16-byte aligned and K-contiguous within 32-bit
+// tile offsets, and B rows allow 8-byte loads.
+hipError_t launch_bf16_mfma_dma_nn(const Problem &p, hipStream_t s, const char **name, bool f16) {
+    const bool ok = !p.ta && !p.tb && DMA_RING32 == 5 && p.M % DMA_BM == 0 && p.N % DMA_BN == 0 &&
+                    p.K % DMA_BK == 0 && p.K > 0 && p.lda % 8 == 0 && aligned16(p.A) &&
+                    p.ldb % 4 == 0 && aligned8(p.B) &&
+                    (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
+                    (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
+                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128;
+    if (!ok) return hipErrorNotSupported;
+#define REGTILE_DMA_NN_NAME(elt)                                                                   \
+    elt "_mfma32x32x16_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)   \
+        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_nn"
+    if (f16) {
+        *name = REGTILE_DMA_NN_NAME("f16");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, true>(p, s);
+    }
+    *name = REGTILE_DMA_NN_NAME("bf16");
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, true>(p, s);
+#undef REGTILE_DMA_NN_NAME
 }
 
 }  // namespace regtile

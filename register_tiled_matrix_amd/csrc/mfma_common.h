@@ -97,6 +97,23 @@ __device__ __forceinline__ void store_f32_buf(rsrc_t r, uint32_t voff, uint32_t 
 #endif
 }
 
+// Transpose of a 4 x 8 block of 16-bit values held as 8 runs along the first index: lo[kk] has
+// rows 0 and 1 at column kk (row 0 in the low half), hi[kk] rows 2 and 3. out[j] receives row
+// j as 8 consecutive columns (dword d = columns 2d, 2d + 1), the form of one 16-byte slab chunk
+// of a K-contiguous slab when rows are M (or N) indices and columns are k.
+__device__ __forceinline__ void transpose_4x8(const uint32_t lo[8], const uint32_t hi[8], uint4 out[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t *src = j < 2 ? lo : hi;
+        uint32_t d[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            d[q] = (j & 1) ? (src[2 * q] >> 16) | (src[2 * q + 1] & 0xFFFF0000u)
+                           : (src[2 * q] & 0xFFFFu) | (src[2 * q + 1] << 16);
+        out[j] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+
 // s_waitcnt lgkmcnt(0) only (LDS reads; LDS DMA is counted by vmcnt, not lgkmcnt).
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 

@@ -147,3 +147,28 @@ def test_16bit_gathered_layouts_large_ragged(shape, ta, tb, dtype):
     got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA)
     assert "256x256x64_w2x4" in name, name
     assert_parity_sampled(inp, got, f"{dtype} layout ({ta},{tb}) {shape} ({name})", n_random=50000)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dist", ["integer", "normal"])
+def test_16bit_row_major_b_on_the_dma_kernel(dtype, dist):
+    # both operands row-major on full tiles (128 of 256x256): A over LDS DMA, B as row runs
+    # transposed in registers into the same slabs; integer inputs must match bitwise
+    M, N, K = 4096, 2048, 320
+    if dist == "integer":
+        rng = np.random.Generator(np.random.PCG64(123 + (dtype == "f16")))
+        to_bits = gi.f32_to_bf16_bits if dtype == "bf16" else gi.f32_to_f16_bits
+        A = to_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+        Bt = to_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+        inp = gi.GemmInputs(M, N, K, 1.0, 0.0, dtype, True, A, Bt, None)
+    else:
+        inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.0, beta=0.0, seed=321)
+    announce(f"{dtype} row-major B DMA path {dist}")
+    got, name = _run(inp, 0, 0, rt.ALGO_BF16_MFMA)
+    assert "_dma_" in name and name.endswith("_nn"), name
+    if dist == "integer":
+        I, J = sample_positions(M, N, n_random=30000, seed=8)
+        ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+        assert np.array_equal(got[I, J].astype(np.float64), ref), name
+    else:
+        assert_parity_sampled(inp, got, f"{dtype} row-major B ({name})", n_random=50000)
