@@ -323,8 +323,8 @@ const char *const kLayoutNames[2][2][3][2] = {
 
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16) {
-    if (!p.ta && !p.tb && shape == 32) {  // both row-major: the LDS-DMA kernel with B rows
-        const hipError_t e = launch_bf16_mfma_dma_nn(p, s, name, f16);
+    if (p.ta == p.tb && shape == 32) {  // "n n" or "t t": the LDS-DMA kernel with one row operand
+        const hipError_t e = launch_bf16_mfma_dma_rows(p, s, name, f16);
         if (e != hipErrorNotSupported) return e;
     }
     if (p.ta || !p.tb) {  // not the native K-contiguous pair

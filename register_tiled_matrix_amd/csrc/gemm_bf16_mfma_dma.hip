@@ -37,7 +37,7 @@ namespace {
 using namespace mfma;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16,
-          int RING = 2, bool B_ROW = false>
+          int RING = 2, int ROWS = 0>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -56,7 +56,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     static_assert(PER_SLAB < 64, "vmcnt range");
     constexpr int STAGES = 2;
     static_assert(RING == 2 || (RING == 5 && A_SLOTS == B_SLOTS), "two stages, or a ring of five halves");
-    static_assert(!B_ROW || RING == 5, "row-major B goes through the ring");
+    // ROWS: 0 both operands K-contiguous over DMA; 1 B stored K x N (N-contiguous); 2 A stored
+    // K x M (M-contiguous). The M/N-contiguous operand arrives as rows through registers.
+    constexpr bool A_ROW = ROWS == 2, ANY_ROW = ROWS != 0;
+    static_assert(ROWS >= 0 && ROWS <= 2 && (!ANY_ROW || RING == 5), "row operands go through the ring");
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
 
@@ -111,24 +114,34 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     auto dma_b = [&](int q, int k0, uint4 *dst) {
         dma16_buf(b_rsrc, b_voff[q & 1], (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
     };
+    // the operand that keeps its DMA when the other arrives as rows
+    auto dma_e = [&](int q, int k0, uint4 *dst) {
+        if constexpr (A_ROW)
+            dma_b(q, k0, dst);
+        else
+            dma_a(q, k0, dst);
+    };
 
-    // B stored K x N row-major (B_ROW): no DMA for B. Each thread owns two 4 x 8 blocks of the
-    // slab (4 consecutive n, 8 consecutive k), reads them as 8-byte runs along n (consecutive
+    // The row operand (ANY_ROW) has no DMA. Each thread owns two 4 x 8 blocks of its slab (4
+    // consecutive m or n, 8 consecutive k), reads them as 8-byte runs along m or n (consecutive
     // lanes take consecutive runs of one k row), and after the half they go to is free writes
     // them transposed (8 k per 16-byte chunk, mfma_common.h) into the swizzled slab.
     constexpr int NT = NWAVES * 64;
-    constexpr int B_BLOCKS = B_ROW ? 2 : 1;
-    static_assert(!B_ROW || (BN / 4) * KCH == B_BLOCKS * NT, "two 4 x 8 blocks of B per thread");
-    constexpr int NBL = B_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
+    constexpr int RLEN = A_ROW ? BM : BN;  // slab rows of the row operand
+    constexpr int B_BLOCKS = ANY_ROW ? 2 : 1;
+    static_assert(!ANY_ROW || (RLEN / 4) * KCH == B_BLOCKS * NT, "two 4 x 8 blocks per thread");
+    constexpr int NBL = ANY_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
+    const uint16_t *const rsrc_base = A_ROW ? A + m0 : B + n0;
+    const int64_t ld_row = A_ROW ? lda : ldb;
     uint32_t bl[B_BLOCKS][8], bh[B_BLOCKS][8];
     int brow_n[B_BLOCKS], brow_kc[B_BLOCKS];
     const uint16_t *brow_src[B_BLOCKS];
 #pragma unroll
     for (int i = 0; i < B_BLOCKS; ++i) {
         const int b = tid + NT * i;
-        brow_n[i] = (b % (BN / 4)) * 4;
-        brow_kc[i] = b / (BN / 4);
-        brow_src[i] = B + (int64_t)(brow_kc[i] * 8) * ldb + n0 + brow_n[i];
+        brow_n[i] = (b % (RLEN / 4)) * 4;
+        brow_kc[i] = b / (RLEN / 4);
+        brow_src[i] = rsrc_base + (int64_t)(brow_kc[i] * 8) * ld_row + brow_n[i];
     }
     auto load_brow = [&](int slab) {
         const int64_t k0 = (int64_t)min(slab, K / BK - 1) * BK;
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         for (int i = 0; i < B_BLOCKS; ++i)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(brow_src[i] + (k0 + kk) * ldb);
+                const uint2 v = *reinterpret_cast<const uint2 *>(brow_src[i] + (k0 + kk) * ld_row);
                 bl[i][kk] = v.x;
                 bh[i][kk] = v.y;
             }
@@ -198,7 +211,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int NMFMA = MI * NI;
     constexpr int NREAD = MI + NI;
     constexpr int NWIN = KSTEPS - 1 < WINDOWS ? KSTEPS - 1 : WINDOWS;
-    constexpr int PER_SET = B_ROW ? JA : PER_SLAB;  // DMA instructions per wave and slab
+    constexpr int JE = A_ROW ? JB : JA;  // DMA instructions of the early (DMA) operand
+    constexpr int PER_SET = ANY_ROW ? JE : PER_SLAB;  // DMA instructions per wave and slab
     constexpr int DMA_PER_WIN = (PER_SET + NWIN - 1) / NWIN;
     static_assert(KSTEPS % 2 == 0 && NWIN >= 1, "even number of k steps per slab");
     static_assert(NREAD <= NMFMA && DMA_PER_WIN <= NMFMA, "one extra instruction per MFMA slot");
@@ -327,8 +341,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
         for (int d = 0; d < DMA_PER_WIN; ++d) {
             const int q = win * DMA_PER_WIN + d;  // B instructions first, then A
-            if constexpr (B_ROW) {  // B arrives as rows through registers
-                if (q < JA) dma_a(q, ka, smem + h_a * A_SLOTS);
+            if constexpr (ANY_ROW) {  // only the DMA operand; the other arrives as rows
+                if (q < JE) dma_e(q, ka, smem + h_a * A_SLOTS);
             } else if (q < JB) {
                 dma_b(q, kb, smem + h_b * A_SLOTS);
             } else if (q < PER_SLAB) {
@@ -380,41 +394,47 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             ha = wrap5(ha + 2);
         }
     };
-    // Ring with B row-major (B_ROW): in k step 2 of slab s a wave writes the B rows of slab s+1
-    // (read into registers one slab earlier), transposed, into their half (freed by slab s-1's
-    // barrier), then reads slab s+2's rows into the same registers: four k steps to land. A
-    // keeps its DMA and its early half. The vector-memory order per wave is ... rows (s+1),
-    // A (s+2), rows (s+2), A (s+3) ..., so waiting for the rows of slab s+1 leaves JA
-    // operations in flight, and the barrier needs no vector-memory wait at all (A of slab s+1
-    // precedes those rows).
-    auto ring_loop_brow = [&](auto shift_tag) {
+    // Ring with a row operand (ANY_ROW): the DMA operand takes the early half of each slab
+    // ((2t) % 5), the row operand the late one ((2t + 1) % 5). In k step 2 of slab s a wave
+    // writes the rows of slab s+1 (read into registers one slab earlier), transposed, into
+    // their half (freed by slab s-1's barrier), then reads slab s+2's rows into the same
+    // registers: four k steps to land. The vector-memory order per wave is ... rows (s+1),
+    // DMA (s+2), rows (s+2), DMA (s+3) ..., so waiting for the rows of slab s+1 leaves JE
+    // operations in flight, and the barrier needs no vector-memory wait at all (the DMA of slab
+    // s+1 precedes those rows).
+    auto frags_at = [&](int h_early, int h_late, int kk, int buf) {
+        if constexpr (A_ROW)
+            read_frags(smem + h_late * A_SLOTS, smem + h_early * A_SLOTS, kk, buf);
+        else
+            read_frags(smem + h_early * A_SLOTS, smem + h_late * A_SLOTS, kk, buf);
+    };
+    auto ring_loop_rows = [&](auto shift_tag) {
         constexpr int SH = decltype(shift_tag)::value;
-        static_assert(SH + NWIN <= KSTEPS && KSTEPS >= 3, "k step 2 carries the B rows");
+        static_assert(SH + NWIN <= KSTEPS && KSTEPS >= 3, "k step 2 carries the rows");
         constexpr int NVALU_T = B_BLOCKS * 16;  // dword selects of the transposes
         load_brow(0);
 #pragma unroll
-        for (int q = 0; q < JA; ++q) dma_a(q, 0, smem);
+        for (int q = 0; q < JE; ++q) dma_e(q, 0, smem);
 #pragma unroll
-        for (int q = 0; q < JA; ++q) dma_a(q, min(1, nslabs - 1) * BK, smem + 2 * A_SLOTS);
-        wait_vmcnt<2 * JA>();  // rows of slab 0
+        for (int q = 0; q < JE; ++q) dma_e(q, min(1, nslabs - 1) * BK, smem + 2 * A_SLOTS);
+        wait_vmcnt<2 * JE>();  // rows of slab 0
         write_brow(smem + A_SLOTS);
         load_brow(1);
-        if (SH == 0) ring_window(0, 1, 3, 2, 4);  // A of slab 2 (the B part is rows)
-        wait_vmcnt<JA + NBL + (SH == 0 ? JA : 0)>();  // A of slab 0
+        if (SH == 0) ring_window(0, 1, 3, 2, 4);  // DMA operand of slab 2
+        wait_vmcnt<JE + NBL + (SH == 0 ? JE : 0)>();  // DMA operand of slab 0
         wait_lgkmcnt0();
         lds_barrier();
-        read_frags(smem, smem + A_SLOTS, 0, 0);
-        int ha = 0;
+        frags_at(0, 1, 0, 0);
+        int ha = 0;  // early half of slab s; its late half is ha + 1
         for (int s = 0; s < nslabs; ++s) {
             const int hb = wrap5(ha + 1), hna = wrap5(ha + 2), hnb = wrap5(ha + 3), hfa = wrap5(ha + 4);
-            const uint4 *sa = smem + ha * A_SLOTS, *sb = smem + hb * A_SLOTS;
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk) {
                 const int cb = kk & 1;
                 wait_lgkmcnt0();
                 if (kk + 1 < KSTEPS) {
                     __builtin_amdgcn_sched_barrier(0);
-                    read_frags(sa, sb, kk + 1, cb ^ 1);
+                    frags_at(ha, hb, kk + 1, cb ^ 1);
                     const int win = kk + 1 - SH;
                     const bool has = win >= 0 && win < NWIN;
                     if (has) ring_window(win, s + 1, hnb, s + 2, hfa);
@@ -422,7 +442,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                     if (kk == 2) {
                         // one register buffer: slab s+1's rows go to LDS before the same
                         // registers take slab s+2's
-                        wait_vmcnt<JA>();  // rows of slab s+1 (only A of slab s+2 after them)
+                        wait_vmcnt<JE>();  // rows of slab s+1 (only the DMA of slab s+2 after them)
                         write_brow(smem + hnb * A_SLOTS);
                         load_brow(s + 2);
                         mfma_spread(cb, NREAD, dmas + NBL, NVALU_T, B_BLOCKS * 4);
@@ -431,7 +451,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                     }
                 } else {
                     lds_barrier();  // slab s+1 published (its rows were written and waited for)
-                    read_frags(smem + hna * A_SLOTS, smem + hnb * A_SLOTS, 0, cb ^ 1);
+                    frags_at(hna, hnb, 0, cb ^ 1);
                     if (SH == 0) ring_window(0, s + 2, ha, s + 3, hb);
                     mfma_woven(cb, NREAD, SH == 0 ? dmas_in(0) : 0);
                 }
@@ -439,11 +459,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             ha = wrap5(ha + 2);
         }
     };
-    if constexpr (RING == 5 && B_ROW) {
+    if constexpr (RING == 5 && ANY_ROW) {
         if (STAGGER && wave >= NWAVES / 2)
-            ring_loop_brow(std::integral_constant<int, STAGGER ? 1 : 0>{});
+            ring_loop_rows(std::integral_constant<int, STAGGER ? 1 : 0>{});
         else
-            ring_loop_brow(std::integral_constant<int, 0>{});
+            ring_loop_rows(std::integral_constant<int, 0>{});
     } else if constexpr (RING == 5) {
         if (STAGGER && wave >= NWAVES / 2)
             ring_loop(std::integral_constant<int, STAGGER ? 1 : 0>{});
@@ -492,10 +512,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING,
-          bool B_ROW = false>
+          int ROWS = 0>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = p.M / BM, tiles_n = p.N / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, B_ROW>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -561,28 +581,40 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 #undef REGTILE_DMA_NAME
 }
 
-// Both operands row-major (B stored K x N): A over LDS DMA, B as 8-byte row runs through
-// registers, transposed into the slab. Returns hipErrorNotSupported (launching nothing) unless
-// the problem is made of full tiles, A rows are 16-byte aligned and K-contiguous within 32-bit
-// tile offsets, and B rows allow 8-byte loads.
-hipError_t launch_bf16_mfma_dma_nn(const Problem &p, hipStream_t s, const char **name, bool f16) {
-    const bool ok = !p.ta && !p.tb && DMA_RING32 == 5 && p.M % DMA_BM == 0 && p.N % DMA_BN == 0 &&
-                    p.K % DMA_BK == 0 && p.K > 0 && p.lda % 8 == 0 && aligned16(p.A) &&
-                    p.ldb % 4 == 0 && aligned8(p.B) &&
-                    (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
+// One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)
+// or "t t" (A stored K x M, B stored N x K). The K-contiguous operand goes over LDS DMA, the
+// other as 8-byte row runs through registers, transposed into the slab. Returns
+// hipErrorNotSupported (launching nothing) unless the problem is made of full tiles, the DMA
+// operand's rows are 16-byte aligned within 32-bit tile offsets, and the row operand allows
+// 8-byte loads.
+hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16) {
+    const bool nn = !p.ta && !p.tb, tt = p.ta && p.tb;
+    const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31))
+                           : (p.ldb % 8 == 0 && aligned16(p.B) && (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31));
+    const bool rows_ok = nn ? (p.ldb % 4 == 0 && aligned8(p.B)) : (p.lda % 4 == 0 && aligned8(p.A));
+    const bool ok = (nn || tt) && DMA_RING32 == 5 && dma_ok && rows_ok && p.M % DMA_BM == 0 &&
+                    p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
                     (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
                     (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128;
     if (!ok) return hipErrorNotSupported;
-#define REGTILE_DMA_NN_NAME(elt)                                                                   \
+#define REGTILE_DMA_ROWS_NAME(elt, lay)                                                            \
     elt "_mfma32x32x16_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)   \
-        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_nn"
-    if (f16) {
-        *name = REGTILE_DMA_NN_NAME("f16");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, true>(p, s);
+        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_" lay
+    if (nn) {
+        if (f16) {
+            *name = REGTILE_DMA_ROWS_NAME("f16", "nn");
+            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, 1>(p, s);
+        }
+        *name = REGTILE_DMA_ROWS_NAME("bf16", "nn");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, 1>(p, s);
     }
-    *name = REGTILE_DMA_NN_NAME("bf16");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, true>(p, s);
-#undef REGTILE_DMA_NN_NAME
+    if (f16) {
+        *name = REGTILE_DMA_ROWS_NAME("f16", "tt");
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, 2>(p, s);
+    }
+    *name = REGTILE_DMA_ROWS_NAME("bf16", "tt");
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, 2>(p, s);
+#undef REGTILE_DMA_ROWS_NAME
 }
 
 }  // namespace regtile

@@ -39,9 +39,9 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
 // Full aligned tiles only; return hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16);
-// Both operands row-major (A M x K, B K x N) on full aligned tiles; hipErrorNotSupported
-// without launching otherwise.
-hipError_t launch_bf16_mfma_dma_nn(const Problem &p, hipStream_t s, const char **name, bool f16);
+// "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) on full
+// aligned tiles; hipErrorNotSupported without launching otherwise.
+hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16);
 
 // Host-side launch checks.
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -151,9 +151,11 @@ def test_16bit_gathered_layouts_large_ragged(shape, ta, tb, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("dist", ["integer", "normal"])
-def test_16bit_row_major_b_on_the_dma_kernel(dtype, dist):
-    # both operands row-major on full tiles (128 of 256x256): A over LDS DMA, B as row runs
-    # transposed in registers into the same slabs; integer inputs must match bitwise
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 1)])
+def test_16bit_row_operand_on_the_dma_kernel(ta, tb, dtype, dist):
+    # "n n" (B stored K x N) and "t t" (A stored K x M) on full tiles (128 of 256x256): the
+    # K-contiguous operand over LDS DMA, the other as row runs transposed in registers into the
+    # same slabs; integer inputs must match bitwise
     M, N, K = 4096, 2048, 320
     if dist == "integer":
         rng = np.random.Generator(np.random.PCG64(123 + (dtype == "f16")))
@@ -163,12 +165,12 @@ def test_16bit_row_major_b_on_the_dma_kernel(dtype, dist):
         inp = gi.GemmInputs(M, N, K, 1.0, 0.0, dtype, True, A, Bt, None)
     else:
         inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.0, beta=0.0, seed=321)
-    announce(f"{dtype} row-major B DMA path {dist}")
-    got, name = _run(inp, 0, 0, rt.ALGO_BF16_MFMA)
-    assert "_dma_" in name and name.endswith("_nn"), name
+    announce(f"{dtype} row operand DMA path {ta}{tb} {dist}")
+    got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA)
+    assert "_dma_" in name and name.endswith("_nn" if ta == 0 else "_tt"), name
     if dist == "integer":
         I, J = sample_positions(M, N, n_random=30000, seed=8)
         ref, _ = oracle.gemm_inputs_entries(inp, I, J)
         assert np.array_equal(got[I, J].astype(np.float64), ref), name
     else:
-        assert_parity_sampled(inp, got, f"{dtype} row-major B ({name})", n_random=50000)
+        assert_parity_sampled(inp, got, f"{dtype} row operand ({ta},{tb}) ({name})", n_random=50000)
