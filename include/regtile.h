@@ -52,7 +52,7 @@ extern "C" {
 /* Kernel ladder for the fp32 entry points ("Understanding Register Tiling", the three-version
  * comparison: naive -> shared memory -> register tiling). */
 enum regtile_algo_f32 {
-    REGTILE_F32_AUTO = 0,    /* library's choice among the register-tiled kernels (3 or 5) */
+    REGTILE_F32_AUTO = 0,    /* library's choice among the register-tiled kernels (3, 4 or 5) */
     REGTILE_F32_NAIVE = 1,   /* one thread per C element, operands straight from HBM */
     REGTILE_F32_LDS = 2,     /* 32x32 LDS tiles, 1024 threads, one C element per thread */
     REGTILE_F32_REGTILE = 3, /* 128x256 LDS tiles, 256 threads, 8x16 register micro-tiles */
@@ -75,9 +75,12 @@ enum regtile_algo_bf16 {
 /*
  * gemm_f32 -- fp32 C = alpha*A*B + beta*C with fp32 FMA accumulation, on the register-tiled
  * kernel ("Understanding Register Tiling", the key loop; "寄存器Tiling跨架构解析" section 1.1):
- * 128x256 workgroup tiles of 8x16 micro-tiles, or for problems with fewer than two 128x128 tiles
- * per CU 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD (section 2.4 / 7.2 of the second
- * page: tile size against resident waves).
+ * 128x256 workgroup tiles of 8x16 micro-tiles. Problems with fewer than two 128x128 tiles per
+ * CU take smaller tiles (section 2.4 / 7.2 of the second page: tile size against resident
+ * waves): with K >= 1024 and at most two 64x64 tiles per CU, the split-K kernel (64x64 tiles
+ * of 8x8 micro-tiles, each wave a quarter of K, partials summed in a fixed order); otherwise
+ * 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD. Every kernel but split-K sums k in natural
+ * order, so its results equal the naive rung bitwise.
  *   M, N, K    (args 1-3)  sizes, >= 0
  *   alpha      (arg 4)     scale of A*B
  *   A, lda     (args 5-6)  device, row-major M x K, lda >= max(1,K); may be NULL if M*K == 0

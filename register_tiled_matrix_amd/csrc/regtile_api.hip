@@ -89,11 +89,19 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
     const char *name = "none";
     hipError_t err;
     if (algo == REGTILE_F32_AUTO) {
-        // Fewer than two 128x128 tiles per CU leaves SIMDs idle: 64x64 tiles with 4x4 micro-tiles
-        // at 4 waves per SIMD (measured ahead of the split-K kernel on the tall-skinny and
-        // ragged shapes, and bitwise equal to the naive rung).
+        // Fewer than two 128x128 tiles per CU leaves SIMDs idle. Smaller tiles restore the
+        // parallelism: with a long K, the split-K kernel (64x64 tiles, 8x8 micro-tiles, each
+        // wave a quarter of K; row-major operands only), measured about 12% ahead of 4x4
+        // micro-tiles on 16384x128x4096, whose LDS reads bound them; otherwise 64x64 tiles of
+        // 4x4 micro-tiles at 4 waves per SIMD (bitwise equal to the naive rung).
         const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-        algo = tiles < 2 * 256 ? REGTILE_F32_REGTILE_SMALL : REGTILE_F32_REGTILE;
+        const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+        if (tiles >= 2 * 256)
+            algo = REGTILE_F32_REGTILE;
+        else if (!ta && !tb && K >= 1024 && tiles64 <= 2 * 256)
+            algo = REGTILE_F32_SPLITK;
+        else
+            algo = REGTILE_F32_REGTILE_SMALL;
     }
     switch (algo) {
         case REGTILE_F32_NAIVE: err = regtile::launch_f32_naive(p, s, &name); break;

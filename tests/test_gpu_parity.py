@@ -63,7 +63,8 @@ def test_f32_tall_sampled():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
     announce("f32_tall default entry point")
     got = run(inp, torch).cpu().numpy()
-    assert "64x64x32_4x4" in rt.last_kernel()  # 128 tiles of 128x128: the small-tile kernel
+    # 128 tiles of 128x128 and a long K: the split-K kernel (64x64 tiles, 8x8 micro-tiles)
+    assert "splitk" in rt.last_kernel(), rt.last_kernel()
     assert_parity_sampled(inp, got, "f32_tall")
 
 
