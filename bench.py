@@ -9,10 +9,12 @@ kernel ladder (naive -> LDS-tiled -> register-tiled -> MFMA), each timed the sam
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-ladder] [--no-cpu]
 
-Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize() calls
-(wall clock -> ms_per_step and value), with a HIP event pair around every launch on the
-stream the library launches on (the caller's current stream) -> the average kernel
-duration used for the roofline figure. The CPU baseline times the fp64 oracle as it stands
+Timing: W untimed warm-up steps, then the timed region: K back-to-back steps between two
+torch.cuda.synchronize() calls (wall clock -> ms_per_step and value; one HIP event pair
+around the region -> back_to_back_ms_per_launch). A second pass of K launches puts a HIP
+event pair around every launch on the stream the library launches on (the caller's current
+stream) -> the average kernel duration used for the roofline figure, which is what the
+rocprofv3 kernel trace reports per dispatch. The CPU baseline times the fp64 oracle as it stands
 on a bounded row sample of the same workload, and a blocked multithreaded fp32 CPU GEMM
 (cpu_baseline/) on the whole workload.
 """
@@ -39,7 +41,9 @@ def _parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50,
+                   help="untimed launches before each timed region (after idle the GPU needs "
+                        "about 20 fp32 4096^3 or 50 bf16 8192^3 launches to reach its steady clock)")
     p.add_argument("--no-ladder", action="store_true", help="skip the naive/LDS rungs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 and fp16 8192^3 legs")
@@ -80,9 +84,31 @@ def _time(torch, fn, steps, warmup):
     return wall_ms, float(np.mean(kern)), float(np.min(kern))
 
 
+def _time_steps(torch, fn, steps, warmup):
+    """The timed region of a leg: `steps` back-to-back launches bracketed by synchronisations
+    (no per-launch events in between). Returns (wall ms per step, event ms per step from one
+    event pair around the region), then a second pass with an event pair around every launch
+    for the per-launch kernel duration: (mean, fastest) ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    region_ms = e0.elapsed_time(e1) / steps
+    _, kern = _kernel_times(torch, fn, steps, 0)
+    return wall_ms, region_ms, float(np.mean(kern)), float(np.min(kern))
+
+
 def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
-    """Every configuration through the default entry points: 5 warm-up and 30 timed launches,
-    TFLOP/s from the median event time, and the fraction of the peak that bounds it."""
+    """Every configuration through the default entry points: at least 50 warm-up launches and
+    100 ms, then 30 timed launches; TFLOP/s from the median event time, and the fraction of the
+    peak that bounds it."""
     res = {}
     names = ["f32_256", "f32_4096", "f32_ragged", "f32_tall"] + (["bf16_8192"] if with_16bit else [])
     for wname in names:
@@ -108,7 +134,14 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
 
         step()
         kname = rt.last_kernel()
-        _, kern = _kernel_times(torch, step, 30, 5)
+        # warm up for at least 50 launches and 100 ms (small problems ramp the clock slowly)
+        t_end, n = time.perf_counter() + 0.1, 0
+        while n < 50 or time.perf_counter() < t_end:
+            step()
+            n += 1
+            if n % 50 == 0:
+                torch.cuda.synchronize()
+        _, kern = _kernel_times(torch, step, 30, 0)
         med = float(np.median(kern))
         tf = wc.flop / (med * 1e-3) / 1e12
         res[wname] = {"shape": [wc.M, wc.N, wc.K], "kernel": kname, "kernel_ms_median": round(med, 4),
@@ -283,7 +316,7 @@ def main():
     step_f32()
     kernel_name = rt.last_kernel()
     torch.cuda.synchronize()
-    wall_ms, kern_ms, kern_min = _time(torch, step_f32, args.steps, args.warmup)
+    wall_ms, region_ms, kern_ms, kern_min = _time_steps(torch, step_f32, args.steps, args.warmup)
     flop = w.flop
     value = flop / (wall_ms * 1e-3) / 1e12
     achieved = flop / (kern_ms * 1e-3) / 1e12
@@ -317,6 +350,7 @@ def main():
             "kernel_ms_mean": round(kern_ms, 4),
             "kernel_ms_min": round(kern_min, 4),
             "flop_per_launch": flop,
+            "back_to_back_ms_per_launch": round(region_ms, 4),
         },
     }
 
@@ -337,7 +371,7 @@ def main():
 
         step_16()
         kname = rt.last_kernel()
-        wms, kms, kmin = _time(torch, step_16, args.steps, args.warmup)
+        wms, rms, kms, kmin = _time_steps(torch, step_16, args.steps, args.warmup)
         v = wb.flop / (wms * 1e-3) / 1e12
         a = wb.flop / (kms * 1e-3) / 1e12
         res = {
@@ -350,7 +384,8 @@ def main():
                          "traffic": _traffic(kname),
                          "algorithmic_hbm_bytes": acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes,
                          "kernel": kname, "kernel_ms_mean": round(kms, 4),
-                         "kernel_ms_min": round(kmin, 4), "flop_per_launch": wb.flop},
+                         "kernel_ms_min": round(kmin, 4), "flop_per_launch": wb.flop,
+                         "back_to_back_ms_per_launch": round(rms, 4)},
         }
 
         # the same tiles and pipeline on 16x16x32 MFMA fragments (the fragment-shape rung)

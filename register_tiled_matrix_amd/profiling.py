@@ -58,7 +58,7 @@ def _bench_cmd(*extra):
 def passes(out):
     """(name, rocprofv3 argv, seconds allowed) for every pass, in order."""
     p = [("trace", ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out, "trace"), "-o", "trace",
-                    "--output-format", "csv", "--", *_bench_cmd("--no-cpu", "--steps", "20", "--warmup", "5")], 420)]
+                    "--output-format", "csv", "--", *_bench_cmd("--no-cpu", "--steps", "20", "--warmup", "50")], 420)]
     for w in PMC_WORKLOADS:
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             p.append((f"pmc_{c}_{w}", ["rocprofv3", "--pmc", c, "-d", os.path.join(out, f"pmc_{c}_{w}"), "-o", "pmc",
