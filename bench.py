@@ -7,7 +7,7 @@ resident in HBM before the timed region. The same JSON line also carries the bf1
 MFMA paths at 8192^3 (A row-major, B column-major, N(0,1) rounded to the 16-bit type) and the
 kernel ladder (naive -> LDS-tiled -> register-tiled -> MFMA), each timed the same way.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-ladder] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-ladder] [--no-cpu]
 
 Timing: W untimed warm-up steps, then the timed region: K back-to-back steps between two
 torch.cuda.synchronize() calls (wall clock -> ms_per_step and value; one HIP event pair
