@@ -110,7 +110,7 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
     100 ms, then 30 timed launches; TFLOP/s from the median event time, and the fraction of the
     peak that bounds it."""
     res = {}
-    names = ["f32_256", "f32_4096", "f32_ragged", "f32_tall"] + (["bf16_8192"] if with_16bit else [])
+    names = ["f32_256", "f32_4096", "f32_ragged", "f32_tall", "f32_8192"] + (["bf16_8192"] if with_16bit else [])
     for wname in names:
         wc = gi.WORKLOADS[wname]
         ic = gi.workload_inputs(wc)

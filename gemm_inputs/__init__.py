@@ -61,7 +61,8 @@ class Workload:
 
 
 # The five workloads: a small correctness case, the square fp32 case, a ragged case
-# with a non-trivial epilogue, the square bf16 case (column-major B) and a tall-skinny case.
+# with a non-trivial epilogue, the square bf16 case (column-major B) and a tall-skinny case;
+# then fp16 operands at the bf16 case's shape, and the fp32 path at that shape.
 WORKLOADS = {
     "f32_256": Workload("f32_256", 256, 256, 256, "f32", "uniform", 1.0, 0.0, 1001,
                         description="fp32 256^3, U[-1,1], alpha=1, beta=0"),
@@ -77,6 +78,8 @@ WORKLOADS = {
     "f16_8192": Workload("f16_8192", 8192, 8192, 8192, "f16", "normal", 1.0, 0.0, 1006,
                          b_col_major=True,
                          description="fp16 8192^3, A row-major, B column-major, N(0,1) rounded to fp16, fp32 C"),
+    "f32_8192": Workload("f32_8192", 8192, 8192, 8192, "f32", "uniform", 1.0, 0.0, 1007,
+                         description="fp32 8192^3, U[-1,1], alpha=1, beta=0 (the fp32 path at the bf16 size)"),
 }
 
 

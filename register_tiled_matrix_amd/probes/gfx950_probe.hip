@@ -10,6 +10,10 @@
 //         the clock the SIMD ran at and the cycles one wave64 FMA took per SIMD.
 //   mfma  v_mfma_f32_32x32x16_bf16 with 8 independent accumulators per wave: the attainable
 //         matrix rate on this machine.
+//   valu_sustained  FP32 FMAs at two waves per SIMD for 30 back-to-back launches of a few ms,
+//         with constant and with random operands.
+//   mfma_sustained  the MFMA loop for 30 back-to-back launches of a few ms, with constant and with
+//         random bf16 operands: the clock the package sustains under matrix load alone.
 //   lds   one kernel per LDS address pattern (16 bytes per lane); run under
 //         `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES` for the
 //         cycles and conflict cycles per instruction.
@@ -176,6 +180,170 @@ int run_mfma() {
     return 0;
 }
 
+// Sustained matrix rate with operands like a GEMM's: every lane holds four A and four B
+// fragments of random bf16 values (random sign and mantissa, magnitudes 0.25 to 4) and
+// consecutive MFMAs take different fragments, so the matrix unit's inputs toggle as they do on
+// N(0,1) data. RAND = false keeps the constant near-1 operands of mfma_kernel. Launched 30 times
+// back to back (a few ms each) to show the clock the package settles at.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+template <bool RAND>
+__global__ __launch_bounds__(256) void mfma_sustained_kernel(float *out, uint64_t *clk, int iters) {
+    bf16x8 a[4], b[4];
+    const uint32_t lane = blockIdx.x * 256 + threadIdx.x;
+    for (int f = 0; f < 4; ++f)
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ha = mix32(lane * 64 + f * 8 + i), hb = mix32(~(lane * 64 + f * 8 + i));
+            a[f][i] = RAND ? (short)(((ha & 1u) << 15) | ((125u + ((ha >> 1) & 3u)) << 7) | ((ha >> 8) & 0x7fu))
+                           : (short)(0x3f80 + (threadIdx.x & 7));
+            b[f][i] = RAND ? (short)(((hb & 1u) << 15) | ((125u + ((hb >> 1) & 3u)) << 7) | ((hb >> 8) & 0x7fu))
+                           : (short)(0x3c00 + i);
+        }
+    f32x16 acc[8];
+    for (int j = 0; j < 8; ++j)
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+    const uint64_t t0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j >> 1) & 3], acc[j], 0, 0, 0);
+    const uint64_t t1 = clock64(), w1 = wall_clock64();
+    if ((threadIdx.x & 63) == 0) {
+        const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = w1 - w0;
+    }
+    float s = 0.0f;
+    for (int j = 0; j < 8; ++j)
+        for (int v = 0; v < 16; ++v) s += acc[j][v];
+    out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+template <bool RAND>
+int run_mfma_sustained() {
+    const int blocks = 256, iters = 10000, launches = 30;
+    float *d;
+    uint64_t *clk;
+    CHECK(hipMalloc(&d, sizeof(float) * blocks * 256));
+    CHECK(hipMalloc(&clk, sizeof(uint64_t) * 2 * 4 * blocks * launches));
+    static uint64_t h[2 * 4 * 256 * 30];
+    int wall_khz = 0;
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
+    hipEvent_t e[launches + 1];
+    for (int i = 0; i <= launches; ++i) CHECK(hipEventCreate(&e[i]));
+    CHECK(hipEventRecord(e[0]));
+    for (int i = 0; i < launches; ++i) {
+        hipLaunchKernelGGL(mfma_sustained_kernel<RAND>, dim3(blocks), dim3(256), 0, 0, d,
+                           clk + 2 * 4 * blocks * i, iters);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e[i + 1]));
+    }
+    CHECK(hipEventSynchronize(e[launches]));
+    CHECK(hipMemcpy(h, clk, sizeof(uint64_t) * 2 * 4 * blocks * launches, hipMemcpyDeviceToHost));
+    const double flop = 2.0 * 32 * 32 * 16 * 8.0 * iters * 4 * blocks;
+    for (int i = 0; i < launches; ++i) {
+        if (i != 0 && i != 1 && i != 4 && i != 9 && i != 19 && i != 29) continue;
+        float ms;
+        CHECK(hipEventElapsedTime(&ms, e[i], e[i + 1]));
+        double cyc = 0, wall = 0;
+        for (int w = 0; w < 4 * blocks; ++w) {
+            cyc += (double)h[2 * 4 * blocks * i + 2 * w];
+            wall += (double)h[2 * 4 * blocks * i + 2 * w + 1];
+        }
+        printf("| %s operands | launch %d | %.3f ms | %.2f GHz | %.0f TFLOP/s |\n",
+               RAND ? "random bf16" : "constant", i + 1, ms, cyc / (wall / (wall_khz * 1e3)) / 1e9,
+               flop / (ms * 1e-3) / 1e12);
+    }
+    return 0;
+}
+
+// Sustained FP32 FMA rate at two waves per SIMD (two 256-thread workgroups per CU), 30 launches
+// back to back. Registers are fixed as in valu_kernel so that no FMA pays a bank penalty:
+// accumulators v32..v92 (bank 0), four src0 registers in bank 1 and four src1 registers in
+// bank 3, and consecutive FMAs take different sources. RAND = false: sources 1.0 and
+// accumulators 0 (little toggling); RAND = true: random sources in [-1, 1) and accumulators.
+#define FMA_ROW(D0, D1, D2, D3, S1) \
+    FMA1(D0, "v1", S1) FMA1(D1, "v5", S1) FMA1(D2, "v9", S1) FMA1(D3, "v13", S1)
+#define FMA16_ROT                                                                          \
+    FMA_ROW("v32", "v36", "v40", "v44", "v3") FMA_ROW("v48", "v52", "v56", "v60", "v7")    \
+    FMA_ROW("v64", "v68", "v72", "v76", "v11") FMA_ROW("v80", "v84", "v88", "v92", "v15")
+#define ROT_CLOBBERS                                                                       \
+    "v1", "v3", "v5", "v7", "v9", "v11", "v13", "v15", "v32", "v36", "v40", "v44", "v48",  \
+        "v52", "v56", "v60", "v64", "v68", "v72", "v76", "v80", "v84", "v88", "v92"
+
+template <bool RAND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fma_sustained_kernel(
+    uint64_t *clk, int iters) {
+    const uint32_t lane = blockIdx.x * 256 + threadIdx.x;
+    float r[24];
+    for (int i = 0; i < 24; ++i)
+        r[i] = RAND ? (float)(int)(mix32(lane * 32 + i) >> 8) * (1.0f / 8388608.0f) - 1.0f
+                    : (i < 8 ? 1.0f : 0.0f);
+    asm volatile(
+        "v_mov_b32 v1, %0\nv_mov_b32 v5, %1\nv_mov_b32 v9, %2\nv_mov_b32 v13, %3\n"
+        "v_mov_b32 v3, %4\nv_mov_b32 v7, %5\nv_mov_b32 v11, %6\nv_mov_b32 v15, %7\n"
+        "v_mov_b32 v32, %8\nv_mov_b32 v36, %9\nv_mov_b32 v40, %10\nv_mov_b32 v44, %11\n"
+        "v_mov_b32 v48, %12\nv_mov_b32 v52, %13\nv_mov_b32 v56, %14\nv_mov_b32 v60, %15\n"
+        "v_mov_b32 v64, %16\nv_mov_b32 v68, %17\nv_mov_b32 v72, %18\nv_mov_b32 v76, %19\n"
+        "v_mov_b32 v80, %20\nv_mov_b32 v84, %21\nv_mov_b32 v88, %22\nv_mov_b32 v92, %23\n" ::"v"(r[0]),
+        "v"(r[1]), "v"(r[2]), "v"(r[3]), "v"(r[4]), "v"(r[5]), "v"(r[6]), "v"(r[7]), "v"(r[8]), "v"(r[9]),
+        "v"(r[10]), "v"(r[11]), "v"(r[12]), "v"(r[13]), "v"(r[14]), "v"(r[15]), "v"(r[16]), "v"(r[17]),
+        "v"(r[18]), "v"(r[19]), "v"(r[20]), "v"(r[21]), "v"(r[22]), "v"(r[23])
+        : ROT_CLOBBERS);
+    const uint64_t t0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) asm volatile(FMA16_ROT FMA16_ROT FMA16_ROT FMA16_ROT ::: ROT_CLOBBERS);
+    const uint64_t t1 = clock64(), w1 = wall_clock64();
+    if ((threadIdx.x & 63) == 0) {
+        const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = w1 - w0;
+    }
+}
+
+template <bool RAND>
+int run_fma_sustained() {
+    const int blocks = 512, iters = 20000, launches = 30;
+    uint64_t *clk;
+    CHECK(hipMalloc(&clk, sizeof(uint64_t) * 2 * 4 * blocks * launches));
+    static uint64_t h[2 * 4 * 512 * 30];
+    int wall_khz = 0;
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, 0));
+    hipEvent_t e[launches + 1];
+    for (int i = 0; i <= launches; ++i) CHECK(hipEventCreate(&e[i]));
+    CHECK(hipEventRecord(e[0]));
+    for (int i = 0; i < launches; ++i) {
+        hipLaunchKernelGGL(fma_sustained_kernel<RAND>, dim3(blocks), dim3(256), 0, 0,
+                           clk + 2 * 4 * blocks * i, iters);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e[i + 1]));
+    }
+    CHECK(hipEventSynchronize(e[launches]));
+    CHECK(hipMemcpy(h, clk, sizeof(uint64_t) * 2 * 4 * blocks * launches, hipMemcpyDeviceToHost));
+    const double flop = 2.0 * 64 * 64.0 * iters * 4 * blocks;
+    for (int i = 0; i < launches; ++i) {
+        if (i != 0 && i != 1 && i != 4 && i != 9 && i != 19 && i != 29) continue;
+        float ms;
+        CHECK(hipEventElapsedTime(&ms, e[i], e[i + 1]));
+        double cyc = 0, wall = 0;
+        for (int w = 0; w < 4 * blocks; ++w) {
+            cyc += (double)h[2 * 4 * blocks * i + 2 * w];
+            wall += (double)h[2 * 4 * blocks * i + 2 * w + 1];
+        }
+        const double ghz = cyc / (wall / (wall_khz * 1e3)) / 1e9;
+        printf("| fp32 FMA, %s | launch %d | %.3f ms | %.2f GHz | %.2f cycles per FMA | %.1f TFLOP/s |\n",
+               RAND ? "random operands" : "sources 1.0, accumulators from 0", i + 1, ms, ghz,
+               cyc / (4.0 * blocks) / (64.0 * iters) / 2.0, flop / (ms * 1e-3) / 1e12);
+    }
+    return 0;
+}
+
 // ---- lds ----------------------------------------------------------------------------------
 __device__ __forceinline__ int key_row7(int row, int c) { return row * 128 + ((c ^ (row & 7)) * 16); }
 __device__ __forceinline__ int key_row7_row8(int row, int c) {
@@ -287,6 +455,14 @@ int main(int argc, char **argv) {
     int rc = 0;
     if (!strcmp(what, "valu") || !strcmp(what, "all")) rc |= run_valu();
     if (!strcmp(what, "mfma") || !strcmp(what, "all")) rc |= run_mfma();
+    if (!strcmp(what, "valu_sustained") || !strcmp(what, "all")) {
+        rc |= run_fma_sustained<false>();
+        rc |= run_fma_sustained<true>();
+    }
+    if (!strcmp(what, "mfma_sustained") || !strcmp(what, "all")) {
+        rc |= run_mfma_sustained<false>();
+        rc |= run_mfma_sustained<true>();
+    }
     if (!strcmp(what, "lds")) rc |= run_lds();
     return rc;
 }

@@ -14,6 +14,7 @@ ladder (algorithm 2).
     python -m register_tiled_matrix_amd.tune ladder > ladder.jsonl   # GPU: every rung, every config
     python -m register_tiled_matrix_amd.tune probe --build none   # CPU: build the gfx950 probes
     python -m register_tiled_matrix_amd.tune probe valu           # GPU: FMA issue rate, VGPR banks
+    python -m register_tiled_matrix_amd.tune datadep              # GPU: bf16 rate against input data
 
 Correctness of each variant is checked bitwise against the naive rung of the default library:
 every fp32 rung accumulates each output with fmaf over k in natural order, so any micro-tile
@@ -248,6 +249,69 @@ def cmd_ladder(args) -> int:
     return 0
 
 
+def cmd_datadep(args) -> int:
+    """bf16 8192^3 through the default entry point with four input data sets, interleaved: the
+    clock, and so the rate, depends on how much the matrix unit's operands toggle."""
+    import numpy as np
+    import torch
+
+    import gemm_inputs as gi
+    import register_tiled_matrix_amd as rt
+
+    if not torch.cuda.is_available():
+        print("tune datadep needs a GPU", file=sys.stderr)
+        return 2
+    rt.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    w = gi.WORKLOADS["bf16_8192"]
+    inp = gi.workload_inputs(w)
+    rng = np.random.Generator(np.random.PCG64(2024))
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+    def ints():
+        return gi.f32_to_bf16_bits(rng.integers(-2, 3, size=(w.M, w.K)).astype(np.float32))
+
+    ones = np.full((w.M, w.K), 0x3F80, np.uint16)
+    same = dev(ones)
+    sets = {"N(0,1) rounded to bf16 (the bench workload)": (dev(inp.A), dev(inp.B)),
+            "integers in [-2, 2]": (dev(ints()), dev(ints())),
+            "all ones": (dev(ones), dev(ones)),
+            "all zeros": (dev(np.zeros_like(ones)), dev(np.zeros_like(ones))),
+            "all ones, A and B one 128 MB buffer": (same, same)}
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+    def launcher(A, B):
+        call = (w.M, w.N, w.K, 1.0, A.data_ptr(), w.K, B.data_ptr(), w.K, 0.0, C.data_ptr(), w.N, stream)
+        return lambda: rt.gemm_bf16_raw(*call)
+
+    fns = {k: launcher(*v) for k, v in sets.items()}
+    first = next(iter(fns.values()))
+    for _ in range(args.warmup):
+        assert first() == 0
+    times = {k: [] for k in fns}
+    for _ in range(args.rounds):
+        for k, fn in fns.items():
+            for _ in range(10):
+                assert fn() == 0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            times[k] += [a.elapsed_time(b) for a, b in ev]
+    print(f"kernel `{rt.last_kernel()}`; median of {args.rounds} interleaved rounds of {args.steps} launches "
+          f"after {args.warmup} warm-up launches", flush=True)
+    print("| A, B data | median ms | TFLOP/s |\n|---|---|---|")
+    for k, ts in times.items():
+        ms = float(np.median(ts))
+        print(f"| {k} | {ms:.4f} | {w.flop / (ms * 1e-3) / 1e12:.0f} |", flush=True)
+    return 0
+
+
 def _ladder_report(rows) -> str:
     out = ["# Kernel ladder on every configuration", "",
            "Command (repository root, one MI355X):", "", "```",
@@ -352,8 +416,12 @@ def main(argv=None) -> int:
     lad.add_argument("--warmup", type=int, default=3)
     pr = sub.add_parser("probe", help="gfx950 facts: FP32 FMA issue rate and VGPR banks, "
                                        "MFMA rate, LDS access patterns")
-    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "mfma", "lds", "none"])
+    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "none"])
     pr.add_argument("--build", action="store_true", help="recompile the probe program first")
+    dd = sub.add_parser("datadep", help="bf16 8192^3 rate against the operands' data")
+    dd.add_argument("--steps", type=int, default=20)
+    dd.add_argument("--rounds", type=int, default=4)
+    dd.add_argument("--warmup", type=int, default=80)
     rep = sub.add_parser("report")
     rep.add_argument("jsonl")
     rep.add_argument("--out", default="")
@@ -363,7 +431,7 @@ def main(argv=None) -> int:
         sys.path.insert(0, root)
     t0 = time.time()
     rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report,
-          "probe": cmd_probe}[args.cmd](args)
+          "probe": cmd_probe, "datadep": cmd_datadep}[args.cmd](args)
     print(f"# {args.cmd} done in {time.time() - t0:.1f} s", file=sys.stderr)
     return rc
 

@@ -59,6 +59,14 @@ def test_f32_4096_sampled():
     assert_parity_sampled(inp, got, "f32_4096")
 
 
+def test_f32_8192_sampled():
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_8192"])
+    announce("f32_8192 default entry point")
+    got = run(inp, torch).cpu().numpy()
+    assert rt.last_kernel().startswith("f32_regtile_128x256x16_8x16"), rt.last_kernel()
+    assert_parity_sampled(inp, got, "f32_8192")
+
+
 def test_f32_tall_sampled():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
     announce("f32_tall default entry point")

@@ -52,7 +52,9 @@ def test_workload_table():
     assert (t.M, t.N, t.K) == (16384, 128, 4096)
     h = w["f16_8192"]
     assert h.dtype == "f16" and h.b_col_major and (h.M, h.N, h.K) == (8192, 8192, 8192)
-    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005, 1006]
+    e = w["f32_8192"]
+    assert e.dtype == "f32" and not e.b_col_major and (e.M, e.N, e.K) == (8192, 8192, 8192)
+    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005, 1006, 1007]
 
 
 def test_determinism_and_layout():
