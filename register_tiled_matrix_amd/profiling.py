@@ -129,6 +129,38 @@ def _cmd_block(cmds):
     return ["Commands (repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```", *cmds, "```", ""]
 
 
+LDS_PER_CU = 160 * 1024
+
+
+def _resource_rows(trace_csv):
+    """Per-kernel resources as the kernel trace records them for each dispatch, and the waves
+    per SIMD they allow. rocprofv3's VGPR_Count on gfx950 is the descriptor's granulated
+    register count times 4, half the unified (VGPR + AGPR) registers allocated in granules of 8:
+    it reads 116 for a kernel of 228 VGPRs (232 allocated) and 256 for 256 VGPRs + 256 AGPRs."""
+    seen = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if "regtile::" in r["Kernel_Name"] and r["Kernel_Name"] not in seen:
+                seen[r["Kernel_Name"]] = r
+    out = ["", "Resources per dispatch as the same trace records them (LDS bytes per workgroup, scratch "
+                "bytes per lane, `VGPR_Count` as rocprofv3 reports it; allocated registers = 2 x that, "
+                "see the note in `profiling.py`). Waves per SIMD = min(512 / allocated registers, "
+                "workgroups per CU that fit the 160 KiB LDS x waves per workgroup / 4).", "",
+           "| kernel | workgroup | LDS bytes | scratch | VGPR_Count | allocated registers | waves per SIMD |",
+           "|---|---|---|---|---|---|---|"]
+    for name, r in seen.items():
+        lds, vg, wg = int(r["LDS_Block_Size"]), int(r["VGPR_Count"]), int(r["Workgroup_Size_X"])
+        alloc = 2 * vg
+        by_regs = min(8, 512 // max(alloc, 1))
+        wpw = max(1, wg // 64)
+        by_lds = (LDS_PER_CU // lds) * wpw / 4 if lds else 8
+        waves = min(by_regs, by_lds)
+        short = name.replace("void ", "").replace("regtile::(anonymous namespace)::", "").replace("regtile::", "")
+        short = short.split("(int")[0]
+        out.append(f"| `{short}` | {wg} | {lds} | {r['Scratch_Size']} | {vg} | {alloc} | {waves:g} |")
+    return out
+
+
 def summarize_trace(prof, out_md):
     with open(os.path.join(prof, "trace", "trace_kernel_stats.csv")) as f:
         rows = list(csv.DictReader(f))
@@ -138,6 +170,7 @@ def summarize_trace(prof, out_md):
     for r in rows:
         lines.append(f"| `{r['Name'][:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} % |")
+    lines += _resource_rows(os.path.join(prof, "trace", "trace_kernel_trace.csv"))
     bench_line = None
     with open(os.path.join(prof, "trace.out")) as f:
         for line in f:
