@@ -275,7 +275,9 @@ def cmd_datadep(args) -> int:
 
     ones = np.full((w.M, w.K), 0x3F80, np.uint16)
     same = dev(ones)
-    sets = {"N(0,1) rounded to bf16 (the bench workload)": (dev(inp.A), dev(inp.B)),
+    a_dev = dev(inp.A)
+    sets = {"N(0,1) rounded to bf16 (the bench workload)": (a_dev, dev(inp.B)),
+            "N(0,1), A and B one 128 MB buffer": (a_dev, a_dev),
             "integers in [-2, 2]": (dev(ints()), dev(ints())),
             "all ones": (dev(ones), dev(ones)),
             "all zeros": (dev(np.zeros_like(ones)), dev(np.zeros_like(ones))),
