@@ -24,6 +24,7 @@ import collections
 import hashlib
 import json
 import os
+import statistics
 import subprocess
 import sys
 import time
@@ -166,9 +167,19 @@ def summarize_trace(prof, out_md):
         rows = list(csv.DictReader(f))
     lines = ["# Kernel trace: fp32 4096^3 and bf16 8192^3 bench run (rocprofv3 --kernel-trace --stats)", ""]
     lines += _cmd_block([_display(passes(prof)[0][1], prof)])
-    lines += ["| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    durs = collections.defaultdict(list)
+    with open(os.path.join(prof, "trace", "trace_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    med = {k: statistics.median(v) for k, v in durs.items()}
+    lines += ["The average includes the warm-up launches and the first launches after idle gaps, which run "
+              "at a lower clock; the median is over the same dispatches.", "",
+              "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
+              "|---|---|---|---|---|---|---|"]
     for r in rows:
+        m = med.get(r["Name"])
         lines.append(f"| `{r['Name'][:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{'-' if m is None else f'{m:.1f}'} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} % |")
     lines += _resource_rows(os.path.join(prof, "trace", "trace_kernel_trace.csv"))
     bench_line = None
@@ -178,13 +189,15 @@ def summarize_trace(prof, out_md):
                 bench_line = json.loads(line)
     if bench_line:
         lines += ["", "The same run's bench line (HIP events around each launch on the launch stream):", ""]
-        r = bench_line["roofline"]
-        lines.append(f"- fp32 4096^3 `{r['kernel']}`: event mean {r['kernel_ms_mean'] * 1e3:.1f} us, "
-                     f"achieved {r['achieved']} TFLOP/s")
+        def agree(label, r, sub):
+            m = [v for k, v in med.items() if sub in k]
+            tail = f"; trace median {m[0]:.1f} us ({(r['kernel_ms_mean'] * 1e3 / m[0] - 1) * 100:+.1f}%)" if m else ""
+            lines.append(f"- {label} `{r['kernel']}`: event mean {r['kernel_ms_mean'] * 1e3:.1f} us, "
+                         f"achieved {r['achieved']} TFLOP/s{tail}")
+
+        agree("fp32 4096^3", bench_line["roofline"], KERNELS["f32_4096"][1] + ", false, false, false")
         if "bf16_8192" in bench_line:
-            r2 = bench_line["bf16_8192"]["roofline"]
-            lines.append(f"- bf16 8192^3 `{r2['kernel']}`: event mean {r2['kernel_ms_mean'] * 1e3:.1f} us, "
-                         f"achieved {r2['achieved']} TFLOP/s")
+            agree("bf16 8192^3", bench_line["bf16_8192"]["roofline"], KERNELS["bf16_8192"][1] + ", 1, 1, false, 5, 0>")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
