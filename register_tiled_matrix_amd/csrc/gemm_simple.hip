@@ -57,9 +57,12 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
                                                     const T *__restrict__ A, int64_t lda,
                                                     const T *__restrict__ B, int64_t ldb,
                                                     float beta, float *__restrict__ C,
-                                                    int64_t ldc) {
-    const int col = blockIdx.x * 64 + (threadIdx.x & 63);
-    const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+                                                    int64_t ldc, int col_blocks) {
+    // one-dimensional grid (no 65536 limit on the row blocks): block b covers rows
+    // 4 * (b / col_blocks) .. +3 and columns 64 * (b % col_blocks) .. +63
+    const int by = blockIdx.x / col_blocks, bx = blockIdx.x - by * col_blocks;
+    const int col = bx * 64 + (threadIdx.x & 63);
+    const int row = by * 4 + (threadIdx.x >> 6);
     if (row >= M || col >= N) return;
     const T *a = TA ? A + row : A + (int64_t)row * lda;
     const int64_t a_step = TA ? lda : 1;
@@ -74,20 +77,23 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
 
 template <typename T>
 hipError_t launch_naive(const Problem &p, hipStream_t s) {
-    dim3 grid((p.N + 63) / 64, (p.M + 3) / 4);
+    const int col_blocks = (p.N + 63) / 64;
+    const int64_t blocks = (int64_t)col_blocks * ((p.M + 3) / 4);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
     const T *A = (const T *)p.A, *B = (const T *)p.B;
     if (p.ta && p.tb)
         hipLaunchKernelGGL((naive_kernel<T, true, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc, col_blocks);
     else if (p.ta)
         hipLaunchKernelGGL((naive_kernel<T, true, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc, col_blocks);
     else if (p.tb)
         hipLaunchKernelGGL((naive_kernel<T, false, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc, col_blocks);
     else
         hipLaunchKernelGGL((naive_kernel<T, false, false>), grid, dim3(256), 0, s, p.M, p.N, p.K,
-                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc);
+                           p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc, col_blocks);
     return hipGetLastError();
 }
 
@@ -111,12 +117,14 @@ __global__ __launch_bounds__(1024) void f32_lds_kernel(int M, int N, int K, floa
                                                        const float *__restrict__ A, int64_t lda,
                                                        const float *__restrict__ B, int64_t ldb,
                                                        float beta, float *__restrict__ C,
-                                                       int64_t ldc) {
+                                                       int64_t ldc, int col_blocks) {
     __shared__ float sA[LDS_TILE][LDS_TILE + 1];
     __shared__ float sB[LDS_TILE][LDS_TILE];
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-    const int row = blockIdx.y * LDS_TILE + ty;
-    const int col = blockIdx.x * LDS_TILE + tx;
+    // one-dimensional grid: block b is tile (b / col_blocks, b % col_blocks)
+    const int by = blockIdx.x / col_blocks, bx = blockIdx.x - by * col_blocks;
+    const int row = by * LDS_TILE + ty;
+    const int col = bx * LDS_TILE + tx;
     float acc = 0.0f;
     for (int k0 = 0; k0 < K; k0 += LDS_TILE) {
         sA[ty][tx] = (row < M && k0 + tx < K) ? A[(int64_t)row * lda + k0 + tx] : 0.0f;
@@ -138,10 +146,12 @@ __global__ __launch_bounds__(1024) void f32_lds_kernel(int M, int N, int K, floa
 }
 
 hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name) {
-    dim3 grid((p.N + LDS_TILE - 1) / LDS_TILE, (p.M + LDS_TILE - 1) / LDS_TILE);
-    hipLaunchKernelGGL(f32_lds_kernel, grid, dim3(LDS_TILE * LDS_TILE), 0, s, p.M, p.N, p.K,
-                       p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb, p.beta,
-                       p.C, p.ldc);
+    const int col_blocks = (p.N + LDS_TILE - 1) / LDS_TILE;
+    const int64_t blocks = (int64_t)col_blocks * ((p.M + LDS_TILE - 1) / LDS_TILE);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(f32_lds_kernel, dim3((unsigned)blocks), dim3(LDS_TILE * LDS_TILE), 0, s, p.M,
+                       p.N, p.K, p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb,
+                       p.beta, p.C, p.ldc, col_blocks);
     *name = "f32_lds_32x32";
     return hipGetLastError();
 }
