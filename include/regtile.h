@@ -56,8 +56,9 @@ enum regtile_algo_f32 {
     REGTILE_F32_NAIVE = 1,   /* one thread per C element, operands straight from HBM */
     REGTILE_F32_LDS = 2,     /* 32x32 LDS tiles, 1024 threads, one C element per thread */
     REGTILE_F32_REGTILE = 3, /* 128x256 LDS tiles, 256 threads, 8x16 register micro-tiles */
-    REGTILE_F32_SPLITK = 4,  /* 64x64 tiles, each of 4 waves an 8x8-micro-tiled quarter of K,
-                                partials summed in fixed order (shapes with few tiles) */
+    REGTILE_F32_SPLITK = 4,  /* K split over the waves of a workgroup, partials summed in a
+                                fixed order (shapes with few tiles): 64x128 tiles of 8 waves
+                                with 8x16 micro-tiles, or 64x64 tiles of 4 waves with 8x8 */
     REGTILE_F32_REGTILE_SMALL = 5 /* 64x64 tiles, 256 threads, 4x4 register micro-tiles, 4 waves
                                      per SIMD (shapes with few 128x256 tiles) */
 };
@@ -75,12 +76,13 @@ enum regtile_algo_bf16 {
 /*
  * gemm_f32 -- fp32 C = alpha*A*B + beta*C with fp32 FMA accumulation, on the register-tiled
  * kernel ("Understanding Register Tiling", the key loop; "寄存器Tiling跨架构解析" section 1.1):
- * 128x256 workgroup tiles of 8x16 micro-tiles. Problems with fewer than two 128x128 tiles per
- * CU take smaller tiles (section 2.4 / 7.2 of the second page: tile size against resident
- * waves): with K >= 1024 and at most two 64x64 tiles per CU, the split-K kernel (64x64 tiles
- * of 8x8 micro-tiles, each wave a quarter of K, partials summed in a fixed order); otherwise
- * 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD. Every kernel but split-K sums k in natural
- * order, so its results equal the naive rung bitwise.
+ * 128x256 workgroup tiles of 8x16 micro-tiles. Problems with fewer than 384 such tiles (1.5
+ * per CU) take smaller tiles (section 2.4 / 7.2 of the second page: tile size against resident
+ * waves): with K >= 1024, or K >= 384 and fewer than four 64x64 tiles per CU, the split-K
+ * kernel (K split over the waves of a workgroup, 64x128 tiles of 8x16 or 64x64 tiles of 8x8
+ * micro-tiles, partials summed in a fixed order); otherwise 64x64 tiles of 4x4 micro-tiles at 4
+ * waves per SIMD. Every kernel but split-K sums k in natural order, so its results equal the
+ * naive rung bitwise; split-K's are deterministic but summed in another order.
  *   M, N, K    (args 1-3)  sizes, >= 0
  *   alpha      (arg 4)     scale of A*B
  *   A, lda     (args 5-6)  device, row-major M x K, lda >= max(1,K); may be NULL if M*K == 0
@@ -144,9 +146,10 @@ int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint
  *                    1: B stored N x K row-major (column-major K x N), ldb >= max(1,K)
  *   the rest as gemm_f32 / gemm_bf16 / gemm_f16 at positions 4-15; -2 / -3 for a flag other
  *   than 0 or 1. gemm_f32 is (AUTO, 0, 0) and gemm_bf16 / gemm_f16 are (AUTO, 0, 1).
- * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit); only
- * the 16-bit (0, 1) pair takes the LDS-DMA kernel, the others gather the M- or N-contiguous
- * operand into K-contiguous LDS slabs with scalar loads.
+ * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit). On full
+ * aligned tiles the 16-bit LDS-DMA kernel takes (0, 1), and (0, 0) / (1, 1) with the M- or
+ * N-contiguous operand staged through registers; (1, 0) and edge tiles gather M- or
+ * N-contiguous operands into K-contiguous LDS slabs with 8-byte loads.
  */
 int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
                         const float *A, int lda, const float *B, int ldb, float beta, float *C,

@@ -1,38 +1,59 @@
-// gemm_f32_splitk.hip -- the fp32 register-tiled kernel for problems with few output tiles
+// gemm_f32_splitk.hip -- the fp32 register-tiled kernels for problems with few output tiles
 // (tall-skinny or small M, N): split-K inside the workgroup.
 //
 // With 128x128 tiles a 16384 x 128 output is only 128 workgroups for 256 CUs, half a wave per
-// SIMD. Here a workgroup owns a 64x64 tile and each of its four waves accumulates that whole
-// tile over its own quarter of K, with the same register micro-tile as the square kernel
-// ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA[8],
-// regB[8], 64 FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
-// tile size against the number of resident waves). The four partial tiles are then summed
-// through LDS in a fixed order (wave 0 + wave 1 + wave 2 + wave 3), so results are
-// deterministic; the summation order differs from the square kernel's single k sweep.
+// SIMD. Here a workgroup owns a smaller tile and each of its NW waves accumulates that whole
+// tile over its own share of K, with the register micro-tile of the square kernel
+// ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA / regB per
+// k, TM x TN FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
+// tile size against the number of resident waves). Two shapes:
+//   * 64x64 tile, 4 waves, 8x8 micro-tiles, BK 16 (splitk4);
+//   * 64x128 tile, 8 waves, 8x16 micro-tiles (the square kernel's), BK 8 (splitk8): one
+//     workgroup of two waves per SIMD per CU, and three quarters of the LDS reads per FMA of
+//     8x8.
+// The partial tiles are summed through LDS in a fixed order, so results are deterministic;
+// the summation order differs from the square kernel's single k sweep.
 //
-// Per wave: 64 lanes as an 8x8 grid, lane micro-tile rows {r0..r0+3, r0+32..r0+35} and columns
-// {c0..c0+3, c0+32..c0+35} (every wave-wide 16-byte fragment read is one contiguous 128-byte
-// run). Each wave stages its own A slab (k-major, padded) and B slab in LDS, double-buffered;
-// the workgroup still synchronises once per slab.
+// Per wave: 64 lanes as an 8x8 grid, lane micro-tile rows {r0..r0+3, r0+32..r0+35} and
+// columns c0 + 32 g + {0..3} for g < TN/4 (every wave-wide 16-byte fragment read is one
+// contiguous 128-byte run). Each wave stages its own A slab (k-major, padded) and B slab in
+// its own two LDS buffers. No wave reads another wave's buffers, so the main loop needs no
+// workgroup barrier: a wave writes buffer (s+1) & 1 only after the fragments it read from that
+// buffer one slab earlier have been consumed by its own FMAs.
 #include "regtile_internal.h"
 
 namespace regtile {
 
 namespace {
 
-constexpr int TILE = 64, NW = 4, NT = 256, BK = 16, APAD = 4;
-constexpr int AS = TILE + APAD;  // A slab row stride (floats), k-major
+constexpr int APAD = 4;
 
-struct alignas(16) WaveStage {
-    float a[BK][AS];
-    float b[BK][TILE];
-};
-struct alignas(16) Smem {
-    union {
-        WaveStage st[NW][2];
-        float part[NW][TILE][TILE + 4];  // the four partial tiles after the main loop (padded)
+template <int NW_, int TM_, int TN_, int BK_>
+struct SplitCfg {
+    static constexpr int NW = NW_, TM = TM_, TN = TN_, BK = BK_;
+    static constexpr int NT = NW * 64;
+    static constexpr int TILE_M = 8 * TM, TILE_N = 8 * TN;  // 8 x 8 lanes per wave
+    static constexpr int AS = TILE_M + APAD;                // A slab row stride (floats), k-major
+    static constexpr int NA4 = TILE_M * BK / 256;           // A float4 per lane per slab
+    static constexpr int NB4 = BK * TILE_N / 256;           // B float4 per lane per slab
+    static constexpr int NPART = NW < 4 ? NW : 4;           // partial tiles held in LDS at once
+    static_assert(TM == 8 && (TN == 8 || TN == 16), "micro-tile rows in two groups of 4");
+    static_assert(NW == 4 || NW == 8, "four waves, or eight summed pairwise first");
+    static_assert(NA4 >= 1 && NB4 >= 1 && TILE_M * BK % 256 == 0 && BK * TILE_N % 256 == 0,
+                  "whole float4 per lane");
+    struct alignas(16) WaveStage {
+        float a[BK][AS];
+        float b[BK][TILE_N];
+    };
+    struct alignas(16) Smem {
+        union {
+            WaveStage st[NW][2];
+            float part[NPART][TILE_M][TILE_N + 4];  // partial tiles after the main loop (padded)
+        };
     };
 };
+using Split4 = SplitCfg<4, 8, 8, 16>;
+using Split8 = SplitCfg<8, 8, 16, 8>;
 
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ float4 load4(const float *__restrict__ p, bool row_ok, int cols_left) {
@@ -54,116 +75,159 @@ __device__ __forceinline__ float4 load4(const float *__restrict__ p, bool row_ok
     return v;
 }
 
-// GUARD: bounds checks on every load (ragged M/N, or K not a multiple of 4*BK).
-template <bool GUARD, bool VEC_A, bool VEC_B, bool VEC_C>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void f32_splitk_kernel(
+// GUARD: bounds checks on every load (ragged M/N, or K not a multiple of NW*BK).
+template <class CFG, bool GUARD, bool VEC_A, bool VEC_B, bool VEC_C>
+__global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void f32_splitk_kernel(
     int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, int slabs_per_wave) {
-    __shared__ Smem sm;
+    constexpr int NW = CFG::NW, TM = CFG::TM, TN = CFG::TN, BK = CFG::BK, NT = CFG::NT;
+    constexpr int TILE_M = CFG::TILE_M, TILE_N = CFG::TILE_N, AS = CFG::AS;
+    constexpr int NA4 = CFG::NA4, NB4 = CFG::NB4, NPART = CFG::NPART;
+    constexpr int AQ = BK / 4, BQ = TILE_N / 4;  // float4 per A row / per B row of a slab
+    __shared__ typename CFG::Smem sm;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r0 = (lane >> 3) * 4, c0 = (lane & 7) * 4;
 
     int tm, tn;
     grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * TILE, n0 = tn * TILE;
-    const int kb = wave * slabs_per_wave * BK;           // this wave's k range [kb, ke)
+    const int m0 = tm * TILE_M, n0 = tn * TILE_N;
+    const int kb = wave * slabs_per_wave * BK;  // this wave's k range [kb, ke)
     const int ke = min(K, kb + slabs_per_wave * BK);
 
-    // Staging: A slab 64 rows x 16 k = 256 float4 -> 4 per lane (row q/4, k (q%4)*4);
-    //          B slab 16 k x 64 cols  = 256 float4 -> 4 per lane (k q/16, col (q%16)*4).
-    float4 ra[4], rb[4];
+    // Staging: float4 q of the A slab (TILE_M rows x BK k) is row q / AQ, k (q % AQ) * 4;
+    // float4 q of the B slab (BK k x TILE_N columns) is k q / BQ, column (q % BQ) * 4.
+    float4 ra[NA4], rb[NB4];
     auto load_slab = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NA4; ++i) {
             const int q = lane + 64 * i;
-            const int ar = q >> 2, ak = (q & 3) * 4;
+            const int ar = q / AQ, ak = (q % AQ) * 4;
             ra[i] = load4<GUARD, VEC_A>(A + (int64_t)(m0 + ar) * lda + k0 + ak, m0 + ar < M,
                                         ke - (k0 + ak));
-            const int bk = q >> 4, bc = (q & 15) * 4;
+        }
+#pragma unroll
+        for (int i = 0; i < NB4; ++i) {
+            const int q = lane + 64 * i;
+            const int bk = q / BQ, bc = (q % BQ) * 4;
             rb[i] = load4<GUARD, VEC_B>(B + (int64_t)(k0 + bk) * ldb + n0 + bc, k0 + bk < ke,
                                         N - (n0 + bc));
         }
     };
     auto store_slab = [&](int buf) {
-        WaveStage &w = sm.st[wave][buf];
+        auto &w = sm.st[wave][buf];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NA4; ++i) {
             const int q = lane + 64 * i;
-            const int ar = q >> 2, ak = (q & 3) * 4;
+            const int ar = q / AQ, ak = (q % AQ) * 4;
             w.a[ak + 0][ar] = ra[i].x;
             w.a[ak + 1][ar] = ra[i].y;
             w.a[ak + 2][ar] = ra[i].z;
             w.a[ak + 3][ar] = ra[i].w;
-            const int bk = q >> 4, bc = (q & 15) * 4;
+        }
+#pragma unroll
+        for (int i = 0; i < NB4; ++i) {
+            const int q = lane + 64 * i;
+            const int bk = q / BQ, bc = (q % BQ) * 4;
             *reinterpret_cast<float4 *>(&w.b[bk][bc]) = rb[i];
         }
     };
 
-    float acc[8][8];
+    float acc[TM][TN];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < TM; ++m)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc[m][n] = 0.0f;
+        for (int n = 0; n < TN; ++n) acc[m][n] = 0.0f;
 
+    constexpr int NG = TN / 4;  // column groups of 4, 32 apart
     auto compute_slab = [&](int buf) {
         const float *sa = &sm.st[wave][buf].a[0][0] + r0;
         const float *sb = &sm.st[wave][buf].b[0][0] + c0;
-        float4 fa[2][2], fb[2][2];
+        float4 fa[2][2], fb[2][NG];
         fa[0][0] = *reinterpret_cast<const float4 *>(sa);
         fa[0][1] = *reinterpret_cast<const float4 *>(sa + 32);
-        fb[0][0] = *reinterpret_cast<const float4 *>(sb);
-        fb[0][1] = *reinterpret_cast<const float4 *>(sb + 32);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) fb[0][g] = *reinterpret_cast<const float4 *>(sb + 32 * g);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const int cb = k & 1, nb = cb ^ 1;
             if (k + 1 < BK) {
                 fa[nb][0] = *reinterpret_cast<const float4 *>(sa + (k + 1) * AS);
                 fa[nb][1] = *reinterpret_cast<const float4 *>(sa + (k + 1) * AS + 32);
-                fb[nb][0] = *reinterpret_cast<const float4 *>(sb + (k + 1) * TILE);
-                fb[nb][1] = *reinterpret_cast<const float4 *>(sb + (k + 1) * TILE + 32);
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * TILE_N + 32 * g);
             }
             const float a_[8] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
                                  fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
-            const float b_[8] = {fb[cb][0].x, fb[cb][0].y, fb[cb][0].z, fb[cb][0].w,
-                                 fb[cb][1].x, fb[cb][1].y, fb[cb][1].z, fb[cb][1].w};
+            float b_[TN];
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int g = 0; g < NG; ++g) {
+                b_[4 * g + 0] = fb[cb][g].x;
+                b_[4 * g + 1] = fb[cb][g].y;
+                b_[4 * g + 2] = fb[cb][g].z;
+                b_[4 * g + 3] = fb[cb][g].w;
+            }
 #pragma unroll
-                for (int n = 0; n < 8; ++n) acc[m][n] = fmaf(a_[m], b_[n], acc[m][n]);
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int n = 0; n < TN; ++n) acc[m][n] = fmaf(a_[m], b_[n], acc[m][n]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Every wave runs the same number of slabs (barrier counts must match); a wave whose
-    // range is shorter loads zeros past ke.
+    // Every wave runs the same number of slabs; a wave whose range is shorter loads zeros
+    // past ke (GUARD).
     if (slabs_per_wave > 0) {
         load_slab(kb);
         store_slab(0);
-        __syncthreads();
         for (int s = 0; s + 1 < slabs_per_wave; ++s) {
             load_slab(kb + (s + 1) * BK);
             compute_slab(s & 1);
             store_slab((s + 1) & 1);
-            __syncthreads();
         }
         compute_slab((slabs_per_wave - 1) & 1);
     }
     __syncthreads();  // all waves are done with their stages: the union turns into partials
 
-    // Partial tile of this wave -> LDS.
+    auto write_part = [&](int slot) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int row = r0 + (m < 4 ? m : 28 + m);
-        *reinterpret_cast<float4 *>(&sm.part[wave][row][c0]) =
-            make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
-        *reinterpret_cast<float4 *>(&sm.part[wave][row][c0 + 32]) =
-            make_float4(acc[m][4], acc[m][5], acc[m][6], acc[m][7]);
+        for (int m = 0; m < TM; ++m) {
+            const int row = r0 + (m < 4 ? m : 28 + m);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                *reinterpret_cast<float4 *>(&sm.part[slot][row][c0 + 32 * g]) =
+                    make_float4(acc[m][4 * g], acc[m][4 * g + 1], acc[m][4 * g + 2], acc[m][4 * g + 3]);
+        }
+    };
+    if constexpr (NW == 8) {
+        // waves 4..7 hand their partials to waves 0..3, which add them (acc_w + acc_{w+4})
+        if (wave >= 4) write_part(wave - 4);
+        __syncthreads();
+        if (wave < 4) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                const int row = r0 + (m < 4 ? m : 28 + m);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const float4 p = *reinterpret_cast<const float4 *>(&sm.part[wave][row][c0 + 32 * g]);
+                    acc[m][4 * g] += p.x;
+                    acc[m][4 * g + 1] += p.y;
+                    acc[m][4 * g + 2] += p.z;
+                    acc[m][4 * g + 3] += p.w;
+                }
+            }
+        }
+        __syncthreads();
     }
+    if (wave < NPART) write_part(wave);
     __syncthreads();
 
-    // Fixed-order sum and epilogue: thread t owns row t/4, columns (t%4)*16 .. +15.
-    const int row = tid >> 2, col0 = (tid & 3) * 16;
+    // Fixed-order sum of the NPART partials and epilogue: thread t owns row t / (TILE_N / 16),
+    // columns (t % (TILE_N / 16)) * 16 .. +15.
+    constexpr int TPR = TILE_N / 16;  // threads per row
+    static_assert(NT == TILE_M * TPR, "one 16-column strip per thread");
+    const int row = tid / TPR, col0 = (tid % TPR) * 16;
     const int grow = m0 + row;
     if (GUARD && grow >= M) return;
     float *crow = C + (int64_t)grow * ldc;
@@ -172,7 +236,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const int col = col0 + c4 * 4;
         float4 s = *reinterpret_cast<const float4 *>(&sm.part[0][row][col]);
 #pragma unroll
-        for (int w = 1; w < NW; ++w) {
+        for (int w = 1; w < NPART; ++w) {
             const float4 p = *reinterpret_cast<const float4 *>(&sm.part[w][row][col]);
             s.x += p.x;
             s.y += p.y;
@@ -200,41 +264,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
 }
 
-template <bool G, bool VA, bool VB, bool VC>
+template <class CFG, bool G, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tm, int tn, int spw) {
-    hipLaunchKernelGGL((f32_splitk_kernel<G, VA, VB, VC>), dim3(tm * tn), dim3(NT), 0, s, p.M, p.N,
-                       p.K, p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb, p.beta,
-                       p.C, p.ldc, tm, tn, spw);
+    hipLaunchKernelGGL((f32_splitk_kernel<CFG, G, VA, VB, VC>), dim3(tm * tn), dim3(CFG::NT), 0, s,
+                       p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda, (const float *)p.B,
+                       p.ldb, p.beta, p.C, p.ldc, tm, tn, spw);
     return hipGetLastError();
 }
-template <bool G, bool VA, bool VB>
+template <class CFG, bool G, bool VA, bool VB>
 hipError_t pick_c(const Problem &p, hipStream_t s, int tm, int tn, int spw, bool vc) {
-    return vc ? launch_variant<G, VA, VB, true>(p, s, tm, tn, spw)
-              : launch_variant<G, VA, VB, false>(p, s, tm, tn, spw);
+    return vc ? launch_variant<CFG, G, VA, VB, true>(p, s, tm, tn, spw)
+              : launch_variant<CFG, G, VA, VB, false>(p, s, tm, tn, spw);
 }
-template <bool G, bool VA>
+template <class CFG, bool G, bool VA>
 hipError_t pick_b(const Problem &p, hipStream_t s, int tm, int tn, int spw, bool vb, bool vc) {
-    return vb ? pick_c<G, VA, true>(p, s, tm, tn, spw, vc) : pick_c<G, VA, false>(p, s, tm, tn, spw, vc);
+    return vb ? pick_c<CFG, G, VA, true>(p, s, tm, tn, spw, vc)
+              : pick_c<CFG, G, VA, false>(p, s, tm, tn, spw, vc);
 }
-template <bool G>
-hipError_t pick_a(const Problem &p, hipStream_t s, int tm, int tn, int spw, bool va, bool vb, bool vc) {
-    return va ? pick_b<G, true>(p, s, tm, tn, spw, vb, vc) : pick_b<G, false>(p, s, tm, tn, spw, vb, vc);
+template <class CFG>
+hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name, const char *base,
+                      const char *guarded) {
+    const int tiles_m = (p.M + CFG::TILE_M - 1) / CFG::TILE_M;
+    const int tiles_n = (p.N + CFG::TILE_N - 1) / CFG::TILE_N;
+    const int nslabs = (p.K + CFG::BK - 1) / CFG::BK;
+    const int spw = (nslabs + CFG::NW - 1) / CFG::NW;  // slabs per wave
+    const bool guard = (p.M % CFG::TILE_M) != 0 || (p.N % CFG::TILE_N) != 0 ||
+                       (p.K % (CFG::NW * CFG::BK)) != 0;
+    const bool va = (p.lda % 4) == 0 && aligned16(p.A);
+    const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
+    const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
+    *name = guard ? guarded : base;
+    if (guard)
+        return va ? pick_b<CFG, true, true>(p, s, tiles_m, tiles_n, spw, vb, vc)
+                  : pick_b<CFG, true, false>(p, s, tiles_m, tiles_n, spw, vb, vc);
+    return va ? pick_b<CFG, false, true>(p, s, tiles_m, tiles_n, spw, vb, vc)
+              : pick_b<CFG, false, false>(p, s, tiles_m, tiles_n, spw, vb, vc);
 }
-
 
 }  // namespace
 
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name) {
-    const int tiles_m = (p.M + TILE - 1) / TILE, tiles_n = (p.N + TILE - 1) / TILE;
-    const int nslabs = (p.K + BK - 1) / BK;
-    const int spw = (nslabs + NW - 1) / NW;  // slabs per wave
-    const bool guard = (p.M % TILE) != 0 || (p.N % TILE) != 0 || (p.K % (NW * BK)) != 0;
-    const bool va = (p.lda % 4) == 0 && aligned16(p.A);
-    const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
-    const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
-    *name = guard ? "f32_regtile_splitk4_64x64x16_8x8_guard" : "f32_regtile_splitk4_64x64x16_8x8";
-    return guard ? pick_a<true>(p, s, tiles_m, tiles_n, spw, va, vb, vc)
-                 : pick_a<false>(p, s, tiles_m, tiles_n, spw, va, vb, vc);
+    // 8 waves x 8x16 once 64x128 tiles give most CUs a workgroup (two waves per SIMD), unless
+    // the 4-wave kernel's 64x64 tiles already fill the chip and K is short enough that the
+    // 8-wave kernel's longer reduction does not pay (measured on 13 row-major shapes with
+    // 64 <= K <= 8192; the 8-wave kernel lost at 16384 x 128 x 1024 and won at x 4096).
+    const int64_t tm64 = (p.M + 63) / 64;
+    const int64_t t128 = tm64 * ((p.N + 127) / 128), t64 = tm64 * ((p.N + 63) / 64);
+    if (t128 >= 192 && (p.K >= 1280 || t64 < 448))
+        return launch_cfg<Split8>(p, s, name, "f32_regtile_splitk8_64x128x8_8x16",
+                                  "f32_regtile_splitk8_64x128x8_8x16_guard");
+    return launch_cfg<Split4>(p, s, name, "f32_regtile_splitk4_64x64x16_8x8",
+                              "f32_regtile_splitk4_64x64x16_8x8_guard");
 }
 
 }  // namespace regtile

@@ -89,16 +89,19 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
     const char *name = "none";
     hipError_t err;
     if (algo == REGTILE_F32_AUTO) {
-        // Fewer than two 128x128 tiles per CU leaves SIMDs idle. Smaller tiles restore the
-        // parallelism: with a long K, the split-K kernel (64x64 tiles, 8x8 micro-tiles, each
-        // wave a quarter of K; row-major operands only), measured about 12% ahead of 4x4
-        // micro-tiles on 16384x128x4096, whose LDS reads bound them; otherwise 64x64 tiles of
-        // 4x4 micro-tiles at 4 waves per SIMD (bitwise equal to the naive rung).
-        const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+        // The square kernel (128x256 tiles, two workgroups = two waves per SIMD per CU) needs
+        // about 1.5 tiles per CU: with 256 tiles (one per CU, one wave per SIMD) it ran at
+        // 66 TFLOP/s on 4096x2048x4096 against 86 for split-K, with 384 it led (93 against 87).
+        // Below that, smaller tiles restore the parallelism: the split-K kernel for row-major
+        // operands once K is long enough to pay for its reduction (K >= 1024, or K >= 384
+        // while fewer than four 64x64 tiles per CU leave the small-tile kernel under-filled),
+        // otherwise 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD (bitwise equal to the
+        // naive rung). Measured on 30 shapes with 64 <= K <= 8192.
+        const int64_t sq = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
         const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-        if (tiles >= 2 * 256)
+        if (sq >= 384)
             algo = REGTILE_F32_REGTILE;
-        else if (!ta && !tb && K >= 1024 && tiles64 <= 2 * 256)
+        else if (!ta && !tb && (K >= 1024 || (tiles64 < 4 * 256 && K >= 384)))
             algo = REGTILE_F32_SPLITK;
         else
             algo = REGTILE_F32_REGTILE_SMALL;

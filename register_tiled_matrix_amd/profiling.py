@@ -45,7 +45,7 @@ KERNELS = {
     "bf16_8192": ("bf16_mfma32x32x16_dma_256x256x64_w2x2", "bf16_mfma_dma_kernel<256, 256, 64, 2, 2, 32",
                   ["gemm_bf16_mfma_dma.hip", "mfma_common.h", "regtile_internal.h"],
                   2 * 8192 * 8192 * 2 + 8192 * 8192 * 4),
-    "f32_tall": ("f32_regtile_splitk4_64x64x16_8x8", "f32_splitk_kernel<false",
+    "f32_tall": ("f32_regtile_splitk8_64x128x8_8x16", "SplitCfg<8, 8, 16, 8>, false",
                  ["gemm_f32_splitk.hip", "regtile_internal.h"], (16384 * 4096 + 4096 * 128 + 16384 * 128) * 4),
 }
 PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "copy"]

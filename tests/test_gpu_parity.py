@@ -116,6 +116,43 @@ def test_f32_regtile_edges(shape, algo):
     assert_parity_full(inp, got, f"f32 edges {shape} ({rt.last_kernel()})")
 
 
+# Split-K shapes with at least 192 tiles of 64x128, which take the 8-wave 64x128 kernel:
+# ragged M, N and K; K below the 8 waves x 8 of one slab each (waves past K add zeros);
+# N below one tile; exact multiples (no bounds checks).
+SPLITK8_SHAPES = [(13000, 50, 37), (12289, 130, 1283), (8192, 256, 1300), (12800, 128, 1536),
+                  (12352, 1, 7)]
+
+
+@pytest.mark.parametrize("shape", SPLITK8_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK8_SHAPES])
+def test_f32_splitk8_edges(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=-1.25, beta=0.75, seed=M + N + K)
+    announce(f"f32 split-K 8 waves {shape}")
+    got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
+    name = rt.last_kernel()
+    assert name.startswith("f32_regtile_splitk8_64x128x8_8x16"), name
+    assert name.endswith("_guard") == (M % 64 != 0 or N % 128 != 0 or K % 64 != 0), name
+    assert_parity_full(inp, got, f"f32 split-K {shape} ({name})")
+
+
+def test_f32_auto_picks_by_tile_count():
+    # square kernel from 384 tiles of 128x256; split-K below that for a long enough K;
+    # otherwise the small-tile kernel
+    cases = [((4096, 3072, 64), "f32_regtile_128x256x16_8x16"), ((4096, 2048, 2048), "f32_regtile_splitk8"),
+             ((4096, 2048, 1024), "f32_regtile_splitk4"),
+             ((1000, 1500, 777), "f32_regtile_splitk8"), ((1024, 1024, 1024), "f32_regtile_splitk4"),
+             ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_64x64x32_4x4")]
+    for (M, N, K), prefix in cases:
+        A = torch.zeros((M, K), device="cuda")
+        B = torch.zeros((K, N), device="cuda")
+        rt.gemm_f32(A, B)
+        assert rt.last_kernel().startswith(prefix), ((M, N, K), rt.last_kernel())
+        At = torch.zeros((K, M), device="cuda").t()
+        rt.gemm_f32(At, B)  # transposed A: split-K stages row-major operands only
+        assert "splitk" not in rt.last_kernel(), ((M, N, K), rt.last_kernel())
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("algo", BF16_MFMA_ALGOS)
 @pytest.mark.parametrize("shape", EDGE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in EDGE_SHAPES])
 def test_bf16_mfma_edges(shape, algo):
