@@ -182,9 +182,17 @@ def cmd_run(args) -> int:
 # the compiler's resource report)
 F32_RUNGS = [("naive", 1, "naive_kernelIfLb0ELb0E"), ("lds_32x32", 2, "f32_lds_kernel"),
              ("regtile_8x16", 3, "SquareCfgELb0ELb0E"), ("regtile_small_4x4", 5, "SmallCfgELb0ELb0E"),
-             ("splitk_8x8", 4, "f32_splitk_kernel")]
+             ("splitk", 4, {"splitk8": "SplitCfgILi8ELi8ELi16ELi8E", "splitk4": "SplitCfgILi4ELi8ELi8ELi16E"})]
 R16_RUNGS = [("naive", 1, "naive_kernelI{T}Lb0ELb1E"), ("mfma_32x32x16", 2, "ELi32ELi1ELi1ELb{F}E"),
              ("mfma_16x16x32", 3, "ELi16ELi1ELi0ELb{F}E")]
+
+
+def _rung_prefix(prefix, kernel_name: str) -> str:
+    """A rung's mangled-name prefix; a dict maps a substring of the launched kernel's label
+    to the prefix of that kernel (rungs that pick between kernel shapes)."""
+    if isinstance(prefix, dict):
+        return next(v for k, v in prefix.items() if k in kernel_name)
+    return prefix
 
 
 def _kernel_resources(prefix: str) -> dict:
@@ -244,7 +252,7 @@ def cmd_ladder(args) -> int:
             ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
             print(json.dumps({"workload": wl, "rung": label, "kernel": rt.last_kernel(),
                               "ms_median": round(ms, 4), "tflops": round(w.flop / (ms * 1e-3) / 1e12, 3),
-                              **_kernel_resources(prefix)}), flush=True)
+                              **_kernel_resources(_rung_prefix(prefix, rt.last_kernel()))}), flush=True)
         del A, B, C
     return 0
 
@@ -319,9 +327,10 @@ def _ladder_report(rows) -> str:
            "Command (repository root, one MI355X):", "", "```",
            "python -m register_tiled_matrix_amd.tune ladder > gpurun_out/ladder.jsonl",
            "python -m register_tiled_matrix_amd.tune report gpurun_out/ladder.jsonl", "```", "",
-           "Median of 10 timed launches (3 for the naive and LDS rungs on the large problems), "
-           "operands resident on the device. VGPRs / occupancy / LDS: the compiler's resource "
-           "report for the rung's kernels (largest variant).", "",
+           "Median of 30 timed launches after 50 warm-up launches (3 timed after 1 for the naive "
+           "and LDS rungs on the large problems), operands resident on the device. VGPRs / "
+           "occupancy / LDS: the compiler's resource report for the kernel the rung launched "
+           "(largest of its vector / edge variants).", "",
            "| workload | rung | kernel | median ms | TFLOP/s | VGPRs | AGPRs | waves/SIMD | LDS bytes |",
            "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -414,8 +423,8 @@ def main(argv=None) -> int:
                         "kernels would share the variants' names)")
     lad = sub.add_parser("ladder")
     lad.add_argument("--workloads", default="f32_256,f32_4096,f32_ragged,f32_tall,bf16_8192,f16_8192")
-    lad.add_argument("--steps", type=int, default=10)
-    lad.add_argument("--warmup", type=int, default=3)
+    lad.add_argument("--steps", type=int, default=30)
+    lad.add_argument("--warmup", type=int, default=50)
     pr = sub.add_parser("probe", help="gfx950 facts: FP32 FMA issue rate and VGPR banks, "
                                        "MFMA rate, LDS access patterns")
     pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "none"])
