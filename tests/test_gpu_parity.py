@@ -296,6 +296,25 @@ def test_beta_zero_never_reads_c(dtype):
     assert_parity_full(inp, got, "beta=0 with NaN C")
 
 
+F32_EPILOGUE_CASES = [(rt.ALGO_F32_REGTILE, (200, 300, 64), "f32_regtile_128x256"),
+                      (rt.ALGO_F32_REGTILE_SMALL, (200, 300, 64), "f32_regtile_64x64x32"),
+                      (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk4"),
+                      (rt.ALGO_F32_SPLITK, (13000, 50, 37), "f32_regtile_splitk8"),
+                      (rt.ALGO_F32_SPLITK, (12800, 128, 512), "f32_regtile_splitk8")]
+
+
+@pytest.mark.parametrize("algo,shape,prefix", F32_EPILOGUE_CASES,
+                         ids=[f"{a}-{'x'.join(map(str, s))}" for a, s, _ in F32_EPILOGUE_CASES])
+def test_f32_beta_zero_never_reads_c_every_kernel(algo, shape, prefix):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=0.5, seed=M + N)
+    announce(f"beta=0 NaN C algo={algo} {shape}")
+    got = run(inp, torch, algo, C_init=torch.full((M, N), float("nan"), device="cuda")).cpu().numpy()
+    assert rt.last_kernel().startswith(prefix), rt.last_kernel()
+    assert np.all(np.isfinite(got))
+    assert_parity_full(inp, got, f"beta=0 with NaN C ({rt.last_kernel()})")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_alpha_zero_and_k_zero_scale_c(dtype):
     M, N = 70, 90
@@ -403,9 +422,12 @@ def test_f32_strided_views_every_register_tiled_kernel():
         assert torch.count_nonzero(big_c[:, N + 1:]).item() == 0
 
 
-def test_splitk_is_deterministic_and_matches_oracle_at_tall_shape():
-    inp = gi.make_inputs(4096, 192, 2000, dist="uniform", seed=12)
-    announce("splitk determinism")
+@pytest.mark.parametrize("shape,prefix", [((4096, 192, 2000), "f32_regtile_splitk4"),
+                                          ((13000, 130, 2000), "f32_regtile_splitk8")])
+def test_splitk_is_deterministic_and_matches_oracle_at_tall_shape(shape, prefix):
+    inp = gi.make_inputs(*shape, dist="uniform", seed=12)
+    announce(f"splitk determinism {shape}")
     outs = [run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy() for _ in range(3)]
+    assert rt.last_kernel().startswith(prefix), rt.last_kernel()
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
-    assert_parity_sampled(inp, outs[0], "splitk tall")
+    assert_parity_sampled(inp, outs[0], f"splitk tall ({rt.last_kernel()})")
