@@ -38,23 +38,38 @@ constexpr int KCH = 8;   // 16-byte chunks per slab row
 // are free of LDS bank conflicts.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * KCH + (chunk ^ mfma::slab_key<KCH>(row)); }
 
+// A whole run of 16 (8) bytes at any 2-byte-aligned address, as one global_load_dwordx4
+// (dwordx2): the ROCm driver runs gfx9-class GPUs in unaligned-access mode, so multi-dword
+// global loads take any address (the compiler emits the same single load for these).
+__device__ __forceinline__ uint4 load16_any(const uint16_t *p) {
+    uint4 r;
+    __builtin_memcpy(&r, p, 16);
+    return r;
+}
+__device__ __forceinline__ uint2 load8_any(const uint16_t *p) {
+    uint2 r;
+    __builtin_memcpy(&r, p, 8);
+    return r;
+}
+
 template <bool EDGE, bool VEC>
 __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool row_ok,
                                             int k_left) {
-    // 8 consecutive bf16 starting at p (k index k0); k_left = K - k0.
+    // 8 consecutive bf16 starting at p (k index k0); k_left = K - k0. VEC: p is 16-byte
+    // aligned; otherwise whole chunks still take one unaligned 16-byte load and only a
+    // chunk cut by the end of K is read element by element.
     if (!EDGE) {
         if (VEC) return *reinterpret_cast<const uint4 *>(p);
+        return load16_any(p);
     }
     uint16_t v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0;
-    if (!EDGE || row_ok) {
-        if (VEC && (!EDGE || k_left >= 8)) {
-            return *reinterpret_cast<const uint4 *>(p);
-        }
+    if (row_ok) {
+        if (k_left >= 8) return VEC ? *reinterpret_cast<const uint4 *>(p) : load16_any(p);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (!EDGE || e < k_left) v[e] = p[e];
+            if (e < k_left) v[e] = p[e];
     }
     uint4 r;
     r.x = v[0] | ((uint32_t)v[1] << 16);
@@ -66,9 +81,10 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool
 
 // A 4 x 8 block of an operand stored K-major-outer (element (r, k) at p[k * ld + r] relative
 // to the block's first element, r < 4 along the contiguous M or N dimension, k < 8): read as
-// 8 runs of 4 elements (one 8-byte load per k when `vec`, else predicated 2-byte loads; zero
-// outside r_left x k_left) and transposed in registers into 4 chunks of 8 consecutive k, the
-// K-contiguous form the fragment reads expect. out[j] holds row r = j.
+// 8 runs of 4 elements (one 8-byte load per whole run, aligned when `vec`, else unaligned;
+// predicated 2-byte loads for a run cut by the edge; zero outside r_left x k_left) and
+// transposed in registers into 4 chunks of 8 consecutive k, the K-contiguous form the
+// fragment reads expect. out[j] holds row r = j.
 template <bool EDGE>
 __device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, int64_t ld, bool vec,
                                               int r_left, int k_left, uint4 out[4]) {
@@ -76,8 +92,8 @@ __device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, in
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
         const uint16_t *q = p + kk * ld;
-        if (vec && (!EDGE || (kk < k_left && r_left >= 4))) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(q);
+        if (!EDGE || (kk < k_left && r_left >= 4)) {
+            const uint2 v = vec ? *reinterpret_cast<const uint2 *>(q) : load8_any(q);
             lo[kk] = v.x;
             hi[kk] = v.y;
         } else {
