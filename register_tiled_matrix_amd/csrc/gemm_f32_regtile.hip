@@ -82,12 +82,12 @@ __device__ __forceinline__ float4 load4_rowwise(const float *__restrict__ p, int
     // this row (> 0 means in range), cols_left = columns remaining from col.
     if (!EDGE) {
         if (VEC) return *reinterpret_cast<const float4 *>(p);
-        return make_float4(p[0], p[1], p[2], p[3]);
+        return load_f4_any(p);
     }
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (rows_left > 0) {
-        if (VEC && cols_left >= 4) {
-            v = *reinterpret_cast<const float4 *>(p);
+        if (cols_left >= 4) {
+            v = VEC ? *reinterpret_cast<const float4 *>(p) : load_f4_any(p);
         } else {
             if (cols_left > 0) v.x = p[0];
             if (cols_left > 1) v.y = p[1];

@@ -59,12 +59,12 @@ template <bool GUARD, bool VEC>
 __device__ __forceinline__ float4 load4(const float *__restrict__ p, bool row_ok, int cols_left) {
     if (!GUARD) {
         if (VEC) return *reinterpret_cast<const float4 *>(p);
-        return make_float4(p[0], p[1], p[2], p[3]);
+        return load_f4_any(p);
     }
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row_ok) {
-        if (VEC && cols_left >= 4) {
-            v = *reinterpret_cast<const float4 *>(p);
+        if (cols_left >= 4) {
+            v = VEC ? *reinterpret_cast<const float4 *>(p) : load_f4_any(p);
         } else {
             if (cols_left > 0) v.x = p[0];
             if (cols_left > 1) v.y = p[1];

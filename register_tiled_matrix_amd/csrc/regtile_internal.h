@@ -47,6 +47,15 @@ hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
+// Four consecutive floats at any 4-byte-aligned address as one global_load_dwordx4:
+// multi-dword global loads need only dword alignment on gfx9-class GPUs (the compiler emits
+// the same single load for this copy).
+__device__ __forceinline__ float4 load_f4_any(const float *p) {
+    float4 r;
+    __builtin_memcpy(&r, p, 16);
+    return r;
+}
+
 // s_waitcnt lgkmcnt(N) with no wait on the vector-memory or export counters (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
 template <int N>
