@@ -82,8 +82,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // operand; instruction and slab offsets are wave-uniform (SGPR).
     constexpr int ROWS_PER_INSTR = 64 / KCH;
     static_assert(KCH == 4 || (ROWS_PER_INSTR == 8 && JA % 2 == 0 && JB % 2 == 0), "key periodicity");
-    const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(BM * lda * 2));
-    const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(BN * ldb * 2));
+    // A tile of the last tile row (column) may extend past M (N): its descriptors end at the
+    // last real row, so DMA loads of the rows beyond read zeros.
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(rows_a * lda * 2));
+    const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
     uint32_t a_voff[2], b_voff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -481,12 +484,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // its MF x MF block. Stores go through a buffer descriptor over the tile's BM rows of C:
     // one per-lane byte offset for the whole epilogue, the (i, j, v) part wave-uniform (the
     // launch checks that BM rows of C span less than 2^31 bytes). beta == 0 never reads C.
-    const rsrc_t c_rsrc = make_rsrc(C + (int64_t)m0 * ldc + n0, (uint32_t)(BM * ldc * 4));
+    // (past M, the descriptor drops the stores of the rows beyond; past N, lanes whose column
+    // is beyond N get an offset past the descriptor's end, 2^31 > BM rows of C, so the
+    // hardware drops those stores too)
+    const rsrc_t c_rsrc = make_rsrc(C + (int64_t)m0 * ldc + n0, (uint32_t)(min(BM, M - m0) * ldc * 4));
     // (the lane index is recomputed from mbcnt so no thread-id register stays live across
     // the main loop)
     const int elane = __lane_id();
     const uint32_t lane_off =
         (uint32_t)((wm * WTM + F::row_lane(elane)) * ldc + wn * WTN + elane % MF) * 4u;
+    uint32_t lane_off_j[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+        lane_off_j[j] = n0 + wn * WTN + j * MF + elane % MF < N ? lane_off : 0x80000000u;
     auto c_off = [&](int i, int j, int v) {
         return (uint32_t)((i * MF + F::row_acc(v)) * ldc + j * MF) * 4u;
     };
@@ -497,8 +507,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int v = 0; v < F::NACC; ++v) {
-                    const float c = load_f32_buf(c_rsrc, lane_off, c_off(i, j, v));
-                    store_f32_buf(c_rsrc, lane_off, c_off(i, j, v), fmaf(alpha, acc[i][j][v], beta * c));
+                    const float c = load_f32_buf(c_rsrc, lane_off_j[j], c_off(i, j, v));
+                    store_f32_buf(c_rsrc, lane_off_j[j], c_off(i, j, v), fmaf(alpha, acc[i][j][v], beta * c));
                 }
     } else {
 #pragma unroll
@@ -507,14 +517,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int v = 0; v < F::NACC; ++v)
-                    store_f32_buf(c_rsrc, lane_off, c_off(i, j, v), alpha * acc[i][j][v]);
+                    store_f32_buf(c_rsrc, lane_off_j[j], c_off(i, j, v), alpha * acc[i][j][v]);
     }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING,
           int ROWS = 0>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
-    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
@@ -550,16 +560,18 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 
 }  // namespace
 
-// Returns hipErrorNotSupported (and launches nothing) unless the problem is made of full
-// tiles with 16-byte aligned, K-contiguous rows.
+// Returns hipErrorNotSupported (and launches nothing) unless K is a whole number of slabs and
+// the rows are 16-byte aligned and K-contiguous. M and N may end inside a tile (the tile's
+// descriptors stop at the last real row and column).
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16) {
-    const bool ok = p.M % DMA_BM == 0 && p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
+    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
+    const bool ok = p.K % DMA_BK == 0 && p.K > 0 &&
                     p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
                     (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
                     (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31) &&
                     (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
-                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128 && (shape == 32 || shape == 16);
+                    tiles >= 128 && (shape == 32 || shape == 16);
     if (!ok) return hipErrorNotSupported;
 #define REGTILE_DMA_NAME(elt, mf)                                                                  \
     elt "_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)     \

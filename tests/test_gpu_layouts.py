@@ -140,7 +140,7 @@ def test_16bit_layouts_8192_sampled(ta, tb, dtype):
 def test_16bit_gathered_layouts_large_ragged(shape, ta, tb, dtype):
     # enough 256x256 tiles for the eight-wave gathered kernel, ragged on every side; the second
     # shape's odd leading dimensions (lda = M for A stored K x M, ldb = N for B stored K x N)
-    # take the 2-byte gather instead of the 8-byte runs
+    # make every 8-byte run unaligned
     M, N, K = shape
     inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=0.75, beta=0.5, seed=M + N + K + 2 * ta + tb)
     announce(f"{dtype} gathered layout {ta}{tb} {shape}")

@@ -163,6 +163,38 @@ def test_bf16_mfma_edges(shape, algo):
     assert_parity_full(inp, got, f"bf16 edges {shape}")
 
 
+# ---- LDS-DMA kernel on tiles cut by M or N ---------------------------------------------------
+# At least 128 tiles of 256x256 counting partial ones, K a whole number of 64-deep slabs: the
+# DMA kernel, whose descriptors stop at the last real row of A, B and C. C has padded rows, and
+# the padding (columns N.. of every row) must stay untouched.
+DMA_RAGGED = [("bf16", (8000, 4100, 128), 1.5, -0.5, "full"), ("bf16", (4097, 8191, 64), 1.0, 0.0, "full"),
+              ("f16", (4100, 8000, 192), -1.0, 0.5, "full"), ("bf16", (2049, 4095, 3072), 1.0, 0.0, "sampled")]
+
+
+@pytest.mark.parametrize("dtype,shape,alpha,beta,mode", DMA_RAGGED,
+                         ids=[f"{d}-{'x'.join(map(str, s))}" for d, s, _, _, _ in DMA_RAGGED])
+def test_16bit_dma_kernel_on_ragged_m_n(dtype, shape, alpha, beta, mode):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=alpha, beta=beta, seed=M + 2 * N + K)
+    announce(f"{dtype} DMA ragged {shape}")
+    A, B, C0 = device_operands(inp, torch)
+    big = torch.full((M, N + 7), 1234.5, device="cuda")
+    C = big[:, :N]
+    if inp.C is not None:
+        C.copy_(C0)
+    fn = {"bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[dtype]
+    fn(A, B, C, alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    name = rt.last_kernel()
+    assert "_dma_" in name, name
+    assert torch.all(big[:, N:] == 1234.5).item(), "a store landed past column N"
+    got = C.cpu().numpy()
+    if mode == "full":
+        assert_parity_full(inp, got, f"{dtype} {shape} ({name})")
+    else:
+        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})", n_random=30000)
+
+
 # ---- bitwise: integer-valued operands (every partial sum exact in fp32) ---------------------
 @pytest.mark.parametrize("algo", F32_ALGOS)
 def test_f32_integer_inputs_are_bitwise_exact(algo):
