@@ -37,7 +37,7 @@ namespace {
 using namespace mfma;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16,
-          int RING = 2, int ROWS = 0>
+          int RING = 2, int ROWS = 0, bool KTAIL = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -60,6 +60,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // K x M (M-contiguous). The M/N-contiguous operand arrives as rows through registers.
     constexpr bool A_ROW = ROWS == 2, ANY_ROW = ROWS != 0;
     static_assert(ROWS >= 0 && ROWS <= 2 && (!ANY_ROW || RING == 5), "row operands go through the ring");
+    // KTAIL: K ends inside the last slab (K a multiple of 8, so each 16-byte chunk lies wholly
+    // before or wholly past K); that slab's chunks past K are loaded from an offset past the
+    // descriptor's end, which puts zeros in LDS.
+    static_assert(!KTAIL || !ANY_ROW, "the K tail is masked on the DMA operands");
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
 
@@ -87,7 +91,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(rows_a * lda * 2));
     const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
-    uint32_t a_voff[2], b_voff[2];
+    const int nslabs = KTAIL ? (K + BK - 1) / BK : K / BK;
+    const int k_last = (nslabs - 1) * BK;  // first k of the last slab
+    uint32_t a_voff[2], b_voff[2], a_voff_last[2], b_voff_last[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int pa = (wave * JA + j) * 64 + lane;
@@ -96,26 +102,31 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         const int pb = (wave * JB + j) * 64 + lane;
         const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH, MF>(rb);
         b_voff[j] = (uint32_t)(rb * ldb + cb * 8) * 2u;
+        // (2^31 exceeds every tile's byte count; the uniform parts added to it stay below 2^32)
+        a_voff_last[j] = k_last + ca * 8 < K ? a_voff[j] : a_voff[j] | 0x80000000u;
+        b_voff_last[j] = k_last + cb * 8 < K ? b_voff[j] : b_voff[j] | 0x80000000u;
     }
+    auto voff_a = [&](int q, int k0) { return KTAIL && k0 == k_last ? a_voff_last[q & 1] : a_voff[q & 1]; };
+    auto voff_b = [&](int q, int k0) { return KTAIL && k0 == k_last ? b_voff_last[q & 1] : b_voff[q & 1]; };
     const uint32_t a_step = (uint32_t)(ROWS_PER_INSTR * lda) * 2u;  // bytes per instruction
     const uint32_t b_step = (uint32_t)(ROWS_PER_INSTR * ldb) * 2u;
     // DMA instruction q (A for q < JA, then B) of the slab starting at k0.
     auto dma_q = [&](int q, int k0, uint4 *sa, uint4 *sb) {
         if (q < JA)
-            dma16_buf(a_rsrc, a_voff[q & 1], (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u,
+            dma16_buf(a_rsrc, voff_a(q, k0), (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u,
                       sa + (wave * JA + q) * 64);
         else
-            dma16_buf(b_rsrc, b_voff[(q - JA) & 1], (uint32_t)((q - JA) & ~1) * b_step + (uint32_t)k0 * 2u,
+            dma16_buf(b_rsrc, voff_b(q - JA, k0), (uint32_t)((q - JA) & ~1) * b_step + (uint32_t)k0 * 2u,
                       sb + (wave * JB + (q - JA)) * 64);
     };
 
     // One DMA instruction q of the A part (B part) of the slab starting at k0 into the half
     // (A or B area) at `dst`.
     auto dma_a = [&](int q, int k0, uint4 *dst) {
-        dma16_buf(a_rsrc, a_voff[q & 1], (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u, dst + (wave * JA + q) * 64);
+        dma16_buf(a_rsrc, voff_a(q, k0), (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u, dst + (wave * JA + q) * 64);
     };
     auto dma_b = [&](int q, int k0, uint4 *dst) {
-        dma16_buf(b_rsrc, b_voff[q & 1], (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
+        dma16_buf(b_rsrc, voff_b(q, k0), (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
     };
     // the operand that keeps its DMA when the other arrives as rows
     auto dma_e = [&](int q, int k0, uint4 *dst) {
@@ -147,7 +158,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         brow_src[i] = rsrc_base + (int64_t)(brow_kc[i] * 8) * ld_row + brow_n[i];
     }
     auto load_brow = [&](int slab) {
-        const int64_t k0 = (int64_t)min(slab, K / BK - 1) * BK;
+        const int64_t k0 = (int64_t)min(slab, nslabs - 1) * BK;
 #pragma unroll
         for (int i = 0; i < B_BLOCKS; ++i)
 #pragma unroll
@@ -289,7 +300,6 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 
     // Past the end, requests are clamped to the last slab: they refill a stage nobody reads
     // again with valid data and keep every iteration identical (same counts at every wait).
-    const int nslabs = K / BK;
     if constexpr (RING == 2) {
 #pragma unroll
         for (int q = 0; q < PER_SLAB; ++q) dma_q(q, 0, smem, smem + A_SLOTS);
@@ -522,10 +532,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING,
-          int ROWS = 0>
+          int ROWS = 0, bool KTAIL = false>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS, KTAIL>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -558,39 +568,42 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 #define DMA_RING16 2
 #endif
 
+template <bool F16, bool KTAIL>
+hipError_t launch_dma_shape(const Problem &p, hipStream_t s, int shape) {
+    if (shape == 16)
+        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, F16, DMA_RING16, 0, KTAIL>(p, s);
+    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16, DMA_RING32, 0, KTAIL>(p, s);
+}
+
 }  // namespace
 
-// Returns hipErrorNotSupported (and launches nothing) unless K is a whole number of slabs and
-// the rows are 16-byte aligned and K-contiguous. M and N may end inside a tile (the tile's
-// descriptors stop at the last real row and column).
+// Returns hipErrorNotSupported (and launches nothing) unless K is a multiple of 8 and the rows
+// are 16-byte aligned and K-contiguous. M and N may end inside a tile (the tile's descriptors
+// stop at the last real row and column) and K inside the last slab (its chunks past K load
+// as zeros).
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16) {
     const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool ok = p.K % DMA_BK == 0 && p.K > 0 &&
+    const bool ok = p.K % 8 == 0 && p.K > 0 &&
                     p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
                     (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31) &&
                     (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31) &&
                     (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
                     tiles >= 128 && (shape == 32 || shape == 16);
     if (!ok) return hipErrorNotSupported;
+    const bool ktail = p.K % DMA_BK != 0;
 #define REGTILE_DMA_NAME(elt, mf)                                                                  \
     elt "_mfma" mf "_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)     \
         "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN)
-    if (f16) {
-        if (shape == 16) {
-            *name = REGTILE_DMA_NAME("f16", "16x16x32");
-            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, true, DMA_RING16>(p, s);
-        }
-        *name = REGTILE_DMA_NAME("f16", "32x32x16");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, DMA_RING32>(p, s);
-    }
-    if (shape == 16) {
-        *name = REGTILE_DMA_NAME("bf16", "16x16x32");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, false, DMA_RING16>(p, s);
-    }
-    *name = REGTILE_DMA_NAME("bf16", "32x32x16");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, DMA_RING32>(p, s);
+    static const char *const names[2][2][2] = {
+        {{REGTILE_DMA_NAME("bf16", "32x32x16"), REGTILE_DMA_NAME("bf16", "32x32x16") "_ktail"},
+         {REGTILE_DMA_NAME("bf16", "16x16x32"), REGTILE_DMA_NAME("bf16", "16x16x32") "_ktail"}},
+        {{REGTILE_DMA_NAME("f16", "32x32x16"), REGTILE_DMA_NAME("f16", "32x32x16") "_ktail"},
+         {REGTILE_DMA_NAME("f16", "16x16x32"), REGTILE_DMA_NAME("f16", "16x16x32") "_ktail"}}};
 #undef REGTILE_DMA_NAME
+    *name = names[f16][shape == 16][ktail];
+    if (f16) return ktail ? launch_dma_shape<true, true>(p, s, shape) : launch_dma_shape<true, false>(p, s, shape);
+    return ktail ? launch_dma_shape<false, true>(p, s, shape) : launch_dma_shape<false, false>(p, s, shape);
 }
 
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)

@@ -32,11 +32,12 @@ hipError_t launch_f32_regtile_small(const Problem &p, hipStream_t s, const char 
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name);
 // 16-bit operand kernels: `f16` selects IEEE fp16 operands, otherwise bf16.
 hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name, bool f16);
-// MFMA kernels; `shape` 32 selects 32x32x16 fragments, 16 selects 16x16x32 (full aligned
-// tiles only, others keep the 32x32x16 register-staged kernel).
+// MFMA kernels; `shape` 32 selects 32x32x16 fragments, 16 selects 16x16x32 (on the LDS-DMA
+// kernel only; problems it does not take keep the 32x32x16 register-staged kernel).
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16);
-// Full aligned tiles only; return hipErrorNotSupported without launching otherwise.
+// K-contiguous A and B with 16-byte aligned rows, K a multiple of 8, at least 128 tiles of
+// 256x256 (M, N and K may end inside a tile); hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16);
 // "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) on full

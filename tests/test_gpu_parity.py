@@ -195,6 +195,43 @@ def test_16bit_dma_kernel_on_ragged_m_n(dtype, shape, alpha, beta, mode):
         assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})", n_random=30000)
 
 
+# K ending inside the last 64-deep slab (K a multiple of 8): that slab's chunks past K load as
+# zeros on both operands.
+DMA_KTAIL = [("bf16", rt.ALGO_BF16_MFMA, (4096, 4096, 1000)), ("bf16", rt.ALGO_BF16_MFMA, (4100, 8000, 8)),
+             ("f16", rt.ALGO_BF16_MFMA, (8192, 4096, 72)), ("bf16", rt.ALGO_BF16_MFMA_16X16, (4096, 4096, 1000)),
+             ("bf16", rt.ALGO_BF16_MFMA, (3999, 4101, 1000))]
+
+
+@pytest.mark.parametrize("dtype,algo,shape", DMA_KTAIL,
+                         ids=[f"{d}-{a}-{'x'.join(map(str, s))}" for d, a, s in DMA_KTAIL])
+def test_16bit_dma_kernel_k_tail(dtype, algo, shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.25, beta=-0.5, seed=M + N + 3 * K)
+    announce(f"{dtype} DMA K tail algo={algo} {shape}")
+    got = run(inp, torch, algo).cpu().numpy()
+    name = rt.last_kernel()
+    assert "_dma_" in name and name.endswith("_ktail"), name
+    if M * N * K <= 5_000_000_000:
+        assert_parity_full(inp, got, f"{dtype} {shape} ({name})")
+    else:
+        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})", n_random=30000)
+
+
+def test_16bit_dma_kernel_k_tail_integer_bitwise():
+    # any value read past K (garbage beyond the row's end) would show in an exact result
+    rng = np.random.Generator(np.random.PCG64(81))
+    M, N, K = 4096, 4096, 1000
+    A = gi.f32_to_bf16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_bf16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, A, Bt, None)
+    announce("bf16 DMA K tail integer bitwise")
+    got = run(inp, torch).cpu().numpy()
+    assert rt.last_kernel().endswith("_ktail"), rt.last_kernel()
+    I, J = sample_positions(M, N, n_random=50000, seed=3)
+    ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref)
+
+
 # ---- bitwise: integer-valued operands (every partial sum exact in fp32) ---------------------
 @pytest.mark.parametrize("algo", F32_ALGOS)
 def test_f32_integer_inputs_are_bitwise_exact(algo):
