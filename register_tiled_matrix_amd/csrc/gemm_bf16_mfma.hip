@@ -350,9 +350,9 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
         *name = kLayoutNames[f16][big][lay][vec && !(p.ta && !p.tb)];
         return f16 ? launch_layout<true>(p, s, vec, big) : launch_layout<false>(p, s, vec, big);
     }
-    // Enough 256x256 tiles to fill the chip, K a whole number of slabs and 16-byte aligned
-    // rows: the LDS-DMA kernel, else the register-staged kernel below.
-    if ((int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 128) {
+    // K a multiple of 8 and 16-byte aligned rows: the LDS-DMA kernel, else the
+    // register-staged kernel below.
+    {
         const hipError_t e = launch_bf16_mfma_dma(p, s, name, shape, f16);
         if (e != hipErrorNotSupported) return e;
     }

@@ -36,8 +36,9 @@ hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name,
 // kernel only; problems it does not take keep the 32x32x16 register-staged kernel).
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16);
-// K-contiguous A and B with 16-byte aligned rows, K a multiple of 8, at least 128 tiles of
-// 256x256 (M, N and K may end inside a tile); hipErrorNotSupported without launching otherwise.
+// K-contiguous A and B with 16-byte aligned rows and K a multiple of 8 (M, N and K may end
+// inside a tile; 256x256 tiles, or 128x128 up to 128 tiles of 256x256);
+// hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16);
 // "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) on full
