@@ -15,6 +15,7 @@ ladder (algorithm 2).
     python -m register_tiled_matrix_amd.tune probe --build none   # CPU: build the gfx950 probes
     python -m register_tiled_matrix_amd.tune probe valu           # GPU: FMA issue rate, VGPR banks
     python -m register_tiled_matrix_amd.tune datadep              # GPU: bf16 rate against input data
+    python -m register_tiled_matrix_amd.tune shapes               # GPU: fp32 / bf16 on more shapes
 
 Correctness of each variant is checked bitwise against the naive rung of the default library:
 every fp32 rung accumulates each output with fmaf over k in natural order, so any micro-tile
@@ -322,6 +323,60 @@ def cmd_datadep(args) -> int:
     return 0
 
 
+SHAPES_F32 = [(4096, 4096, 4096), (8192, 8192, 8192), (1000, 1500, 777), (16384, 128, 4096), (256, 256, 256),
+              (2048, 2048, 2048), (4096, 2048, 4096), (3072, 3072, 3072), (1024, 1024, 8192), (3000, 2000, 512),
+              (8190, 8190, 1023)]
+SHAPES_16 = [(8192, 8192, 8192), (8000, 8000, 8192), (6000, 6000, 6000), (4096, 4096, 4096), (4000, 4000, 4000),
+             (2048, 4096, 4096), (2048, 2048, 8192), (1536, 1536, 8192), (1024, 1024, 16384), (3000, 5000, 2000),
+             (8190, 8190, 8190)]
+
+
+def cmd_shapes(args) -> int:
+    """fp32 and bf16 through the default entry points (row-major A; B row-major for fp32,
+    column-major for bf16) on shapes beyond the five workloads: kernel chosen, median time."""
+    import numpy as np
+    import torch
+
+    import register_tiled_matrix_amd as rt
+
+    if not torch.cuda.is_available():
+        print("tune shapes needs a GPU", file=sys.stderr)
+        return 2
+    rt.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cuda").manual_seed(0)
+    print("| dtype | M x N x K | kernel | median ms | TFLOP/s | % of peak |\n|---|---|---|---|---|---|")
+    for dtype, shapes in (("f32", SHAPES_F32), ("bf16", SHAPES_16)):
+        for M, N, K in shapes:
+            if dtype == "f32":
+                A = torch.rand(M, K, device="cuda", generator=g) * 2 - 1
+                B = torch.rand(K, N, device="cuda", generator=g) * 2 - 1
+                call = (M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0.0)
+                fn, peak = rt.gemm_f32_raw, 157.3
+            else:
+                A = torch.randn(M, K, device="cuda", generator=g).bfloat16()
+                B = torch.randn(N, K, device="cuda", generator=g).bfloat16()  # column-major K x N
+                call = (M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), K, 0.0)
+                fn, peak = rt.gemm_bf16_raw, 2516.6
+            C = torch.empty(M, N, device="cuda")
+            launch = lambda: fn(*call, C.data_ptr(), N, stream)
+            for _ in range(args.warmup):
+                assert launch() == 0
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                a.record()
+                launch()
+                b.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            print(f"| {dtype} | {M} x {N} x {K} | `{rt.last_kernel()}` | {ms:.4f} | {tf:.1f} | {100 * tf / peak:.1f} |",
+                  flush=True)
+            del A, B, C
+    return 0
+
+
 def _ladder_report(rows) -> str:
     out = ["# Kernel ladder on every configuration", "",
            "Command (repository root, one MI355X):", "", "```",
@@ -429,6 +484,9 @@ def main(argv=None) -> int:
                                        "MFMA rate, LDS access patterns")
     pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "none"])
     pr.add_argument("--build", action="store_true", help="recompile the probe program first")
+    sh = sub.add_parser("shapes", help="fp32 and bf16 default entry points on more shapes")
+    sh.add_argument("--steps", type=int, default=20)
+    sh.add_argument("--warmup", type=int, default=40)
     dd = sub.add_parser("datadep", help="bf16 8192^3 rate against the operands' data")
     dd.add_argument("--steps", type=int, default=20)
     dd.add_argument("--rounds", type=int, default=4)
@@ -442,7 +500,7 @@ def main(argv=None) -> int:
         sys.path.insert(0, root)
     t0 = time.time()
     rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report,
-          "probe": cmd_probe, "datadep": cmd_datadep}[args.cmd](args)
+          "probe": cmd_probe, "datadep": cmd_datadep, "shapes": cmd_shapes}[args.cmd](args)
     print(f"# {args.cmd} done in {time.time() - t0:.1f} s", file=sys.stderr)
     return rc
 
