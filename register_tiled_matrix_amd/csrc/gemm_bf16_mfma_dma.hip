@@ -63,7 +63,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // KTAIL: K ends inside the last slab (K a multiple of 8, so each 16-byte chunk lies wholly
     // before or wholly past K); that slab's chunks past K are loaded from an offset past the
     // descriptor's end, which puts zeros in LDS.
-    static_assert(!KTAIL || !ANY_ROW, "the K tail is masked on the DMA operands");
+
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
 
@@ -145,25 +145,30 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int B_BLOCKS = ANY_ROW ? 2 : 1;
     static_assert(!ANY_ROW || (RLEN / 4) * KCH == B_BLOCKS * NT, "two 4 x 8 blocks per thread");
     constexpr int NBL = ANY_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
+    // The row operand's loads go through a descriptor over its K rows (of ld_row elements)
+    // from the tile's first column: rows at or past K read zeros (the K tail); columns past M
+    // or N read whatever follows in memory, or zeros past the end, and only feed outputs that
+    // are never stored.
     const uint16_t *const rsrc_base = A_ROW ? A + m0 : B + n0;
     const int64_t ld_row = A_ROW ? lda : ldb;
+    const rsrc_t row_rsrc = make_rsrc(rsrc_base, (uint32_t)(K * ld_row * 2));
     uint32_t bl[B_BLOCKS][8], bh[B_BLOCKS][8];
     int brow_n[B_BLOCKS], brow_kc[B_BLOCKS];
-    const uint16_t *brow_src[B_BLOCKS];
+    uint32_t brow_off[B_BLOCKS];
 #pragma unroll
     for (int i = 0; i < B_BLOCKS; ++i) {
         const int b = tid + NT * i;
         brow_n[i] = (b % (RLEN / 4)) * 4;
         brow_kc[i] = b / (RLEN / 4);
-        brow_src[i] = rsrc_base + (int64_t)(brow_kc[i] * 8) * ld_row + brow_n[i];
+        brow_off[i] = (uint32_t)((brow_kc[i] * 8) * ld_row + brow_n[i]) * 2u;
     }
     auto load_brow = [&](int slab) {
-        const int64_t k0 = (int64_t)min(slab, nslabs - 1) * BK;
+        const uint32_t k0 = (uint32_t)min(slab, nslabs - 1) * BK;
 #pragma unroll
         for (int i = 0; i < B_BLOCKS; ++i)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(brow_src[i] + (k0 + kk) * ld_row);
+                const uint2 v = load_b64_buf(row_rsrc, brow_off[i], (k0 + kk) * (uint32_t)ld_row * 2u);
                 bl[i][kk] = v.x;
                 bh[i][kk] = v.y;
             }
@@ -618,37 +623,41 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)
 // or "t t" (A stored K x M, B stored N x K). The K-contiguous operand goes over LDS DMA, the
 // other as 8-byte row runs through registers, transposed into the slab. Returns
-// hipErrorNotSupported (launching nothing) unless the problem is made of full tiles, the DMA
-// operand's rows are 16-byte aligned within 32-bit tile offsets, and the row operand allows
-// 8-byte loads.
+// hipErrorNotSupported (launching nothing) unless there are at least 128 tiles of 256x256, K
+// is a multiple of 8, the DMA operand's rows are 16-byte aligned within 32-bit tile offsets,
+// and the row operand's rows are 8-byte aligned within 32-bit offsets over all of K. M, N and
+// K may end inside a tile.
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16) {
     const bool nn = !p.ta && !p.tb, tt = p.ta && p.tb;
     const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31))
                            : (p.ldb % 8 == 0 && aligned16(p.B) && (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31));
-    const bool rows_ok = nn ? (p.ldb % 4 == 0 && aligned8(p.B)) : (p.lda % 4 == 0 && aligned8(p.A));
-    const bool ok = (nn || tt) && DMA_RING32 == 5 && dma_ok && rows_ok && p.M % DMA_BM == 0 &&
-                    p.N % DMA_BN == 0 && p.K % DMA_BK == 0 && p.K > 0 &&
-                    (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) &&
-                    (int64_t)(p.M / DMA_BM) * (p.N / DMA_BN) >= 128;
+    const int64_t ld_row = nn ? p.ldb : p.lda;
+    const bool rows_ok = ld_row % 4 == 0 && aligned8(nn ? p.B : p.A) &&
+                         ((int64_t)p.K + 128) * ld_row * 2 + 512 < (int64_t(1) << 31);
+    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
+    const bool ok = (nn || tt) && DMA_RING32 == 5 && dma_ok && rows_ok && p.K % 8 == 0 && p.K > 0 &&
+                    (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) && tiles >= 128;
     if (!ok) return hipErrorNotSupported;
+    const bool ktail = p.K % DMA_BK != 0;
 #define REGTILE_DMA_ROWS_NAME(elt, lay)                                                            \
     elt "_mfma32x32x16_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)   \
         "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_" lay
-    if (nn) {
-        if (f16) {
-            *name = REGTILE_DMA_ROWS_NAME("f16", "nn");
-            return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, 1>(p, s);
-        }
-        *name = REGTILE_DMA_ROWS_NAME("bf16", "nn");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, 1>(p, s);
-    }
-    if (f16) {
-        *name = REGTILE_DMA_ROWS_NAME("f16", "tt");
-        return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, true, 5, 2>(p, s);
-    }
-    *name = REGTILE_DMA_ROWS_NAME("bf16", "tt");
-    return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, false, 5, 2>(p, s);
+    static const char *const names[2][2][2] = {
+        {{REGTILE_DMA_ROWS_NAME("bf16", "tt"), REGTILE_DMA_ROWS_NAME("bf16", "tt") "_ktail"},
+         {REGTILE_DMA_ROWS_NAME("bf16", "nn"), REGTILE_DMA_ROWS_NAME("bf16", "nn") "_ktail"}},
+        {{REGTILE_DMA_ROWS_NAME("f16", "tt"), REGTILE_DMA_ROWS_NAME("f16", "tt") "_ktail"},
+         {REGTILE_DMA_ROWS_NAME("f16", "nn"), REGTILE_DMA_ROWS_NAME("f16", "nn") "_ktail"}}};
 #undef REGTILE_DMA_ROWS_NAME
+    *name = names[f16][nn][ktail];
+#define REGTILE_ROWS_LAUNCH(F16_, ROWS_, KT_) \
+    launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, ROWS_, KT_>(p, s)
+    if (f16) {
+        if (nn) return ktail ? REGTILE_ROWS_LAUNCH(true, 1, true) : REGTILE_ROWS_LAUNCH(true, 1, false);
+        return ktail ? REGTILE_ROWS_LAUNCH(true, 2, true) : REGTILE_ROWS_LAUNCH(true, 2, false);
+    }
+    if (nn) return ktail ? REGTILE_ROWS_LAUNCH(false, 1, true) : REGTILE_ROWS_LAUNCH(false, 1, false);
+    return ktail ? REGTILE_ROWS_LAUNCH(false, 2, true) : REGTILE_ROWS_LAUNCH(false, 2, false);
+#undef REGTILE_ROWS_LAUNCH
 }
 
 }  // namespace regtile

@@ -75,6 +75,20 @@ __device__ __forceinline__ void dma16_buf(rsrc_t r, uint32_t voff, uint32_t soff
 #endif
 }
 
+// 8 bytes per lane at buffer byte offset voff + soff (soff wave-uniform); zero past the
+// descriptor's end.
+__device__ __forceinline__ uint2 load_b64_buf(rsrc_t r, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+#else
+    (void)r;
+    (void)voff;
+    (void)soff;
+    return make_uint2(0u, 0u);
+#endif
+}
+
 // One fp32 per lane at buffer byte offset voff + soff (soff wave-uniform).
 __device__ __forceinline__ float load_f32_buf(rsrc_t r, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)

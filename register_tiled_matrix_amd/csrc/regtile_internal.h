@@ -41,8 +41,9 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
 // hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16);
-// "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) on full
-// aligned tiles; hipErrorNotSupported without launching otherwise.
+// "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) with at
+// least 128 tiles of 256x256 and K a multiple of 8; hipErrorNotSupported without launching
+// otherwise.
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16);
 
 // Host-side launch checks.

@@ -140,12 +140,14 @@ def test_16bit_layouts_8192_sampled(ta, tb, dtype):
 def test_16bit_gathered_layouts_large_ragged(shape, ta, tb, dtype):
     # enough 256x256 tiles for the eight-wave gathered kernel, ragged on every side; the second
     # shape's odd leading dimensions (lda = M for A stored K x M, ldb = N for B stored K x N)
-    # make every 8-byte run unaligned
+    # make every 8-byte run unaligned. "n n" and "t t" with 8-byte aligned row runs take the
+    # DMA kernel instead (the first shape).
     M, N, K = shape
     inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=0.75, beta=0.5, seed=M + N + K + 2 * ta + tb)
     announce(f"{dtype} gathered layout {ta}{tb} {shape}")
     got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA)
-    assert "256x256x64_w2x4" in name, name
+    rows_dma = ta == tb and K % 8 == 0 and (N if ta == 0 else M) % 4 == 0
+    assert ("_dma_" in name) if rows_dma else ("256x256x64_w2x4" in name), name
     assert_parity_sampled(inp, got, f"{dtype} layout ({ta},{tb}) {shape} ({name})", n_random=50000)
 
 
@@ -174,3 +176,47 @@ def test_16bit_row_operand_on_the_dma_kernel(ta, tb, dtype, dist):
         assert np.array_equal(got[I, J].astype(np.float64), ref), name
     else:
         assert_parity_sampled(inp, got, f"{dtype} row operand ({ta},{tb}) ({name})", n_random=50000)
+
+
+# (the row operand's leading dimension, N for "n n" and M for "t t", a multiple of 4 for its
+# 8-byte runs, yet not of 256)
+ROWS_RAGGED = [("bf16", 0, 0, (8000, 4100, 1000), "normal"), ("f16", 1, 1, (4100, 8000, 72), "normal"),
+               ("bf16", 0, 0, (4097, 8188, 64), "integer"), ("bf16", 1, 1, (4000, 4101, 200), "integer")]
+
+
+@pytest.mark.parametrize("dtype,ta,tb,shape,dist", ROWS_RAGGED,
+                         ids=[f"{d}-{a}{b}-{'x'.join(map(str, s))}-{t}" for d, a, b, s, t in ROWS_RAGGED])
+def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
+    # "n n" / "t t" on the DMA kernel with M, N and K ending inside a tile: the row operand's
+    # descriptor reads zeros past K; its columns past M / N only feed outputs that are dropped.
+    # C has padded rows whose padding must stay untouched.
+    M, N, K = shape
+    if dist == "integer":
+        rng = np.random.Generator(np.random.PCG64(M + N + K))
+        to_bits = gi.f32_to_bf16_bits if dtype == "bf16" else gi.f32_to_f16_bits
+        A = to_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+        Bt = to_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+        inp = gi.GemmInputs(M, N, K, 1.0, 0.0, dtype, True, A, Bt, None)
+    else:
+        inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=-0.75, beta=0.5, seed=M + K)
+    announce(f"{dtype} row operand DMA ragged {ta}{tb} {shape} {dist}")
+    A, B, C0 = _operands(inp, ta, tb)
+    big = torch.full((M, N + 5), -77.0, device="cuda")
+    C = big[:, :N]
+    if inp.C is not None:
+        C.copy_(C0)
+    fn = {"bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[dtype]
+    fn(A, B, C, alpha=inp.alpha, beta=inp.beta)
+    torch.cuda.synchronize()
+    name = rt.last_kernel()
+    lay = "_nn" if ta == 0 else "_tt"
+    assert "_dma_" in name and (name.endswith(lay) or name.endswith(lay + "_ktail")), name
+    assert name.endswith("_ktail") == (K % 64 != 0), name
+    assert torch.all(big[:, N:] == -77.0).item(), "a store landed past column N"
+    got = C.cpu().numpy()
+    if dist == "integer":
+        I, J = sample_positions(M, N, n_random=50000, seed=9)
+        ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+        assert np.array_equal(got[I, J].astype(np.float64), ref), name
+    else:
+        assert_parity_full(inp, got, f"{dtype} ({ta},{tb}) {shape} ({name})")
