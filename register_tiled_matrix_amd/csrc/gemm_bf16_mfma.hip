@@ -40,7 +40,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * KCH + (chu
 
 // A whole run of 16 (8) bytes at any 2-byte-aligned address, as one global_load_dwordx4
 // (dwordx2): the ROCm driver runs gfx9-class GPUs in unaligned-access mode, so multi-dword
-// global loads take any address (the compiler emits the same single load for these).
+// global loads take any address (the compiler emits the same single load for these copies).
 __device__ __forceinline__ uint4 load16_any(const uint16_t *p) {
     uint4 r;
     __builtin_memcpy(&r, p, 16);
@@ -79,34 +79,14 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ p, bool
     return r;
 }
 
-// A 4 x 8 block of an operand stored K-major-outer (element (r, k) at p[k * ld + r] relative
-// to the block's first element, r < 4 along the contiguous M or N dimension, k < 8): read as
-// 8 runs of 4 elements (one 8-byte load per whole run, aligned when `vec`, else unaligned;
-// predicated 2-byte loads for a run cut by the edge; zero outside r_left x k_left) and
-// transposed in registers into 4 chunks of 8 consecutive k, the K-contiguous form the
-// fragment reads expect. out[j] holds row r = j.
-template <bool EDGE>
-__device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, int64_t ld, bool vec,
-                                              int r_left, int k_left, uint4 out[4]) {
-    uint32_t lo[8], hi[8];  // k = kk: rows 0, 1 in lo (low half = row 0), rows 2, 3 in hi
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const uint16_t *q = p + kk * ld;
-        if (!EDGE || (kk < k_left && r_left >= 4)) {
-            const uint2 v = vec ? *reinterpret_cast<const uint2 *>(q) : load8_any(q);
-            lo[kk] = v.x;
-            hi[kk] = v.y;
-        } else {
-            uint32_t e[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[j] = (!EDGE || (kk < k_left && j < r_left)) ? q[j] : 0u;
-            lo[kk] = e[0] | (e[1] << 16);
-            hi[kk] = e[2] | (e[3] << 16);
-        }
-    }
-    // out[j] dword d = (k = 2d in the low half, k = 2d + 1 in the high half) of row j (written
-    // out here rather than through mfma::transpose_4x8: the shared helper compiles to a
-    // different, measurably slower schedule in this kernel)
+// A 4 x 8 block of an operand stored K-major-outer (element (r, k) at base[k * ld + r] relative
+// to the block's first element, r < 4 along the contiguous M or N dimension, k < 8), read as
+// 8 runs of 4 elements along M or N and transposed in registers into 4 chunks of 8
+// consecutive k, the K-contiguous form the fragment reads expect: out[j] holds row r = j,
+// dword d = (k = 2d in the low half, k = 2d + 1 in the high half). The transpose is written
+// out here rather than through mfma::transpose_4x8: the shared helper compiles to a
+// different, measurably slower schedule in this kernel.
+__device__ __forceinline__ void transpose_block(const uint32_t lo[8], const uint32_t hi[8], uint4 out[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t *src = j < 2 ? lo : hi;
@@ -119,6 +99,48 @@ __device__ __forceinline__ void load_block_mn(const uint16_t *__restrict__ p, in
     }
 }
 
+// The block through a buffer descriptor over the slab's K rows that lie before K (base: the
+// slab's first row at the tile's first column, `rows` rows of `ld` elements), for ld a
+// multiple of 4, so that no 8-byte run crosses the end of a row: rows past K read zeros;
+// columns past M or N read whatever follows in the row, or zeros past the descriptor, and
+// only feed outputs the epilogue drops. `off` is the block's byte offset from the base.
+// Eight buffer_load_dwordx2 with one lane offset and uniform row offsets, no predication.
+__device__ __forceinline__ void load_block_mn_buf(const uint16_t *base, int64_t ld, int rows, uint32_t off,
+                                                  uint4 out[4]) {
+    const mfma::rsrc_t r = mfma::make_rsrc(base, (uint32_t)(rows * ld * 2));
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const uint2 v = mfma::load_b64_buf(r, off, (uint32_t)(kk * ld * 2));
+        lo[kk] = v.x;
+        hi[kk] = v.y;
+    }
+    transpose_block(lo, hi, out);
+}
+
+// The block for any ld: whole runs (all 4 columns before the edge, k before K) as one
+// unaligned 8-byte load, runs cut by an edge element by element; zero outside r_left x k_left.
+__device__ __forceinline__ void load_block_mn_any(const uint16_t *__restrict__ p, int64_t ld, int r_left,
+                                                  int k_left, uint4 out[4]) {
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const uint16_t *q = p + kk * ld;
+        if (kk < k_left && r_left >= 4) {
+            const uint2 v = load8_any(q);
+            lo[kk] = v.x;
+            hi[kk] = v.y;
+        } else {
+            uint32_t e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) e[j] = (kk < k_left && j < r_left) ? q[j] : 0u;
+            lo[kk] = e[0] | (e[1] << 16);
+            hi[kk] = e[2] | (e[3] << 16);
+        }
+    }
+    transpose_block(lo, hi, out);
+}
+
 // A_MN: A stored K x M (M-contiguous); B_MN: B stored K x N (N-contiguous). The LDS slab is
 // K-contiguous either way; an MN-contiguous operand is gathered with scalar loads that are
 // coalesced across lanes (consecutive lanes take consecutive M / N indices).
@@ -127,7 +149,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, bool EDGE, bool VEC, bool VE
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n, int mn_vec) {
+    int tiles_m, int tiles_n) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int MI = WTM / 32, NI = WTN / 32;
@@ -158,20 +180,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
 
     // MN-contiguous staging: thread t owns the 4 x 8 block at rows 4 (t % (B/4)), chunk
     // t / (B/4) of the slab (B = BM or BN): consecutive lanes read consecutive 8-byte runs
-    // along the contiguous dimension at one k. `mn_vec` (uniform) says the runs are 8-byte
-    // aligned (leading dimension a multiple of 4, operand 8-byte aligned).
+    // along the contiguous dimension at one k (through a descriptor when the leading
+    // dimension is a multiple of 4, else as global loads with edge checks).
     static_assert(!A_MN || BM * BK == 32 * NT, "one 4 x 8 block of A per thread");
     static_assert(!B_MN || BN * BK == 32 * NT, "one 4 x 8 block of B per thread");
     const int amn_row = (tid % (BM / 4)) * 4, amn_chunk = tid / (BM / 4);
     const int bmn_row = (tid % (BN / 4)) * 4, bmn_chunk = tid / (BN / 4);
-    const bool vec_mn = mn_vec != 0;
 
     uint4 ra[A_CH], rb[B_CH];
     auto load_slab = [&](int k0) {
         if (A_MN) {
-            const int kc = k0 + amn_chunk * 8;
-            load_block_mn<EDGE>(A + (int64_t)kc * lda + m0 + amn_row, lda, vec_mn, M - (m0 + amn_row),
-                                K - kc, ra);
+            if ((lda & 3) == 0)
+                load_block_mn_buf(A + (int64_t)k0 * lda + m0, lda, min(BK, K - k0),
+                                  (uint32_t)(amn_chunk * 8 * lda + amn_row) * 2u, ra);
+            else
+                load_block_mn_any(A + (int64_t)(k0 + amn_chunk * 8) * lda + m0 + amn_row, lda,
+                                  M - (m0 + amn_row), K - (k0 + amn_chunk * 8), ra);
         } else {
 #pragma unroll
             for (int i = 0; i < A_CH; ++i)
@@ -180,9 +204,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
                                               K - k0 - ld_chunk * 8);
         }
         if (B_MN) {
-            const int kc = k0 + bmn_chunk * 8;
-            load_block_mn<EDGE>(B + (int64_t)kc * ldb + n0 + bmn_row, ldb, vec_mn, N - (n0 + bmn_row),
-                                K - kc, rb);
+            if ((ldb & 3) == 0)
+                load_block_mn_buf(B + (int64_t)k0 * ldb + n0, ldb, min(BK, K - k0),
+                                  (uint32_t)(bmn_chunk * 8 * ldb + bmn_row) * 2u, rb);
+            else
+                load_block_mn_any(B + (int64_t)(k0 + bmn_chunk * 8) * ldb + n0 + bmn_row, ldb,
+                                  N - (n0 + bmn_row), K - (k0 + bmn_chunk * 8), rb);
         } else {
 #pragma unroll
             for (int i = 0; i < B_CH; ++i)
@@ -272,12 +299,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
 
 template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16, bool A_MN = false,
           bool B_MN = false>
-hipError_t launch_cfg(const Problem &p, hipStream_t s, bool mn_vec = false) {
+hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16, A_MN, B_MN>),
                        dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
                        (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,
-                       p.ldc, tiles_m, tiles_n, mn_vec ? 1 : 0);
+                       p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -292,27 +319,22 @@ hipError_t launch_pick(const Problem &p, hipStream_t s, bool edge, bool vec) {
 // Operands other than K-contiguous A and B: 128x128 tiles, edge-predicated kernel; `vec` only
 // matters for a K-contiguous operand.
 template <int BM, int BN, int WM, int WN, bool F16>
-hipError_t launch_layout_tile(const Problem &p, hipStream_t s, bool vec, bool mn_vec) {
+hipError_t launch_layout_tile(const Problem &p, hipStream_t s, bool vec) {
     const bool a_mn = p.ta, b_mn = !p.tb;
     if (a_mn && b_mn)
-        return launch_cfg<BM, BN, WM, WN, true, false, F16, true, true>(p, s, mn_vec);
+        return launch_cfg<BM, BN, WM, WN, true, false, F16, true, true>(p, s);
     if (a_mn)
-        return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, true, false>(p, s, mn_vec)
-                   : launch_cfg<BM, BN, WM, WN, true, false, F16, true, false>(p, s, mn_vec);
-    return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, false, true>(p, s, mn_vec)
-               : launch_cfg<BM, BN, WM, WN, true, false, F16, false, true>(p, s, mn_vec);
+        return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, true, false>(p, s)
+                   : launch_cfg<BM, BN, WM, WN, true, false, F16, true, false>(p, s);
+    return vec ? launch_cfg<BM, BN, WM, WN, true, true, F16, false, true>(p, s)
+               : launch_cfg<BM, BN, WM, WN, true, false, F16, false, true>(p, s);
 }
 
 // 256x256 tiles of eight waves when there are enough of them to fill the chip, else 128x128.
 template <bool F16>
 hipError_t launch_layout(const Problem &p, hipStream_t s, bool vec, bool big) {
-    const bool a_mn = p.ta, b_mn = !p.tb;
-    // 8-byte runs along M / N: leading dimension a multiple of 4 and an 8-byte aligned base
-    // for every MN-contiguous operand
-    const bool mn_vec = (!a_mn || ((p.lda % 4) == 0 && aligned8(p.A))) &&
-                        (!b_mn || ((p.ldb % 4) == 0 && aligned8(p.B)));
-    return big ? launch_layout_tile<256, 256, 2, 4, F16>(p, s, vec, mn_vec)
-               : launch_layout_tile<128, 128, 2, 2, F16>(p, s, vec, mn_vec);
+    return big ? launch_layout_tile<256, 256, 2, 4, F16>(p, s, vec)
+               : launch_layout_tile<128, 128, 2, 2, F16>(p, s, vec);
 }
 
 #define REGTILE_STAGED_NAMES(elt, tile)                                                        \
@@ -344,6 +366,11 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
         if (e != hipErrorNotSupported) return e;
     }
     if (p.ta || !p.tb) {  // not the native K-contiguous pair
+        // an M/N-contiguous operand is gathered through one descriptor per slab of 64 of its
+        // rows, in 32-bit offsets: rows of 2^24 elements or more go to the naive rung
+        if ((p.ta && (int64_t)BK * p.lda * 2 >= (int64_t(1) << 31)) ||
+            (!p.tb && (int64_t)BK * p.ldb * 2 >= (int64_t(1) << 31)))
+            return launch_bf16_naive(p, s, name, f16);
         const bool vec = (p.ta ? (p.ldb % 8) == 0 && aligned16(p.B) : (p.lda % 8) == 0 && aligned16(p.A));
         const int lay = (p.ta && p.tb) ? 0 : p.ta ? 1 : 2;  // tt: A K x M, B N x K; tn; nn
         const bool big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
