@@ -105,6 +105,19 @@ def _time_steps(torch, fn, steps, warmup):
     return wall_ms, region_ms, float(np.mean(kern)), float(np.min(kern))
 
 
+def _steady_median(torch, step):
+    """Median kernel time (ms) of 30 event-timed launches after warming up for at least 50
+    launches and 100 ms (small problems ramp the clock slowly)."""
+    t_end, n = time.perf_counter() + 0.1, 0
+    while n < 50 or time.perf_counter() < t_end:
+        step()
+        n += 1
+        if n % 50 == 0:
+            torch.cuda.synchronize()
+    _, kern = _kernel_times(torch, step, 30, 0)
+    return float(np.median(kern))
+
+
 def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
     """Every configuration through the default entry points: at least 50 warm-up launches and
     100 ms, then 30 timed launches; TFLOP/s from the median event time, and the fraction of the
@@ -134,15 +147,7 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
 
         step()
         kname = rt.last_kernel()
-        # warm up for at least 50 launches and 100 ms (small problems ramp the clock slowly)
-        t_end, n = time.perf_counter() + 0.1, 0
-        while n < 50 or time.perf_counter() < t_end:
-            step()
-            n += 1
-            if n % 50 == 0:
-                torch.cuda.synchronize()
-        _, kern = _kernel_times(torch, step, 30, 0)
-        med = float(np.median(kern))
+        med = _steady_median(torch, step)
         tf = wc.flop / (med * 1e-3) / 1e12
         res[wname] = {"shape": [wc.M, wc.N, wc.K], "kernel": kname, "kernel_ms_median": round(med, 4),
                       "TFLOP/s": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4)}
@@ -434,7 +439,7 @@ def main():
                             raise rt.RegtileError(st, rt.strerror(st))
 
                     step_l()
-                    _, kms, _ = _time(torch, step_l, max(10, args.steps // 2), 3)
+                    kms = _steady_median(torch, step_l)
                     code = ("n", "t")[ta] + ("n", "t")[tb]
                     lay[f"{wname}_{code}"] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
                                               "TFLOP/s": round(wl.flop / (kms * 1e-3) / 1e12, 2)}
@@ -446,13 +451,15 @@ def main():
     if not args.no_ladder:
         ladder = {}
         for algo, label in ((rt.ALGO_F32_NAIVE, "naive"), (rt.ALGO_F32_LDS, "lds_32x32"),
-                            (rt.ALGO_F32_REGTILE, "regtile_8x8")):
+                            (rt.ALGO_F32_REGTILE, "regtile_8x16")):
             def step(algo=algo):
                 st = rt.regtile_gemm_f32_algo(algo, *f32_args)
                 if st:
                     raise rt.RegtileError(st, rt.strerror(st))
-            reps = 3 if algo != rt.ALGO_F32_REGTILE else args.steps
-            _, kms, _ = _time(torch, step, reps, 1)
+            if algo == rt.ALGO_F32_REGTILE:
+                kms = _steady_median(torch, step)
+            else:  # 9-31 ms per launch: three launches after one
+                _, kms, _ = _time(torch, step, 3, 1)
             ladder[label] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
                              "TFLOP/s": round(flop / (kms * 1e-3) / 1e12, 3)}
         if "bf16_8192" in out:
