@@ -35,6 +35,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_MFMA "
                "SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES")
+LADDER_COUNTERS = "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAVES"
 COPY_BYTES = 1 << 30
 
 # workload -> (kernel label as regtile_last_kernel() names it, substring of the kernel's symbol,
@@ -69,6 +70,10 @@ def passes(out):
         p.append((f"sq_{w}", ["rocprofv3", "--pmc", *SQ_COUNTERS.split(), "-d", os.path.join(out, f"sq_{w}"), "-o", "sq",
                               "--output-format", "csv", "--",
                               *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    p.append(("sq_ladder", ["rocprofv3", "--pmc", *LADDER_COUNTERS.split(), "-d", os.path.join(out, "sq_ladder"),
+                            "-o", "sq", "--output-format", "csv", "--", "python3", "-m",
+                            "register_tiled_matrix_amd.tune", "ladder", "--workloads", "f32_4096,bf16_8192",
+                            "--steps", "2", "--warmup", "1"], 300))
     return p
 
 
@@ -260,12 +265,48 @@ def summarize_sq(prof, out_md):
         f.write("\n".join(md) + "\n")
 
 
+def _short_kernel(name):
+    name = name.replace("void ", "").replace("regtile::(anonymous namespace)::", "").replace("regtile::", "")
+    return name.split("(int")[0]
+
+
+def summarize_ladder_sq(prof, out_md):
+    """Per kernel of the ladder (fp32 rungs at 4096^3, 16-bit rungs at 8192^3), mean per
+    dispatch: LDS, VALU and MFMA instructions per wave, LDS instructions per 1000 VALU, and the
+    share of LDS-active cycles lost to bank conflicts."""
+    d = _pmc(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv"))
+    per = collections.defaultdict(dict)
+    for (k, c), vs in d.items():
+        per[k][c] = sum(vs) / len(vs)
+    cmd = [_display(a, prof) for n, a, _ in passes(prof) if n == "sq_ladder"]
+    md = ["# Ladder rungs: LDS, VALU and MFMA instructions and LDS bank conflicts (rocprofv3 --pmc)", ""]
+    md += _cmd_block(cmd)
+    md += ["Mean per dispatch: fp32 rungs at 4096^3, 16-bit rungs at 8192^3 (every kernel the ladder launched). "
+           "SQ_INSTS_VALU counts the MFMA instructions too on this counter set. The last column is "
+           "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+           "| kernel | LDS instr / wave | VALU instr / wave | MFMA instr / wave | LDS per 1000 VALU | bank-conflict share |",
+           "|---|---|---|---|---|---|"]
+    for k, m in sorted(per.items(), key=lambda kv: _short_kernel(kv[0])):
+        if "regtile" not in k:
+            continue
+        waves = m.get("SQ_WAVES", 0) or 1
+        lds, valu, mfma = m.get("SQ_INSTS_LDS", 0) / waves, m.get("SQ_INSTS_VALU", 0) / waves, m.get("SQ_INSTS_MFMA", 0) / waves
+        act = m.get("SQ_LDS_IDX_ACTIVE", 0)
+        conf = f"{100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / act:.1f} %" if act else "-"
+        md.append(f"| `{_short_kernel(k)}` | {lds:.0f} | {valu:.0f} | {mfma:.0f} | "
+                  f"{1000 * lds / valu if valu else 0:.1f} | {conf} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(prof) -> int:
     prof = os.path.abspath(prof)
     summarize_trace(prof, os.path.join(PROFILES, "kernel_trace_f32_4096_bf16_8192.md"))
     summarize_traffic(prof, os.path.join(PROFILES, "pmc_traffic.json"),
                       os.path.join(PROFILES, "hbm_traffic_f32_4096_bf16_8192.md"))
     summarize_sq(prof, os.path.join(PROFILES, "sq_counters_f32_4096_bf16_8192.md"))
+    if os.path.exists(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv")):
+        summarize_ladder_sq(prof, os.path.join(PROFILES, "lds_counters_ladder_f32_4096_bf16_8192.md"))
     return 0
 
 
