@@ -68,9 +68,9 @@ enum regtile_algo_bf16 {
     REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
     REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
     REGTILE_BF16_MFMA = 2,   /* LDS-tiled, wave-level 32x32x16 MFMA fragments, fp32 accumulators */
-    REGTILE_BF16_MFMA_16X16 = 3 /* the same with 16x16x32 fragments on full aligned 256x256
-                                   tiles (other shapes as REGTILE_BF16_MFMA): the shape
-                                   comparison ("寄存器Tiling跨架构解析" section 3.1) */
+    REGTILE_BF16_MFMA_16X16 = 3 /* the same with 16x16x32 fragments where the LDS-DMA kernel
+                                   runs 256x256 tiles (other problems as REGTILE_BF16_MFMA):
+                                   the shape comparison ("寄存器Tiling跨架构解析" section 3.1) */
 };
 
 /*
@@ -146,9 +146,10 @@ int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint
  *                    1: B stored N x K row-major (column-major K x N), ldb >= max(1,K)
  *   the rest as gemm_f32 / gemm_bf16 / gemm_f16 at positions 4-15; -2 / -3 for a flag other
  *   than 0 or 1. gemm_f32 is (AUTO, 0, 0) and gemm_bf16 / gemm_f16 are (AUTO, 0, 1).
- * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit). On full
- * aligned tiles the 16-bit LDS-DMA kernel takes (0, 1), and (0, 0) / (1, 1) with the M- or
- * N-contiguous operand staged through registers; (1, 0) and edge tiles gather M- or
+ * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit). The
+ * 16-bit LDS-DMA kernel takes (0, 1) whenever K is a multiple of 8 and rows are 16-byte
+ * aligned, and (0, 0) / (1, 1) with at least 128 tiles of 256x256, the M- or N-contiguous
+ * operand staged through registers; other problems, (1, 0) among them, gather M- or
  * N-contiguous operands into K-contiguous LDS slabs with 8-byte loads.
  */
 int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
