@@ -14,6 +14,7 @@
 //         with constant and with random operands.
 //   mfma_sustained  the MFMA loop for 30 back-to-back launches of a few ms, with constant and with
 //         random bf16 operands: the clock the package sustains under matrix load alone.
+//   lds_tr  the lane mapping of ds_read_b64_tr_b16 (transposing 16-bit LDS read).
 //   lds   one kernel per LDS address pattern (16 bytes per lane); run under
 //         `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES` for the
 //         cycles and conflict cycles per instruction.
@@ -344,6 +345,37 @@ int run_fma_sustained() {
     return 0;
 }
 
+// ---- lds_tr: lane mapping of the transposing LDS read ---------------------------------------
+// ds_read_b64_tr_b16: every lane gives an address of 4 consecutive 16-bit elements. LDS holds
+// each element's own index; lane l reads row l of a 64-element-wide image (elements 64 l ..
+// 64 l + 3), all in bounds of the 16 KB array. Prints which source elements each lane receives.
+typedef short trv4i16 __attribute__((ext_vector_type(4)));
+__global__ void lds_tr_kernel(short *out) {
+    __shared__ short lds[8192];
+    for (int i = threadIdx.x; i < 8192; i += 64) lds[i] = (short)i;
+    __syncthreads();
+    const int l = threadIdx.x;
+    const trv4i16 v =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) trv4i16 *)(lds + 64 * l));
+    for (int j = 0; j < 4; ++j) out[l * 4 + j] = v[j];
+}
+
+int run_lds_tr() {
+    short *d;
+    CHECK(hipMalloc(&d, 256 * sizeof(short)));
+    hipLaunchKernelGGL(lds_tr_kernel, dim3(1), dim3(64), 0, 0, d);
+    CHECK(hipGetLastError());
+    static short h[256];
+    CHECK(hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost));
+    printf("| lane | receives (source lane . element) |\n|---|---|\n");
+    for (int l = 0; l < 20; ++l) {
+        printf("| %d |", l);
+        for (int j = 0; j < 4; ++j) printf(" %d.%d", h[l * 4 + j] / 64, h[l * 4 + j] % 64);
+        printf(" |\n");
+    }
+    return 0;
+}
+
 // ---- lds ----------------------------------------------------------------------------------
 __device__ __forceinline__ int key_row7(int row, int c) { return row * 128 + ((c ^ (row & 7)) * 16); }
 __device__ __forceinline__ int key_row7_row8(int row, int c) {
@@ -464,5 +496,6 @@ int main(int argc, char **argv) {
         rc |= run_mfma_sustained<true>();
     }
     if (!strcmp(what, "lds")) rc |= run_lds();
+    if (!strcmp(what, "lds_tr") || !strcmp(what, "all")) rc |= run_lds_tr();
     return rc;
 }

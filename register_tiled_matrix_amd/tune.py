@@ -482,7 +482,7 @@ def main(argv=None) -> int:
     lad.add_argument("--warmup", type=int, default=50)
     pr = sub.add_parser("probe", help="gfx950 facts: FP32 FMA issue rate and VGPR banks, "
                                        "MFMA rate, LDS access patterns")
-    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "none"])
+    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "lds_tr", "none"])
     pr.add_argument("--build", action="store_true", help="recompile the probe program first")
     sh = sub.add_parser("shapes", help="fp32 and bf16 default entry points on more shapes")
     sh.add_argument("--steps", type=int, default=20)
