@@ -361,8 +361,12 @@ const char *const kLayoutNames[2][2][3][2] = {
 
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16) {
-    if (p.ta == p.tb && shape == 32) {  // "n n" or "t t": the LDS-DMA kernel with one row operand
-        const hipError_t e = launch_bf16_mfma_dma_rows(p, s, name, f16);
+    if ((p.ta || !p.tb) && shape == 32) {
+        // M/N-contiguous operands on the LDS-DMA kernel: "t n" in their own storage with
+        // transposing fragment reads; "n n" / "t t" with the M/N-contiguous operand through
+        // registers as rows (the transposing reads measured level or 3% slower there)
+        const hipError_t e = p.ta == p.tb ? launch_bf16_mfma_dma_rows(p, s, name, f16)
+                                          : launch_bf16_mfma_dma_mn(p, s, name, f16);
         if (e != hipErrorNotSupported) return e;
     }
     if (p.ta || !p.tb) {  // not the native K-contiguous pair

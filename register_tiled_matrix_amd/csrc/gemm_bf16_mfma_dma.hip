@@ -37,7 +37,7 @@ namespace {
 using namespace mfma;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MF, int WINDOWS, int STAGGER, bool F16,
-          int RING = 2, int ROWS = 0, bool KTAIL = false>
+          int RING = 2, int ROWS = 0, bool KTAIL = false, int MN = 0>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -63,6 +63,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // KTAIL: K ends inside the last slab (K a multiple of 8, so each 16-byte chunk lies wholly
     // before or wholly past K); that slab's chunks past K are loaded from an offset past the
     // descriptor's end, which puts zeros in LDS.
+    // MN: bit 0, A is stored K x M; bit 1, B is stored K x N. Such an operand keeps its storage
+    // in LDS: a slab of BK rows (k) of BM (BN) elements, 16-byte chunk c of row r at slot
+    // c ^ mkey(r). Its DMA reads through a descriptor over its K rows from the tile's first
+    // column (rows past K read zeros, columns past M or N only feed dropped outputs), and its
+    // fragments come from pairs of transposing LDS reads.
+    constexpr bool A_MN = (MN & 1) != 0, B_MN = (MN & 2) != 0;
+    static_assert(MN == 0 || (ROWS == 0 && RING == 5 && MF == 32 && BM == 256 && BN == 256 && BK == 64),
+                  "M/N-major slabs: 32x32x16 fragments on the 256x256 ring");
 
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
@@ -89,10 +97,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // A tile of the last tile row (column) may extend past M (N): its descriptors end at the
     // last real row, so DMA loads of the rows beyond read zeros.
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-    const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(rows_a * lda * 2));
-    const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
+    const rsrc_t a_rsrc = A_MN ? make_rsrc(A + m0, (uint32_t)(K * lda * 2))
+                               : make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(rows_a * lda * 2));
+    const rsrc_t b_rsrc = B_MN ? make_rsrc(B + n0, (uint32_t)(K * ldb * 2))
+                               : make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
     const int nslabs = KTAIL ? (K + BK - 1) / BK : K / BK;
     const int k_last = (nslabs - 1) * BK;  // first k of the last slab
+    // An M/N-major slab row holds MCH chunks; one DMA instruction covers 64 / MCH rows.
+    constexpr int MCH = BM / 8;
+    auto mkey = [](int row) { return 4 * (row & 3); };
     uint32_t a_voff[2], b_voff[2], a_voff_last[2], b_voff_last[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -105,28 +118,46 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         // (2^31 exceeds every tile's byte count; the uniform parts added to it stay below 2^32)
         a_voff_last[j] = k_last + ca * 8 < K ? a_voff[j] : a_voff[j] | 0x80000000u;
         b_voff_last[j] = k_last + cb * 8 < K ? b_voff[j] : b_voff[j] | 0x80000000u;
+        // M/N-major: instruction q fills rows 2 (wave * J + q) and the next; its lane part is
+        // the row within the pair and the source chunk of slot lane % 32 (the row's parity
+        // pattern repeats every two instructions, J being even)
+        const int r_in = lane / MCH, slot = lane % MCH, key = mkey(2 * j + r_in);
+        if (A_MN) a_voff[j] = (uint32_t)(r_in * lda + (slot ^ key) * 8) * 2u;
+        if (B_MN) b_voff[j] = (uint32_t)(r_in * ldb + (slot ^ key) * 8) * 2u;
     }
-    auto voff_a = [&](int q, int k0) { return KTAIL && k0 == k_last ? a_voff_last[q & 1] : a_voff[q & 1]; };
-    auto voff_b = [&](int q, int k0) { return KTAIL && k0 == k_last ? b_voff_last[q & 1] : b_voff[q & 1]; };
+    static_assert(MN == 0 || (JA % 2 == 0 && JB % 2 == 0 && 64 / MCH == 2), "two rows per instruction");
+    auto voff_a = [&](int q, int k0) {
+        return KTAIL && !A_MN && k0 == k_last ? a_voff_last[q & 1] : a_voff[q & 1];
+    };
+    auto voff_b = [&](int q, int k0) {
+        return KTAIL && !B_MN && k0 == k_last ? b_voff_last[q & 1] : b_voff[q & 1];
+    };
     const uint32_t a_step = (uint32_t)(ROWS_PER_INSTR * lda) * 2u;  // bytes per instruction
     const uint32_t b_step = (uint32_t)(ROWS_PER_INSTR * ldb) * 2u;
+    // uniform byte offset of DMA instruction q of the slab starting at k0
+    auto soff_a = [&](int q, int k0) {
+        return A_MN ? (uint32_t)(2 * (wave * JA + q) + k0) * (uint32_t)lda * 2u
+                    : (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u;
+    };
+    auto soff_b = [&](int q, int k0) {
+        return B_MN ? (uint32_t)(2 * (wave * JB + q) + k0) * (uint32_t)ldb * 2u
+                    : (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u;
+    };
     // DMA instruction q (A for q < JA, then B) of the slab starting at k0.
     auto dma_q = [&](int q, int k0, uint4 *sa, uint4 *sb) {
         if (q < JA)
-            dma16_buf(a_rsrc, voff_a(q, k0), (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u,
-                      sa + (wave * JA + q) * 64);
+            dma16_buf(a_rsrc, voff_a(q, k0), soff_a(q, k0), sa + (wave * JA + q) * 64);
         else
-            dma16_buf(b_rsrc, voff_b(q - JA, k0), (uint32_t)((q - JA) & ~1) * b_step + (uint32_t)k0 * 2u,
-                      sb + (wave * JB + (q - JA)) * 64);
+            dma16_buf(b_rsrc, voff_b(q - JA, k0), soff_b(q - JA, k0), sb + (wave * JB + (q - JA)) * 64);
     };
 
     // One DMA instruction q of the A part (B part) of the slab starting at k0 into the half
     // (A or B area) at `dst`.
     auto dma_a = [&](int q, int k0, uint4 *dst) {
-        dma16_buf(a_rsrc, voff_a(q, k0), (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u, dst + (wave * JA + q) * 64);
+        dma16_buf(a_rsrc, voff_a(q, k0), soff_a(q, k0), dst + (wave * JA + q) * 64);
     };
     auto dma_b = [&](int q, int k0, uint4 *dst) {
-        dma16_buf(b_rsrc, voff_b(q, k0), (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u, dst + (wave * JB + q) * 64);
+        dma16_buf(b_rsrc, voff_b(q, k0), soff_b(q, k0), dst + (wave * JB + q) * 64);
     };
     // the operand that keeps its DMA when the other arrives as rows
     auto dma_e = [&](int q, int k0, uint4 *dst) {
@@ -200,17 +231,41 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // Fragment reads of one k step (F::KSTEP wide) into register buffer `buf`. Every group
     // of MF lanes reads MF consecutive slab rows at one chunk: conflict-free under the key.
     bf16x8 fa[2][MI], fb[2][NI];
+    // M/N-major fragment: lane l needs column c of the fragment (c = l % 32) at k = 8 (l / 32)
+    // .. +7 of the k step. In each group of 16 lanes, lane t addresses row k + t / 4 (+ 4 for
+    // the second read) at columns 16 ((l / 16) % 2) + 4 (t % 4) .. +3, so that lane t receives
+    // column 16 ((l / 16) % 2) + t of four consecutive rows (the transposing read's mapping).
+    const int tr_t = lane & 15;
+    const int tr_row = 8 * (lane >> 5) + (tr_t >> 2);                    // row within the k step
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_t & 3);         // column within the fragment
+    auto mn_frag = [&](const uint4 *slab, int col0, int kk) {
+        const char *base = reinterpret_cast<const char *>(slab);
+        const int row = kk * F::KSTEP + tr_row, col = col0 + tr_col;
+        // row & 3 == tr_t >> 2 for both reads (rows 4 apart)
+        const int off = ((col >> 3) ^ mkey(row)) * 16 + (col & 7) * 2;
+        const uint2 lo = lds_read_tr16(base + row * (MCH * 16) + off);
+        const uint2 hi = lds_read_tr16(base + (row + 4) * (MCH * 16) + off);
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
     auto read_frags = [&](const uint4 *sa, const uint4 *sb, int kk, int buf) {
         const int chunk = kk * (F::KSTEP / 8) + frag_kg;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int row = wm * WTM + i * MF + frag_r;
-            fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
+            if constexpr (A_MN) {
+                fa[buf][i] = mn_frag(sa, wm * WTM + i * MF, kk);
+            } else {
+                const int row = wm * WTM + i * MF + frag_r;
+                fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int row = wn * WTN + j * MF + frag_r;
-            fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
+            if constexpr (B_MN) {
+                fb[buf][j] = mn_frag(sb, wn * WTN + j * MF, kk);
+            } else {
+                const int row = wn * WTN + j * MF + frag_r;
+                fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * KCH + (chunk ^ slab_key<KCH, MF>(row))]);
+            }
         }
     };
     // One slab is KSTEPS k steps. Each starts by waiting for its own fragments (read during
@@ -228,7 +283,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // load has more than a k step to land before the barrier that waits for it.
     constexpr int KSTEPS = BK / F::KSTEP;
     constexpr int NMFMA = MI * NI;
-    constexpr int NREAD = MI + NI;
+    constexpr int NREAD = MI * (A_MN ? 2 : 1) + NI * (B_MN ? 2 : 1);  // LDS reads per k step
     constexpr int NWIN = KSTEPS - 1 < WINDOWS ? KSTEPS - 1 : WINDOWS;
     constexpr int JE = A_ROW ? JB : JA;  // DMA instructions of the early (DMA) operand
     constexpr int PER_SET = ANY_ROW ? JE : PER_SLAB;  // DMA instructions per wave and slab
@@ -537,10 +592,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGGER, bool F16, int RING,
-          int ROWS = 0, bool KTAIL = false>
+          int ROWS = 0, bool KTAIL = false, int MN = 0>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS, KTAIL>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS, KTAIL, MN>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);
     return hipGetLastError();
@@ -618,6 +673,37 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
     *name = names[f16][kind][ktail];
     if (f16) return ktail ? launch_dma_shape<true, true>(p, s, shape, small) : launch_dma_shape<true, false>(p, s, shape, small);
     return ktail ? launch_dma_shape<false, true>(p, s, shape, small) : launch_dma_shape<false, false>(p, s, shape, small);
+}
+
+// "t n": A stored K x M and B stored K x N, both M/N-contiguous. Both reach LDS by DMA in their
+// own storage and feed the MFMAs through transposing LDS reads (the kernel template takes
+// either operand that way; for "n n" and "t t" the register-row kernel measured level or
+// faster, so only "t n" launches it). Returns hipErrorNotSupported (launching nothing) unless
+// there are at least 128 tiles of 256x256 and both operands' rows are 16-byte aligned within
+// 32-bit offsets over all of K. M, N and K may end inside a tile.
+hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16) {
+    const int64_t lim = int64_t(1) << 31;
+    auto mn_ok = [&](int64_t ld, const void *ptr) {
+        return ld % 8 == 0 && aligned16(ptr) && ((int64_t)p.K + 64) * ld * 2 + 512 < lim;
+    };
+    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
+    const bool ok = p.ta && !p.tb && DMA_RING32 == 5 && p.K > 0 && tiles >= 128 &&
+                    (int64_t)DMA_BM * p.ldc * 4 < lim && mn_ok(p.lda, p.A) && mn_ok(p.ldb, p.B);
+    if (!ok) return hipErrorNotSupported;
+    const bool ktail = p.K % DMA_BK != 0;
+#define REGTILE_DMA_MN_NAME(elt)                                                                   \
+    elt "_mfma32x32x16_dma_tr_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK) \
+        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_tn"
+    static const char *const names[2][2] = {
+        {REGTILE_DMA_MN_NAME("bf16"), REGTILE_DMA_MN_NAME("bf16") "_ktail"},
+        {REGTILE_DMA_MN_NAME("f16"), REGTILE_DMA_MN_NAME("f16") "_ktail"}};
+#undef REGTILE_DMA_MN_NAME
+    *name = names[f16][ktail];
+#define REGTILE_MN_LAUNCH(F16_, KT_) \
+    launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, 0, KT_, 3>(p, s)
+    if (f16) return ktail ? REGTILE_MN_LAUNCH(true, true) : REGTILE_MN_LAUNCH(true, false);
+    return ktail ? REGTILE_MN_LAUNCH(false, true) : REGTILE_MN_LAUNCH(false, false);
+#undef REGTILE_MN_LAUNCH
 }
 
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)

@@ -89,6 +89,23 @@ __device__ __forceinline__ uint2 load_b64_buf(rsrc_t r, uint32_t voff, uint32_t 
 #endif
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Each lane gives the LDS address of 4 consecutive
+// 16-bit elements; in every group of 16 lanes, lane 4a + b receives element b of the vectors
+// addressed by lanes a, 4 + a, 8 + a and 12 + a (measured). So if lane 4j + a addresses row
+// r0 + j, columns c0 + 4a .. c0 + 4a + 3 of a row-major image, lane i receives column c0 + i of
+// rows r0 .. r0 + 3.
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) tr_v4i16 *)lds);
+    return __builtin_bit_cast(uint2, v);
+#else
+    (void)lds;
+    return make_uint2(0u, 0u);
+#endif
+}
+
 // One fp32 per lane at buffer byte offset voff + soff (soff wave-uniform).
 __device__ __forceinline__ float load_f32_buf(rsrc_t r, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -220,3 +220,37 @@ def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
         assert np.array_equal(got[I, J].astype(np.float64), ref), name
     else:
         assert_parity_full(inp, got, f"{dtype} ({ta},{tb}) {shape} ({name})")
+
+
+TN_DMA = [("bf16", (4096, 2048, 320), "integer", "sampled"), ("f16", (4096, 2048, 320), "normal", "sampled"),
+          ("bf16", (4000, 4104, 200), "normal", "full"), ("bf16", (4104, 4000, 1000), "integer", "sampled"),
+          ("bf16", (8192, 8192, 8192), "normal", "sampled")]
+
+
+@pytest.mark.parametrize("dtype,shape,dist,mode", TN_DMA,
+                         ids=[f"{d}-{'x'.join(map(str, s))}-{t}" for d, s, t, _ in TN_DMA])
+def test_16bit_tn_on_the_dma_kernel(dtype, shape, dist, mode):
+    # "t n" (A stored K x M, B stored K x N): both operands reach LDS by DMA in their own
+    # storage and the fragments come from transposing LDS reads; M, N and K may end inside a
+    # tile (leading dimensions M and N multiples of 8)
+    M, N, K = shape
+    if dist == "integer":
+        rng = np.random.Generator(np.random.PCG64(M + N + K + 5))
+        to_bits = gi.f32_to_bf16_bits if dtype == "bf16" else gi.f32_to_f16_bits
+        A = to_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+        Bt = to_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+        inp = gi.GemmInputs(M, N, K, 1.0, 0.0, dtype, True, A, Bt, None)
+    else:
+        inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.25, beta=-0.5, seed=M + 3 * N + K)
+    announce(f"{dtype} t n DMA {shape} {dist}")
+    got, name = _run(inp, 1, 0, rt.ALGO_BF16_MFMA)
+    assert "_dma_tr_" in name and (name.endswith("_tn") or name.endswith("_tn_ktail")), name
+    assert name.endswith("_ktail") == (K % 64 != 0), name
+    if dist == "integer":
+        I, J = sample_positions(M, N, n_random=50000, seed=10)
+        ref, _ = oracle.gemm_inputs_entries(inp, I, J)
+        assert np.array_equal(got[I, J].astype(np.float64), ref), name
+    elif mode == "full":
+        assert_parity_full(inp, got, f"{dtype} t n {shape} ({name})")
+    else:
+        assert_parity_sampled(inp, got, f"{dtype} t n {shape} ({name})", n_random=50000)
