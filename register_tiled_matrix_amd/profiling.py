@@ -202,7 +202,7 @@ def summarize_trace(prof, out_md):
 
         agree("fp32 4096^3", bench_line["roofline"], KERNELS["f32_4096"][1] + ", false, false, false")
         if "bf16_8192" in bench_line:
-            agree("bf16 8192^3", bench_line["bf16_8192"]["roofline"], KERNELS["bf16_8192"][1] + ", 1, 1, false, 5, 0, false>")
+            agree("bf16 8192^3", bench_line["bf16_8192"]["roofline"], KERNELS["bf16_8192"][1] + ", 1, 1, false, 5, 0, false, 0>")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
