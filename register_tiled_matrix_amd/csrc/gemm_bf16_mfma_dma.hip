@@ -1,5 +1,7 @@
-// gemm_bf16_mfma_dma.hip -- the bf16 MFMA rung for full, aligned tiles: HBM -> LDS by direct
-// DMA loads, a multi-stage LDS ring, and wave tiles of 32x32x16 MFMA fragments.
+// gemm_bf16_mfma_dma.hip -- the bf16 / fp16 MFMA kernel: HBM -> LDS by direct DMA loads
+// through per-tile buffer descriptors, a multi-stage LDS ring, and wave tiles of MFMA
+// fragments. It takes every problem whose rows are 16-byte aligned (M, N and K may end inside
+// a tile); others go to the register-staged kernel (gemm_bf16_mfma.hip).
 //
 // Same three levels as the other rungs ("寄存器Tiling跨架构解析" (www.zskr.cn/news/2170507)
 // section 1.1: global block tile -> shared tile -> register tile), with the register level
@@ -17,6 +19,11 @@
 //      KCH = 8, MF = 32: key(r) = (r & 7) ^ ((r >> 3) & 1)
 //      KCH = 8, MF = 16: key(r) = ((r >> 1) & 7) ^ ((r & 1) << 2)
 //      KCH = 4 (64-byte rows): key(r) = (r >> 2) & 3
+//  * M/N-contiguous operands: as rows staged through registers ("n n", "t t"), or in their own
+//    storage with transposing fragment reads ("t n"); see the kernel.
+//  * Edges: descriptors end at the last real row, so loads past it read zeros and stores past
+//    it are dropped; columns past N get an out-of-range store offset; chunks past K in the
+//    last slab an out-of-range load offset.
 //  * Two LDS stages and one barrier per slab, placed inside the slab's last k step: the
 //    next slab is loaded while the current one is consumed, and its first fragments are
 //    read before the current slab's last MFMAs (section 6.3: prefetch of the next k slice
