@@ -1,7 +1,7 @@
 """rocprofv3 evidence for the benchmark's kernels: collect on the GPU, summarise on the CPU.
 
-    python -m register_tiled_matrix_amd.profiling collect gpurun_out/prof    # GPU machine
-    python -m register_tiled_matrix_amd.profiling summarize gpurun_out/prof  # writes profiles/
+    python -m register_tiled_matrix_amd.profiling collect OUT/prof    # on the MI355X
+    python -m register_tiled_matrix_amd.profiling summarize OUT/prof  # writes profiles/
 
 `collect` runs each profiler pass as a child process (rocprofv3 starts the program itself;
 this process never touches the GPU), one pass at a time, each under its own time limit, and
@@ -78,9 +78,8 @@ def passes(out):
 
 
 def _display(argv, prof):
-    """A pass's command as the profiles print it: output under gpurun_out/prof, other paths
-    relative to the repository root."""
-    return " ".join(argv).replace(prof, "gpurun_out/prof").replace(ROOT + os.sep, "")
+    """A pass's command as the profiles print it: every path relative to the repository root."""
+    return " ".join(argv).replace(prof, os.path.relpath(prof, ROOT)).replace(ROOT + os.sep, "")
 
 
 def collect(out, only=None) -> int:

@@ -377,11 +377,11 @@ def cmd_shapes(args) -> int:
     return 0
 
 
-def _ladder_report(rows) -> str:
+def _ladder_report(rows, src) -> str:
     out = ["# Kernel ladder on every configuration", "",
            "Command (repository root, one MI355X):", "", "```",
-           "python -m register_tiled_matrix_amd.tune ladder > gpurun_out/ladder.jsonl",
-           "python -m register_tiled_matrix_amd.tune report gpurun_out/ladder.jsonl", "```", "",
+           f"python -m register_tiled_matrix_amd.tune ladder > {src}",
+           f"python -m register_tiled_matrix_amd.tune report {src}", "```", "",
            "Median of 30 timed launches after 50 warm-up launches (3 timed after 1 for the naive "
            "and LDS rungs on the large problems), operands resident on the device. VGPRs / "
            "occupancy / LDS: the compiler's resource report for the kernel the rung launched "
@@ -397,8 +397,9 @@ def _ladder_report(rows) -> str:
 
 def cmd_report(args) -> int:
     rows = [json.loads(l) for l in open(args.jsonl) if l.strip().startswith("{")]
+    src = os.path.relpath(os.path.abspath(args.jsonl), _build.ROOT)
     if rows and "rung" in rows[0]:
-        text = _ladder_report(rows)
+        text = _ladder_report(rows, src)
         if args.out:
             with open(args.out, "w") as f:
                 f.write(text)
@@ -408,8 +409,8 @@ def cmd_report(args) -> int:
     out = ["# fp32 micro-tile / occupancy sweep", "",
            "Commands (repository root; the variants are built on the CPU first):", "", "```",
            "python -m register_tiled_matrix_amd.tune build",
-           "python -m register_tiled_matrix_amd.tune run --workloads f32_4096,f32_tall > gpurun_out/sweep.jsonl",
-           "python -m register_tiled_matrix_amd.tune report gpurun_out/sweep.jsonl", "```", "",
+           f"python -m register_tiled_matrix_amd.tune run --workloads f32_4096,f32_tall > {src}",
+           f"python -m register_tiled_matrix_amd.tune report {src}", "```", "",
            "Each variant is the same kernel source with other compile-time values: micro-tile TM x TN "
            "per lane (workgroup tile 16TM x 16TN, 256 threads), slab depth BK, and the waves per SIMD "
            "requested from the compiler (`amdgpu_waves_per_eu`). VGPRs, scratch and occupancy are the "
