@@ -174,14 +174,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
             dma_a(q, k0, dst);
     };
 
-    // The row operand (ANY_ROW) has no DMA. Each thread owns two 4 x 8 blocks of its slab (4
-    // consecutive m or n, 8 consecutive k), reads them as 8-byte runs along m or n (consecutive
-    // lanes take consecutive runs of one k row), and after the half they go to is free writes
-    // them transposed (8 k per 16-byte chunk, mfma_common.h) into the swizzled slab.
+    // The row operand (ANY_ROW) has no DMA. Each thread owns 4 x 8 blocks of its slab (4
+    // consecutive m or n, 8 consecutive k; two blocks on 256x256 tiles, one on 128x128), reads
+    // them as 8-byte runs along m or n (consecutive lanes take consecutive runs of one k row),
+    // and after the half they go to is free writes them transposed (8 k per 16-byte chunk,
+    // mfma_common.h) into the swizzled slab.
     constexpr int NT = NWAVES * 64;
     constexpr int RLEN = A_ROW ? BM : BN;  // slab rows of the row operand
-    constexpr int B_BLOCKS = ANY_ROW ? 2 : 1;
-    static_assert(!ANY_ROW || (RLEN / 4) * KCH == B_BLOCKS * NT, "two 4 x 8 blocks per thread");
+    constexpr int B_BLOCKS = ANY_ROW ? (RLEN / 4) * KCH / NT : 1;
+    static_assert(!ANY_ROW || (B_BLOCKS >= 1 && (RLEN / 4) * KCH == B_BLOCKS * NT),
+                  "whole 4 x 8 blocks per thread");
     constexpr int NBL = ANY_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
     // The row operand's loads go through a descriptor over its K rows (of ld_row elements)
     // from the tile's first column: rows at or past K read zeros (the K tail); columns past M
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         write_brow(smem + A_SLOTS);
         load_brow(1);
         if (SH == 0) ring_window(0, 1, 3, 2, 4);  // DMA operand of slab 2
-        wait_vmcnt<JE + NBL + (SH == 0 ? JE : 0)>();  // DMA operand of slab 0
+        wait_vmcnt<JE + NBL + (SH == 0 ? DMA_PER_WIN : 0)>();  // DMA operand of slab 0
         wait_lgkmcnt0();
         lds_barrier();
         frags_at(0, 1, 0, 0);
@@ -715,35 +717,45 @@ hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char *
 
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)
 // or "t t" (A stored K x M, B stored N x K). The K-contiguous operand goes over LDS DMA, the
-// other as 8-byte row runs through registers, transposed into the slab. Returns
-// hipErrorNotSupported (launching nothing) unless there are at least 128 tiles of 256x256, K
+// other as 8-byte row runs through registers, transposed into the slab. Fewer than 128 tiles
+// of 256x256 run on 128x128 tiles. Returns hipErrorNotSupported (launching nothing) unless K
 // is a multiple of 8, the DMA operand's rows are 16-byte aligned within 32-bit tile offsets,
 // and the row operand's rows are 8-byte aligned within 32-bit offsets over all of K. M, N and
 // K may end inside a tile.
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16) {
     const bool nn = !p.ta && !p.tb, tt = p.ta && p.tb;
-    const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && (int64_t)DMA_BM * p.lda * 2 < (int64_t(1) << 31))
-                           : (p.ldb % 8 == 0 && aligned16(p.B) && (int64_t)DMA_BN * p.ldb * 2 < (int64_t(1) << 31));
+    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
+    const bool small = tiles < 128;  // 128x128 tiles, as in the K-contiguous kernel
+    const int64_t bm = small ? 128 : DMA_BM, bn = small ? 128 : DMA_BN;
+    const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && bm * p.lda * 2 < (int64_t(1) << 31))
+                           : (p.ldb % 8 == 0 && aligned16(p.B) && bn * p.ldb * 2 < (int64_t(1) << 31));
     const int64_t ld_row = nn ? p.ldb : p.lda;
     const bool rows_ok = ld_row % 4 == 0 && aligned8(nn ? p.B : p.A) &&
                          ((int64_t)p.K + 128) * ld_row * 2 + 512 < (int64_t(1) << 31);
-    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
     const bool ok = (nn || tt) && DMA_RING32 == 5 && dma_ok && rows_ok && p.K % 8 == 0 && p.K > 0 &&
-                    (int64_t)DMA_BM * p.ldc * 4 < (int64_t(1) << 31) && tiles >= 128;
+                    bm * p.ldc * 4 < (int64_t(1) << 31);
     if (!ok) return hipErrorNotSupported;
     const bool ktail = p.K % DMA_BK != 0;
-#define REGTILE_DMA_ROWS_NAME(elt, lay)                                                            \
-    elt "_mfma32x32x16_dma_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK)   \
-        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_" lay
-    static const char *const names[2][2][2] = {
-        {{REGTILE_DMA_ROWS_NAME("bf16", "tt"), REGTILE_DMA_ROWS_NAME("bf16", "tt") "_ktail"},
-         {REGTILE_DMA_ROWS_NAME("bf16", "nn"), REGTILE_DMA_ROWS_NAME("bf16", "nn") "_ktail"}},
-        {{REGTILE_DMA_ROWS_NAME("f16", "tt"), REGTILE_DMA_ROWS_NAME("f16", "tt") "_ktail"},
-         {REGTILE_DMA_ROWS_NAME("f16", "nn"), REGTILE_DMA_ROWS_NAME("f16", "nn") "_ktail"}}};
+#define REGTILE_DMA_ROWS_NAME(elt, bm, bn, lay)                                                   \
+    elt "_mfma32x32x16_dma_" bm "x" bn "x" REGTILE_STR(DMA_BK) "_w" REGTILE_STR(DMA_WM) "x"        \
+        REGTILE_STR(DMA_WN) "_" lay
+#define REGTILE_DMA_ROWS_PAIR(elt, bm, bn, lay)                                                   \
+    {REGTILE_DMA_ROWS_NAME(elt, bm, bn, lay), REGTILE_DMA_ROWS_NAME(elt, bm, bn, lay) "_ktail"}
+#define REGTILE_DMA_ROWS_SIZE(elt, bm, bn)                                                        \
+    {REGTILE_DMA_ROWS_PAIR(elt, bm, bn, "tt"), REGTILE_DMA_ROWS_PAIR(elt, bm, bn, "nn")}
+    static const char *const names[2][2][2][2] = {
+        {REGTILE_DMA_ROWS_SIZE("bf16", REGTILE_STR(DMA_BM), REGTILE_STR(DMA_BN)),
+         REGTILE_DMA_ROWS_SIZE("bf16", "128", "128")},
+        {REGTILE_DMA_ROWS_SIZE("f16", REGTILE_STR(DMA_BM), REGTILE_STR(DMA_BN)),
+         REGTILE_DMA_ROWS_SIZE("f16", "128", "128")}};
+#undef REGTILE_DMA_ROWS_SIZE
+#undef REGTILE_DMA_ROWS_PAIR
 #undef REGTILE_DMA_ROWS_NAME
-    *name = names[f16][nn][ktail];
-#define REGTILE_ROWS_LAUNCH(F16_, ROWS_, KT_) \
-    launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, ROWS_, KT_>(p, s)
+    *name = names[f16][small][nn][ktail];
+    // small: the K-contiguous kernel's 128x128 set-up (two DMA windows per slab, no stagger)
+#define REGTILE_ROWS_LAUNCH(F16_, ROWS_, KT_)                                                      \
+    (small ? launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, 2, 0, F16_, 5, ROWS_, KT_>(p, s)            \
+           : launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, ROWS_, KT_>(p, s))
     if (f16) {
         if (nn) return ktail ? REGTILE_ROWS_LAUNCH(true, 1, true) : REGTILE_ROWS_LAUNCH(true, 1, false);
         return ktail ? REGTILE_ROWS_LAUNCH(true, 2, true) : REGTILE_ROWS_LAUNCH(true, 2, false);

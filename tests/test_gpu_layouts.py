@@ -181,7 +181,11 @@ def test_16bit_row_operand_on_the_dma_kernel(ta, tb, dtype, dist):
 # (the row operand's leading dimension, N for "n n" and M for "t t", a multiple of 4 for its
 # 8-byte runs, yet not of 256)
 ROWS_RAGGED = [("bf16", 0, 0, (8000, 4100, 1000), "normal"), ("f16", 1, 1, (4100, 8000, 72), "normal"),
-               ("bf16", 0, 0, (4097, 8188, 64), "integer"), ("bf16", 1, 1, (4000, 4101, 200), "integer")]
+               ("bf16", 0, 0, (4097, 8188, 64), "integer"), ("bf16", 1, 1, (4000, 4101, 200), "integer"),
+               # fewer than 128 tiles of 256x256: 128x128 tiles
+               ("bf16", 0, 0, (1000, 1500, 776), "normal"), ("f16", 1, 1, (700, 900, 200), "normal"),
+               ("bf16", 0, 0, (1536, 1028, 2048), "integer"), ("bf16", 1, 1, (2000, 1001, 520), "integer"),
+               ("f16", 0, 0, (33, 4, 8), "normal")]
 
 
 @pytest.mark.parametrize("dtype,ta,tb,shape,dist", ROWS_RAGGED,
@@ -212,6 +216,7 @@ def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
     lay = "_nn" if ta == 0 else "_tt"
     assert "_dma_" in name and (name.endswith(lay) or name.endswith(lay + "_ktail")), name
     assert name.endswith("_ktail") == (K % 64 != 0), name
+    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) < 128), name
     assert torch.all(big[:, N:] == -77.0).item(), "a store landed past column N"
     got = C.cpu().numpy()
     if dist == "integer":
