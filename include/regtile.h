@@ -149,10 +149,9 @@ int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint
  * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit). The
  * 16-bit LDS-DMA kernel takes (0, 1) whenever K is a multiple of 8 and rows are 16-byte
  * aligned; (0, 0) / (1, 1) when in addition the M- or N-contiguous operand's rows are 8-byte
- * aligned (that operand staged through registers); and (1, 0) with at least 128 tiles of
- * 256x256 and 16-byte aligned rows (both operands in their own storage, transposing LDS
- * reads). Other problems gather M- or N-contiguous operands into K-contiguous LDS slabs with
- * 8-byte loads.
+ * aligned (that operand staged through registers); and (1, 0) with 16-byte aligned rows (both
+ * operands in their own storage, transposing LDS reads). Other problems gather M- or
+ * N-contiguous operands into K-contiguous LDS slabs with 8-byte loads.
  */
 int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
                         const float *A, int lda, const float *B, int ldb, float beta, float *C,

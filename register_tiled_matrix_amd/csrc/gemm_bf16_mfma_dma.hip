@@ -76,8 +76,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // column (rows past K read zeros, columns past M or N only feed dropped outputs), and its
     // fragments come from pairs of transposing LDS reads.
     constexpr bool A_MN = (MN & 1) != 0, B_MN = (MN & 2) != 0;
-    static_assert(MN == 0 || (ROWS == 0 && RING == 5 && MF == 32 && BM == 256 && BN == 256 && BK == 64),
-                  "M/N-major slabs: 32x32x16 fragments on the 256x256 ring");
+    static_assert(MN == 0 || (ROWS == 0 && RING == 5 && MF == 32 && BM == BN && (BM == 256 || BM == 128) && BK == 64),
+                  "M/N-major slabs: 32x32x16 fragments on the 256x256 or 128x128 ring");
 
 
     __shared__ uint4 smem[RING == 5 ? 5 * A_SLOTS : STAGES * STAGE_SLOTS];
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                                : make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
     const int nslabs = KTAIL ? (K + BK - 1) / BK : K / BK;
     const int k_last = (nslabs - 1) * BK;  // first k of the last slab
-    // An M/N-major slab row holds MCH chunks; one DMA instruction covers 64 / MCH rows.
-    constexpr int MCH = BM / 8;
+    // An M/N-major slab row holds MCH chunks; one DMA instruction covers MROWS = 64 / MCH rows.
+    constexpr int MCH = BM / 8, MROWS = 64 / MCH;
     auto mkey = [](int row) { return 4 * (row & 3); };
     uint32_t a_voff[2], b_voff[2], a_voff_last[2], b_voff_last[2];
 #pragma unroll
@@ -125,14 +125,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         // (2^31 exceeds every tile's byte count; the uniform parts added to it stay below 2^32)
         a_voff_last[j] = k_last + ca * 8 < K ? a_voff[j] : a_voff[j] | 0x80000000u;
         b_voff_last[j] = k_last + cb * 8 < K ? b_voff[j] : b_voff[j] | 0x80000000u;
-        // M/N-major: instruction q fills rows 2 (wave * J + q) and the next; its lane part is
-        // the row within the pair and the source chunk of slot lane % 32 (the row's parity
-        // pattern repeats every two instructions, J being even)
-        const int r_in = lane / MCH, slot = lane % MCH, key = mkey(2 * j + r_in);
+        // M/N-major: instruction q fills rows MROWS (wave * J + q) .. +MROWS-1; its lane part
+        // is the row within those and the source chunk of slot lane % MCH (the key, a function
+        // of row % 4, repeats every two instructions: J is even, MROWS 2 or 4)
+        const int r_in = lane / MCH, slot = lane % MCH, key = mkey(MROWS * j + r_in);
         if (A_MN) a_voff[j] = (uint32_t)(r_in * lda + (slot ^ key) * 8) * 2u;
         if (B_MN) b_voff[j] = (uint32_t)(r_in * ldb + (slot ^ key) * 8) * 2u;
     }
-    static_assert(MN == 0 || (JA % 2 == 0 && JB % 2 == 0 && 64 / MCH == 2), "two rows per instruction");
+    static_assert(MN == 0 || (JA % 2 == 0 && JB % 2 == 0 && (MROWS == 2 || MROWS == 4)),
+                  "two or four rows per instruction");
     auto voff_a = [&](int q, int k0) {
         return KTAIL && !A_MN && k0 == k_last ? a_voff_last[q & 1] : a_voff[q & 1];
     };
@@ -143,11 +144,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     const uint32_t b_step = (uint32_t)(ROWS_PER_INSTR * ldb) * 2u;
     // uniform byte offset of DMA instruction q of the slab starting at k0
     auto soff_a = [&](int q, int k0) {
-        return A_MN ? (uint32_t)(2 * (wave * JA + q) + k0) * (uint32_t)lda * 2u
+        return A_MN ? (uint32_t)(MROWS * (wave * JA + q) + k0) * (uint32_t)lda * 2u
                     : (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u;
     };
     auto soff_b = [&](int q, int k0) {
-        return B_MN ? (uint32_t)(2 * (wave * JB + q) + k0) * (uint32_t)ldb * 2u
+        return B_MN ? (uint32_t)(MROWS * (wave * JB + q) + k0) * (uint32_t)ldb * 2u
                     : (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u;
     };
     // DMA instruction q (A for q < JA, then B) of the slab starting at k0.
@@ -298,7 +299,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     constexpr int PER_SET = ANY_ROW ? JE : PER_SLAB;  // DMA instructions per wave and slab
     constexpr int DMA_PER_WIN = (PER_SET + NWIN - 1) / NWIN;
     static_assert(KSTEPS % 2 == 0 && NWIN >= 1, "even number of k steps per slab");
-    static_assert(NREAD <= NMFMA && DMA_PER_WIN <= NMFMA, "one extra instruction per MFMA slot");
+    // (transposing reads on 64x64 wave tiles: 8 per k step against 4 MFMAs, two per slot)
+    static_assert((NREAD <= NMFMA || (MN != 0 && NREAD <= 2 * NMFMA)) && DMA_PER_WIN <= NMFMA,
+                  "one extra instruction per MFMA slot, or two fragment reads");
 
     auto dma_window = [&](int slab, int stage, int win) {
         const int k0 = slab * BK;
@@ -329,8 +332,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 --d_left;
             } else if (r_left > 0) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                --r_left;
+                if (NREAD > NMFMA && r_left > 1) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    r_left -= 2;
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    --r_left;
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -687,29 +695,35 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 // "t n": A stored K x M and B stored K x N, both M/N-contiguous. Both reach LDS by DMA in their
 // own storage and feed the MFMAs through transposing LDS reads (the kernel template takes
 // either operand that way; for "n n" and "t t" the register-row kernel measured level or
-// faster, so only "t n" launches it). Returns hipErrorNotSupported (launching nothing) unless
-// there are at least 128 tiles of 256x256 and both operands' rows are 16-byte aligned within
-// 32-bit offsets over all of K. M, N and K may end inside a tile.
+// faster, so only "t n" launches it). Fewer than 128 tiles of 256x256 run on 128x128 tiles.
+// Returns hipErrorNotSupported (launching nothing) unless both operands' rows are 16-byte
+// aligned within 32-bit offsets over all of K. M, N and K may end inside a tile.
 hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16) {
     const int64_t lim = int64_t(1) << 31;
     auto mn_ok = [&](int64_t ld, const void *ptr) {
         return ld % 8 == 0 && aligned16(ptr) && ((int64_t)p.K + 64) * ld * 2 + 512 < lim;
     };
     const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool ok = p.ta && !p.tb && DMA_RING32 == 5 && p.K > 0 && tiles >= 128 &&
-                    (int64_t)DMA_BM * p.ldc * 4 < lim && mn_ok(p.lda, p.A) && mn_ok(p.ldb, p.B);
+    const bool small = tiles < 128;  // 128x128 tiles
+    const int64_t bm = small ? 128 : DMA_BM;
+    const bool ok = p.ta && !p.tb && DMA_RING32 == 5 && p.K > 0 &&
+                    bm * p.ldc * 4 < lim && mn_ok(p.lda, p.A) && mn_ok(p.ldb, p.B);
     if (!ok) return hipErrorNotSupported;
     const bool ktail = p.K % DMA_BK != 0;
-#define REGTILE_DMA_MN_NAME(elt)                                                                   \
-    elt "_mfma32x32x16_dma_tr_" REGTILE_STR(DMA_BM) "x" REGTILE_STR(DMA_BN) "x" REGTILE_STR(DMA_BK) \
-        "_w" REGTILE_STR(DMA_WM) "x" REGTILE_STR(DMA_WN) "_tn"
-    static const char *const names[2][2] = {
-        {REGTILE_DMA_MN_NAME("bf16"), REGTILE_DMA_MN_NAME("bf16") "_ktail"},
-        {REGTILE_DMA_MN_NAME("f16"), REGTILE_DMA_MN_NAME("f16") "_ktail"}};
+#define REGTILE_DMA_MN_NAME(elt, bm, bn)                                                           \
+    elt "_mfma32x32x16_dma_tr_" bm "x" bn "x" REGTILE_STR(DMA_BK) "_w" REGTILE_STR(DMA_WM) "x"       \
+        REGTILE_STR(DMA_WN) "_tn"
+#define REGTILE_DMA_MN_PAIR(elt, bm, bn) {REGTILE_DMA_MN_NAME(elt, bm, bn), REGTILE_DMA_MN_NAME(elt, bm, bn) "_ktail"}
+    static const char *const names[2][2][2] = {
+        {REGTILE_DMA_MN_PAIR("bf16", REGTILE_STR(DMA_BM), REGTILE_STR(DMA_BN)), REGTILE_DMA_MN_PAIR("bf16", "128", "128")},
+        {REGTILE_DMA_MN_PAIR("f16", REGTILE_STR(DMA_BM), REGTILE_STR(DMA_BN)), REGTILE_DMA_MN_PAIR("f16", "128", "128")}};
+#undef REGTILE_DMA_MN_PAIR
 #undef REGTILE_DMA_MN_NAME
-    *name = names[f16][ktail];
-#define REGTILE_MN_LAUNCH(F16_, KT_) \
-    launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, 0, KT_, 3>(p, s)
+    *name = names[f16][small][ktail];
+    // small: the K-contiguous kernel's 128x128 set-up (two DMA windows per slab, no stagger)
+#define REGTILE_MN_LAUNCH(F16_, KT_)                                                               \
+    (small ? launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, 2, 0, F16_, 5, 0, KT_, 3>(p, s)             \
+           : launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, 0, KT_, 3>(p, s))
     if (f16) return ktail ? REGTILE_MN_LAUNCH(true, true) : REGTILE_MN_LAUNCH(true, false);
     return ktail ? REGTILE_MN_LAUNCH(false, true) : REGTILE_MN_LAUNCH(false, false);
 #undef REGTILE_MN_LAUNCH

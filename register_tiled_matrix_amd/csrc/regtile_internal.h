@@ -46,8 +46,8 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 // without launching otherwise.
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16);
 // "t n" (A stored K x M, B stored K x N) with both operands in their own storage in LDS (DMA)
-// and transposing fragment reads; at least 128 tiles of 256x256, 16-byte aligned rows;
-// hipErrorNotSupported without launching otherwise.
+// and transposing fragment reads (256x256 tiles, or 128x128 below 128 tiles of 256x256);
+// 16-byte aligned rows; hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16);
 
 // Host-side launch checks.

@@ -229,7 +229,10 @@ def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
 
 TN_DMA = [("bf16", (4096, 2048, 320), "integer", "sampled"), ("f16", (4096, 2048, 320), "normal", "sampled"),
           ("bf16", (4000, 4104, 200), "normal", "full"), ("bf16", (4104, 4000, 1000), "integer", "sampled"),
-          ("bf16", (8192, 8192, 8192), "normal", "sampled")]
+          ("bf16", (8192, 8192, 8192), "normal", "sampled"),
+          # fewer than 128 tiles of 256x256: 128x128 tiles
+          ("bf16", (1000, 1504, 777), "normal", "full"), ("f16", (2048, 2048, 4096), "integer", "sampled"),
+          ("bf16", (1536, 1032, 520), "integer", "sampled"), ("f16", (40, 8, 3), "normal", "full")]
 
 
 @pytest.mark.parametrize("dtype,shape,dist,mode", TN_DMA,
@@ -251,6 +254,7 @@ def test_16bit_tn_on_the_dma_kernel(dtype, shape, dist, mode):
     got, name = _run(inp, 1, 0, rt.ALGO_BF16_MFMA)
     assert "_dma_tr_" in name and (name.endswith("_tn") or name.endswith("_tn_ktail")), name
     assert name.endswith("_ktail") == (K % 64 != 0), name
+    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) < 128), name
     if dist == "integer":
         I, J = sample_positions(M, N, n_random=50000, seed=10)
         ref, _ = oracle.gemm_inputs_entries(inp, I, J)
