@@ -695,7 +695,7 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 // "t n": A stored K x M and B stored K x N, both M/N-contiguous. Both reach LDS by DMA in their
 // own storage and feed the MFMAs through transposing LDS reads (the kernel template takes
 // either operand that way; for "n n" and "t t" the register-row kernel measured level or
-// faster, so only "t n" launches it). Fewer than 128 tiles of 256x256 run on 128x128 tiles.
+// faster, so only "t n" launches it). Up to 128 tiles of 256x256 run on 128x128 tiles.
 // Returns hipErrorNotSupported (launching nothing) unless both operands' rows are 16-byte
 // aligned within 32-bit offsets over all of K. M, N and K may end inside a tile.
 hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16) {
@@ -704,7 +704,7 @@ hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char *
         return ld % 8 == 0 && aligned16(ptr) && ((int64_t)p.K + 64) * ld * 2 + 512 < lim;
     };
     const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool small = tiles < 128;  // 128x128 tiles
+    const bool small = tiles <= 128;  // 128x128 tiles
     const int64_t bm = small ? 128 : DMA_BM;
     const bool ok = p.ta && !p.tb && DMA_RING32 == 5 && p.K > 0 &&
                     bm * p.ldc * 4 < lim && mn_ok(p.lda, p.A) && mn_ok(p.ldb, p.B);
@@ -731,7 +731,7 @@ hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char *
 
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)
 // or "t t" (A stored K x M, B stored N x K). The K-contiguous operand goes over LDS DMA, the
-// other as 8-byte row runs through registers, transposed into the slab. Fewer than 128 tiles
+// other as 8-byte row runs through registers, transposed into the slab. Up to 128 tiles
 // of 256x256 run on 128x128 tiles. Returns hipErrorNotSupported (launching nothing) unless K
 // is a multiple of 8, the DMA operand's rows are 16-byte aligned within 32-bit tile offsets,
 // and the row operand's rows are 8-byte aligned within 32-bit offsets over all of K. M, N and
@@ -739,7 +739,7 @@ hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char *
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16) {
     const bool nn = !p.ta && !p.tb, tt = p.ta && p.tb;
     const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool small = tiles < 128;  // 128x128 tiles, as in the K-contiguous kernel
+    const bool small = tiles <= 128;  // 128x128 tiles, as in the K-contiguous kernel
     const int64_t bm = small ? 128 : DMA_BM, bn = small ? 128 : DMA_BN;
     const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && bm * p.lda * 2 < (int64_t(1) << 31))
                            : (p.ldb % 8 == 0 && aligned16(p.B) && bn * p.ldb * 2 < (int64_t(1) << 31));

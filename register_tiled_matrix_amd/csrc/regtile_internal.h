@@ -42,11 +42,11 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
 hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
                                 bool f16);
 // "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) with K a
-// multiple of 8 (256x256 tiles, or 128x128 below 128 tiles of 256x256); hipErrorNotSupported
+// multiple of 8 (256x256 tiles, or 128x128 up to 128 tiles of 256x256); hipErrorNotSupported
 // without launching otherwise.
 hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16);
 // "t n" (A stored K x M, B stored K x N) with both operands in their own storage in LDS (DMA)
-// and transposing fragment reads (256x256 tiles, or 128x128 below 128 tiles of 256x256);
+// and transposing fragment reads (256x256 tiles, or 128x128 up to 128 tiles of 256x256);
 // 16-byte aligned rows; hipErrorNotSupported without launching otherwise.
 hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16);
 

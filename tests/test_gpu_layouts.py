@@ -182,7 +182,7 @@ def test_16bit_row_operand_on_the_dma_kernel(ta, tb, dtype, dist):
 # 8-byte runs, yet not of 256)
 ROWS_RAGGED = [("bf16", 0, 0, (8000, 4100, 1000), "normal"), ("f16", 1, 1, (4100, 8000, 72), "normal"),
                ("bf16", 0, 0, (4097, 8188, 64), "integer"), ("bf16", 1, 1, (4000, 4101, 200), "integer"),
-               # fewer than 128 tiles of 256x256: 128x128 tiles
+               # at most 128 tiles of 256x256: 128x128 tiles
                ("bf16", 0, 0, (1000, 1500, 776), "normal"), ("f16", 1, 1, (700, 900, 200), "normal"),
                ("bf16", 0, 0, (1536, 1028, 2048), "integer"), ("bf16", 1, 1, (2000, 1001, 520), "integer"),
                ("f16", 0, 0, (33, 4, 8), "normal")]
@@ -216,7 +216,7 @@ def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
     lay = "_nn" if ta == 0 else "_tt"
     assert "_dma_" in name and (name.endswith(lay) or name.endswith(lay + "_ktail")), name
     assert name.endswith("_ktail") == (K % 64 != 0), name
-    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) < 128), name
+    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) <= 128), name
     assert torch.all(big[:, N:] == -77.0).item(), "a store landed past column N"
     got = C.cpu().numpy()
     if dist == "integer":
@@ -230,7 +230,7 @@ def test_16bit_row_operand_dma_ragged(dtype, ta, tb, shape, dist):
 TN_DMA = [("bf16", (4096, 2048, 320), "integer", "sampled"), ("f16", (4096, 2048, 320), "normal", "sampled"),
           ("bf16", (4000, 4104, 200), "normal", "full"), ("bf16", (4104, 4000, 1000), "integer", "sampled"),
           ("bf16", (8192, 8192, 8192), "normal", "sampled"),
-          # fewer than 128 tiles of 256x256: 128x128 tiles
+          # at most 128 tiles of 256x256: 128x128 tiles
           ("bf16", (1000, 1504, 777), "normal", "full"), ("f16", (2048, 2048, 4096), "integer", "sampled"),
           ("bf16", (1536, 1032, 520), "integer", "sampled"), ("f16", (40, 8, 3), "normal", "full")]
 
@@ -254,7 +254,7 @@ def test_16bit_tn_on_the_dma_kernel(dtype, shape, dist, mode):
     got, name = _run(inp, 1, 0, rt.ALGO_BF16_MFMA)
     assert "_dma_tr_" in name and (name.endswith("_tn") or name.endswith("_tn_ktail")), name
     assert name.endswith("_ktail") == (K % 64 != 0), name
-    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) < 128), name
+    assert ("_128x128x64_" in name) == (((M + 255) // 256) * ((N + 255) // 256) <= 128), name
     if dist == "integer":
         I, J = sample_positions(M, N, n_random=50000, seed=10)
         ref, _ = oracle.gemm_inputs_entries(inp, I, J)
