@@ -10,10 +10,11 @@
 //
 // Operands are K-contiguous on both sides (A row-major, B column-major), so A and B slabs
 // share one LDS layout: a tile row (an A row, or a B column) is BK = 64 bf16 = 8 chunks of
-// 16 bytes, and chunk c of row r is stored at slot c ^ (r & 7). A fragment read (lanes 0..31
-// = 32 consecutive rows, same chunk) then spreads every 8 consecutive lanes over 8 distinct
-// slots = 128 bytes = all 32 banks, so the reads are free of bank conflicts, and the
-// cooperative 16-byte stores (8 lanes per row) are too.
+// 16 bytes, and chunk c of row r is stored at slot c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1)
+// (addr::slab_key for 32x32 fragments). gfx950's LDS has 64 banks and serves a 128-bit read
+// 16 lanes at a time, so two addresses 256 bytes apart collide; under this key the 16 rows
+// (one chunk each) of a fragment read's half-wave land in 16 distinct 16-byte bank groups,
+// and the reads are free of bank conflicts (r & 7 alone left a 2-way conflict, measured).
 //
 // Pipeline: two LDS stages; the next slab's global loads (16-byte, coalesced: 8 lanes cover
 // one 128-byte row segment) are issued into registers before the current slab's MFMAs and
@@ -99,19 +100,22 @@ __device__ __forceinline__ void transpose_block(const uint32_t lo[8], const uint
     }
 }
 
-// The block through a buffer descriptor over the slab's K rows that lie before K (base: the
-// slab's first row at the tile's first column, `rows` rows of `ld` elements), for ld a
-// multiple of 4, so that no 8-byte run crosses the end of a row: rows past K read zeros;
-// columns past M or N read whatever follows in the row, or zeros past the descriptor, and
-// only feed outputs the epilogue drops. `off` is the block's byte offset from the base.
-// Eight buffer_load_dwordx2 with one lane offset and uniform row offsets, no predication.
-__device__ __forceinline__ void load_block_mn_buf(const uint16_t *base, int64_t ld, int rows, uint32_t off,
-                                                  uint4 out[4]) {
-    const mfma::rsrc_t r = mfma::make_rsrc(base, (uint32_t)(rows * ld * 2));
+// The block through a buffer descriptor over the slab's rows that lie before K (base: the
+// slab's first row at the tile's first column, `rows` rows of `ld` elements), ending at the
+// operand's column M - 1 (N - 1) of the last of those rows (`cols_from` = columns from the
+// tile's first to the operand's last). Taken only when ld and the operand's column count are
+// multiples of 4 (addr::gather_desc_takes), so that no 8-byte run crosses a row end or that
+// descriptor end: rows past K read zeros, and so do the last row's columns past M or N;
+// other columns past M or N read the operand's own storage and only feed outputs the
+// epilogue drops. `off` is the block's byte offset from the base. Eight buffer_load_dwordx2
+// with one lane offset and uniform row offsets, no predication.
+__device__ __forceinline__ void load_block_mn_buf(const uint16_t *base, int64_t ld, int rows, int cols_from,
+                                                  uint32_t off, uint4 out[4]) {
+    const mfma::rsrc_t r = mfma::make_rsrc(base, addr::desc_bytes(rows, ld, cols_from, 2));
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-        const uint2 v = mfma::load_b64_buf(r, off, (uint32_t)(kk * ld * 2));
+        const uint2 v = mfma::load_b64_buf(r, off, addr::row_run_off(kk, ld));
         lo[kk] = v.x;
         hi[kk] = v.y;
     }
@@ -184,15 +188,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
     // dimension is a multiple of 4, else as global loads with edge checks).
     static_assert(!A_MN || BM * BK == 32 * NT, "one 4 x 8 block of A per thread");
     static_assert(!B_MN || BN * BK == 32 * NT, "one 4 x 8 block of B per thread");
-    const int amn_row = (tid % (BM / 4)) * 4, amn_chunk = tid / (BM / 4);
-    const int bmn_row = (tid % (BN / 4)) * 4, bmn_chunk = tid / (BN / 4);
+    const int amn_row = addr::row_block_col(tid, BM), amn_chunk = addr::row_block_kc(tid, BM);
+    const int bmn_row = addr::row_block_col(tid, BN), bmn_chunk = addr::row_block_kc(tid, BN);
 
     uint4 ra[A_CH], rb[B_CH];
     auto load_slab = [&](int k0) {
         if (A_MN) {
-            if ((lda & 3) == 0)
-                load_block_mn_buf(A + (int64_t)k0 * lda + m0, lda, min(BK, K - k0),
-                                  (uint32_t)(amn_chunk * 8 * lda + amn_row) * 2u, ra);
+            if (addr::gather_desc_takes(M, lda))
+                load_block_mn_buf(A + (int64_t)k0 * lda + m0, lda, min(BK, K - k0), M - m0,
+                                  addr::row_block_off(tid, BM, lda), ra);
             else
                 load_block_mn_any(A + (int64_t)(k0 + amn_chunk * 8) * lda + m0 + amn_row, lda,
                                   M - (m0 + amn_row), K - (k0 + amn_chunk * 8), ra);
@@ -204,9 +208,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_kernel(
                                               K - k0 - ld_chunk * 8);
         }
         if (B_MN) {
-            if ((ldb & 3) == 0)
-                load_block_mn_buf(B + (int64_t)k0 * ldb + n0, ldb, min(BK, K - k0),
-                                  (uint32_t)(bmn_chunk * 8 * ldb + bmn_row) * 2u, rb);
+            if (addr::gather_desc_takes(N, ldb))
+                load_block_mn_buf(B + (int64_t)k0 * ldb + n0, ldb, min(BK, K - k0), N - n0,
+                                  addr::row_block_off(tid, BN, ldb), rb);
             else
                 load_block_mn_any(B + (int64_t)(k0 + bmn_chunk * 8) * ldb + n0 + bmn_row, ldb,
                                   N - (n0 + bmn_row), K - (k0 + bmn_chunk * 8), rb);
@@ -361,13 +365,14 @@ const char *const kLayoutNames[2][2][3][2] = {
 
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16) {
+    hipError_t err = hipSuccess;
     if ((p.ta || !p.tb) && shape == 32) {
         // M/N-contiguous operands on the LDS-DMA kernel: "t n" in their own storage with
         // transposing fragment reads; "n n" / "t t" with the M/N-contiguous operand through
         // registers as rows (the transposing reads measured level or 3% slower there)
-        const hipError_t e = p.ta == p.tb ? launch_bf16_mfma_dma_rows(p, s, name, f16)
-                                          : launch_bf16_mfma_dma_mn(p, s, name, f16);
-        if (e != hipErrorNotSupported) return e;
+        const bool taken = p.ta == p.tb ? launch_bf16_mfma_dma_rows(p, s, name, f16, &err)
+                                        : launch_bf16_mfma_dma_mn(p, s, name, f16, &err);
+        if (taken) return err;
     }
     if (p.ta || !p.tb) {  // not the native K-contiguous pair
         // an M/N-contiguous operand is gathered through one descriptor per slab of 64 of its
@@ -383,10 +388,7 @@ hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, 
     }
     // K a multiple of 8 and 16-byte aligned rows: the LDS-DMA kernel, else the
     // register-staged kernel below.
-    {
-        const hipError_t e = launch_bf16_mfma_dma(p, s, name, shape, f16);
-        if (e != hipErrorNotSupported) return e;
-    }
+    if (launch_bf16_mfma_dma(p, s, name, shape, f16, &err)) return err;
     const bool vec = (p.lda % 8) == 0 && (p.ldb % 8) == 0 && aligned16(p.A) && aligned16(p.B);
     const bool big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
     const int tile = big ? 256 : 128;

@@ -21,9 +21,10 @@
 //      KCH = 4 (64-byte rows): key(r) = (r >> 2) & 3
 //  * M/N-contiguous operands: as rows staged through registers ("n n", "t t"), or in their own
 //    storage with transposing fragment reads ("t n"); see the kernel.
-//  * Edges: descriptors end at the last real row, so loads past it read zeros and stores past
-//    it are dropped; columns past N get an out-of-range store offset; chunks past K in the
-//    last slab an out-of-range load offset.
+//  * Edges: every descriptor ends at the last element of the matrix it covers
+//    (tile_addressing.h), so loads past it read zeros and stores past it are dropped; columns
+//    past N get an out-of-range store offset; chunks past K in the last slab an out-of-range
+//    load offset. Nothing outside the caller's matrices is read or written.
 //  * Two LDS stages and one barrier per slab, placed inside the slab's last k step: the
 //    next slab is loaded while the current one is consumed, and its first fragments are
 //    read before the current slab's last MFMAs (section 6.3: prefetch of the next k slice
@@ -72,9 +73,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // descriptor's end, which puts zeros in LDS.
     // MN: bit 0, A is stored K x M; bit 1, B is stored K x N. Such an operand keeps its storage
     // in LDS: a slab of BK rows (k) of BM (BN) elements, 16-byte chunk c of row r at slot
-    // c ^ mkey(r). Its DMA reads through a descriptor over its K rows from the tile's first
-    // column (rows past K read zeros, columns past M or N only feed dropped outputs), and its
-    // fragments come from pairs of transposing LDS reads.
+    // c ^ mn_key(r). Its DMA reads through a descriptor over its K rows from the tile's first
+    // column that ends at the operand's last element (rows past K read zeros; other columns
+    // past M or N only feed dropped outputs), and its fragments come from pairs of
+    // transposing LDS reads.
     constexpr bool A_MN = (MN & 1) != 0, B_MN = (MN & 2) != 0;
     static_assert(MN == 0 || (ROWS == 0 && RING == 5 && MF == 32 && BM == BN && (BM == 256 || BM == 128) && BK == 64),
                   "M/N-major slabs: 32x32x16 fragments on the 256x256 or 128x128 ring");
@@ -101,36 +103,32 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // operand; instruction and slab offsets are wave-uniform (SGPR).
     constexpr int ROWS_PER_INSTR = 64 / KCH;
     static_assert(KCH == 4 || (ROWS_PER_INSTR == 8 && JA % 2 == 0 && JB % 2 == 0), "key periodicity");
-    // A tile of the last tile row (column) may extend past M (N): its descriptors end at the
-    // last real row, so DMA loads of the rows beyond read zeros.
+    // Every descriptor ends at the last element of the matrix it reads (tile_addressing.h):
+    // a K-contiguous tile's at element K - 1 of its last real row, so that DMA loads of rows
+    // past M (N) read zeros; an M/N-major operand's at column M - 1 (N - 1) of row K - 1, so
+    // that rows past K and that row's columns past M (N) read zeros. The launchers admit an
+    // M/N-major operand only when its column count and leading dimension are multiples of 8,
+    // so no 16-byte chunk straddles that end.
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-    const rsrc_t a_rsrc = A_MN ? make_rsrc(A + m0, (uint32_t)(K * lda * 2))
-                               : make_rsrc(A + (int64_t)m0 * lda, (uint32_t)(rows_a * lda * 2));
-    const rsrc_t b_rsrc = B_MN ? make_rsrc(B + n0, (uint32_t)(K * ldb * 2))
-                               : make_rsrc(B + (int64_t)n0 * ldb, (uint32_t)(rows_b * ldb * 2));
+    const rsrc_t a_rsrc = A_MN ? make_rsrc(A + m0, addr::desc_bytes(K, lda, M - m0, 2))
+                               : make_rsrc(A + (int64_t)m0 * lda, addr::desc_bytes(rows_a, lda, K, 2));
+    const rsrc_t b_rsrc = B_MN ? make_rsrc(B + n0, addr::desc_bytes(K, ldb, N - n0, 2))
+                               : make_rsrc(B + (int64_t)n0 * ldb, addr::desc_bytes(rows_b, ldb, K, 2));
     const int nslabs = KTAIL ? (K + BK - 1) / BK : K / BK;
     const int k_last = (nslabs - 1) * BK;  // first k of the last slab
     // An M/N-major slab row holds MCH chunks; one DMA instruction covers MROWS = 64 / MCH rows.
     constexpr int MCH = BM / 8, MROWS = 64 / MCH;
-    auto mkey = [](int row) { return 4 * (row & 3); };
     uint32_t a_voff[2], b_voff[2], a_voff_last[2], b_voff_last[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int pa = (wave * JA + j) * 64 + lane;
-        const int ra = pa / KCH, ca = (pa % KCH) ^ slab_key<KCH, MF>(ra);
-        a_voff[j] = (uint32_t)(ra * lda + ca * 8) * 2u;
-        const int pb = (wave * JB + j) * 64 + lane;
-        const int rb = pb / KCH, cb = (pb % KCH) ^ slab_key<KCH, MF>(rb);
-        b_voff[j] = (uint32_t)(rb * ldb + cb * 8) * 2u;
-        // (2^31 exceeds every tile's byte count; the uniform parts added to it stay below 2^32)
-        a_voff_last[j] = k_last + ca * 8 < K ? a_voff[j] : a_voff[j] | 0x80000000u;
-        b_voff_last[j] = k_last + cb * 8 < K ? b_voff[j] : b_voff[j] | 0x80000000u;
-        // M/N-major: instruction q fills rows MROWS (wave * J + q) .. +MROWS-1; its lane part
-        // is the row within those and the source chunk of slot lane % MCH (the key, a function
-        // of row % 4, repeats every two instructions: J is even, MROWS 2 or 4)
-        const int r_in = lane / MCH, slot = lane % MCH, key = mkey(MROWS * j + r_in);
-        if (A_MN) a_voff[j] = (uint32_t)(r_in * lda + (slot ^ key) * 8) * 2u;
-        if (B_MN) b_voff[j] = (uint32_t)(r_in * ldb + (slot ^ key) * 8) * 2u;
+        int ka, kb;  // first k of each lane's chunk within the slab
+        a_voff[j] = addr::kc_dma_lane<KCH, MF>(wave, JA, j, lane, lda, &ka);
+        b_voff[j] = addr::kc_dma_lane<KCH, MF>(wave, JB, j, lane, ldb, &kb);
+        // (the uniform parts added to kPastEnd stay below 2^32)
+        a_voff_last[j] = k_last + ka < K ? a_voff[j] : a_voff[j] | addr::kPastEnd;
+        b_voff_last[j] = k_last + kb < K ? b_voff[j] : b_voff[j] | addr::kPastEnd;
+        if (A_MN) a_voff[j] = addr::mn_dma_lane(lane, j, lda, MCH);
+        if (B_MN) b_voff[j] = addr::mn_dma_lane(lane, j, ldb, MCH);
     }
     static_assert(MN == 0 || (JA % 2 == 0 && JB % 2 == 0 && (MROWS == 2 || MROWS == 4)),
                   "two or four rows per instruction");
@@ -140,16 +138,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     auto voff_b = [&](int q, int k0) {
         return KTAIL && !B_MN && k0 == k_last ? b_voff_last[q & 1] : b_voff[q & 1];
     };
-    const uint32_t a_step = (uint32_t)(ROWS_PER_INSTR * lda) * 2u;  // bytes per instruction
-    const uint32_t b_step = (uint32_t)(ROWS_PER_INSTR * ldb) * 2u;
     // uniform byte offset of DMA instruction q of the slab starting at k0
     auto soff_a = [&](int q, int k0) {
-        return A_MN ? (uint32_t)(MROWS * (wave * JA + q) + k0) * (uint32_t)lda * 2u
-                    : (uint32_t)(q & ~1) * a_step + (uint32_t)k0 * 2u;
+        return A_MN ? addr::mn_dma_instr(wave, JA, q, k0, lda, MCH) : addr::kc_dma_instr<KCH>(q, k0, lda);
     };
     auto soff_b = [&](int q, int k0) {
-        return B_MN ? (uint32_t)(MROWS * (wave * JB + q) + k0) * (uint32_t)ldb * 2u
-                    : (uint32_t)(q & ~1) * b_step + (uint32_t)k0 * 2u;
+        return B_MN ? addr::mn_dma_instr(wave, JB, q, k0, ldb, MCH) : addr::kc_dma_instr<KCH>(q, k0, ldb);
     };
     // DMA instruction q (A for q < JA, then B) of the slab starting at k0.
     auto dma_q = [&](int q, int k0, uint4 *sa, uint4 *sb) {
@@ -187,29 +181,31 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
                   "whole 4 x 8 blocks per thread");
     constexpr int NBL = ANY_ROW ? B_BLOCKS * 8 : 0;  // row loads per thread per slab
     // The row operand's loads go through a descriptor over its K rows (of ld_row elements)
-    // from the tile's first column: rows at or past K read zeros (the K tail); columns past M
-    // or N read whatever follows in memory, or zeros past the end, and only feed outputs that
-    // are never stored.
+    // from the tile's first column, ending at its last element: rows at or past K read zeros
+    // (the K tail), and so do the last row's columns past M or N (the launcher admits a row
+    // operand only when its column count and leading dimension are multiples of 4, so no
+    // 8-byte run straddles that end). Other columns past M or N read the operand's own
+    // storage and only feed outputs that are never stored.
     const uint16_t *const rsrc_base = A_ROW ? A + m0 : B + n0;
     const int64_t ld_row = A_ROW ? lda : ldb;
-    const rsrc_t row_rsrc = make_rsrc(rsrc_base, (uint32_t)(K * ld_row * 2));
+    const rsrc_t row_rsrc = make_rsrc(rsrc_base, addr::desc_bytes(K, ld_row, A_ROW ? M - m0 : N - n0, 2));
     uint32_t bl[B_BLOCKS][8], bh[B_BLOCKS][8];
     int brow_n[B_BLOCKS], brow_kc[B_BLOCKS];
     uint32_t brow_off[B_BLOCKS];
 #pragma unroll
     for (int i = 0; i < B_BLOCKS; ++i) {
         const int b = tid + NT * i;
-        brow_n[i] = (b % (RLEN / 4)) * 4;
-        brow_kc[i] = b / (RLEN / 4);
-        brow_off[i] = (uint32_t)((brow_kc[i] * 8) * ld_row + brow_n[i]) * 2u;
+        brow_n[i] = addr::row_block_col(b, RLEN);
+        brow_kc[i] = addr::row_block_kc(b, RLEN);
+        brow_off[i] = addr::row_block_off(b, RLEN, ld_row);
     }
     auto load_brow = [&](int slab) {
-        const uint32_t k0 = (uint32_t)min(slab, nslabs - 1) * BK;
+        const int k0 = min(slab, nslabs - 1) * BK;
 #pragma unroll
         for (int i = 0; i < B_BLOCKS; ++i)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const uint2 v = load_b64_buf(row_rsrc, brow_off[i], (k0 + kk) * (uint32_t)ld_row * 2u);
+                const uint2 v = load_b64_buf(row_rsrc, brow_off[i], addr::row_run_off(k0 + kk, ld_row));
                 bl[i][kk] = v.x;
                 bh[i][kk] = v.y;
             }
@@ -252,7 +248,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
         const char *base = reinterpret_cast<const char *>(slab);
         const int row = kk * F::KSTEP + tr_row, col = col0 + tr_col;
         // row & 3 == tr_t >> 2 for both reads (rows 4 apart)
-        const int off = ((col >> 3) ^ mkey(row)) * 16 + (col & 7) * 2;
+        const int off = ((col >> 3) ^ addr::mn_key(row)) * 16 + (col & 7) * 2;
         const uint2 lo = lds_read_tr16(base + row * (MCH * 16) + off);
         const uint2 hi = lds_read_tr16(base + (row + 4) * (MCH * 16) + off);
         return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -574,19 +570,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
     // (past M, the descriptor drops the stores of the rows beyond; past N, lanes whose column
     // is beyond N get an offset past the descriptor's end, 2^31 > BM rows of C, so the
     // hardware drops those stores too)
-    const rsrc_t c_rsrc = make_rsrc(C + (int64_t)m0 * ldc + n0, (uint32_t)(min(BM, M - m0) * ldc * 4));
+    const rsrc_t c_rsrc = make_rsrc(C + (int64_t)m0 * ldc + n0, addr::desc_bytes(min(BM, M - m0), ldc, N - n0, 4));
     // (the lane index is recomputed from mbcnt so no thread-id register stays live across
     // the main loop)
     const int elane = __lane_id();
-    const uint32_t lane_off =
-        (uint32_t)((wm * WTM + F::row_lane(elane)) * ldc + wn * WTN + elane % MF) * 4u;
+    const uint32_t lane_off = addr::c_lane_off<MF>(wm * WTM, wn * WTN, elane, ldc);
     uint32_t lane_off_j[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-        lane_off_j[j] = n0 + wn * WTN + j * MF + elane % MF < N ? lane_off : 0x80000000u;
-    auto c_off = [&](int i, int j, int v) {
-        return (uint32_t)((i * MF + F::row_acc(v)) * ldc + j * MF) * 4u;
-    };
+        lane_off_j[j] = n0 + wn * WTN + j * MF + elane % MF < N ? lane_off : addr::kPastEnd;
+    auto c_off = [&](int i, int j, int v) { return addr::c_acc_off<MF>(i, j, v, ldc); };
     if (beta != 0.0f) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -658,22 +651,19 @@ hipError_t launch_dma_shape(const Problem &p, hipStream_t s, int shape, bool sma
 
 }  // namespace
 
-// Returns hipErrorNotSupported (and launches nothing) unless K is a multiple of 8 and the rows
-// are 16-byte aligned and K-contiguous. M and N may end inside a tile (the tile's descriptors
-// stop at the last real row and column) and K inside the last slab (its chunks past K load
-// as zeros). Up to 128 tiles of 256x256 (half a tile per CU) run on 128x128 tiles, which
-// measured 24-76% faster there (2048x4096x4096: 986 against 769-799 TFLOP/s) and 5-10% slower
-// from 144 tiles on (3072^3: 796 against 840), always with 32x32x16 fragments.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
-                                bool f16) {
-    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool small = tiles <= 128;
-    const int64_t bm = small ? 128 : DMA_BM, bn = small ? 128 : DMA_BN;
-    const bool ok = p.K % 8 == 0 && p.K > 0 &&
-                    p.lda % 8 == 0 && p.ldb % 8 == 0 && aligned16(p.A) && aligned16(p.B) &&
-                    bm * p.lda * 2 < (int64_t(1) << 31) && bn * p.ldb * 2 < (int64_t(1) << 31) &&
-                    bm * p.ldc * 4 < (int64_t(1) << 31) && (shape == 32 || shape == 16);
-    if (!ok) return hipErrorNotSupported;
+// Takes (and launches, status in *err) every problem whose operands are K-contiguous with
+// K a multiple of 8 and 16-byte aligned rows (addr::kc_dma_takes); returns false, launching
+// nothing, for any other. M and N may end inside a tile (the tile's descriptors stop at the
+// last real row and column) and K inside the last slab (its chunks past K load as zeros). Up
+// to 128 tiles of 256x256 (half a tile per CU) run on 128x128 tiles, which measured 24-76%
+// faster there (2048x4096x4096: 986 against 769-799 TFLOP/s) and 5-10% slower from 144 tiles
+// on (3072^3: 796 against 840), always with 32x32x16 fragments.
+bool launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape, bool f16,
+                          hipError_t *err) {
+    const bool small = addr::dma_tile(p.M, p.N) == 128;
+    if (!(addr::kc_dma_takes(p.M, p.N, p.K, p.lda, p.ldb, p.ldc) && aligned16(p.A) && aligned16(p.B) &&
+          (shape == 32 || shape == 16)))
+        return false;
     const bool ktail = p.K % DMA_BK != 0;
     const int kind = small ? 2 : shape == 16;  // 0: 256x256 32x32x16, 1: 256x256 16x16x32, 2: 128x128
 #define REGTILE_DMA_NAME(elt, mf, bm, bn)                                                          \
@@ -688,27 +678,27 @@ hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **na
 #undef REGTILE_DMA_NAMES
 #undef REGTILE_DMA_NAME
     *name = names[f16][kind][ktail];
-    if (f16) return ktail ? launch_dma_shape<true, true>(p, s, shape, small) : launch_dma_shape<true, false>(p, s, shape, small);
-    return ktail ? launch_dma_shape<false, true>(p, s, shape, small) : launch_dma_shape<false, false>(p, s, shape, small);
+    if (f16)
+        *err = ktail ? launch_dma_shape<true, true>(p, s, shape, small) : launch_dma_shape<true, false>(p, s, shape, small);
+    else
+        *err = ktail ? launch_dma_shape<false, true>(p, s, shape, small) : launch_dma_shape<false, false>(p, s, shape, small);
+    return true;
 }
 
 // "t n": A stored K x M and B stored K x N, both M/N-contiguous. Both reach LDS by DMA in their
 // own storage and feed the MFMAs through transposing LDS reads (the kernel template takes
 // either operand that way; for "n n" and "t t" the register-row kernel measured level or
 // faster, so only "t n" launches it). Up to 128 tiles of 256x256 run on 128x128 tiles.
-// Returns hipErrorNotSupported (launching nothing) unless both operands' rows are 16-byte
-// aligned within 32-bit offsets over all of K. M, N and K may end inside a tile.
-hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16) {
-    const int64_t lim = int64_t(1) << 31;
-    auto mn_ok = [&](int64_t ld, const void *ptr) {
-        return ld % 8 == 0 && aligned16(ptr) && ((int64_t)p.K + 64) * ld * 2 + 512 < lim;
-    };
-    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool small = tiles <= 128;  // 128x128 tiles
-    const int64_t bm = small ? 128 : DMA_BM;
-    const bool ok = p.ta && !p.tb && DMA_RING32 == 5 && p.K > 0 &&
-                    bm * p.ldc * 4 < lim && mn_ok(p.lda, p.A) && mn_ok(p.ldb, p.B);
-    if (!ok) return hipErrorNotSupported;
+// Takes (and launches, status in *err) a problem only when both operands' leading dimensions
+// and column counts are multiples of 8 (so no 16-byte chunk straddles a descriptor that ends
+// at the operand's last element), their rows are 16-byte aligned, and the offsets over all of
+// K fit in 32 bits (addr::mn_dma_takes); returns false, launching nothing, otherwise. K and
+// the tile grid may end anywhere.
+bool launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16, hipError_t *err) {
+    const bool small = addr::dma_tile(p.M, p.N) == 128;  // 128x128 tiles
+    if (!(p.ta && !p.tb && DMA_RING32 == 5 && addr::mn_dma_takes(p.M, p.N, p.K, p.lda, p.ldb, p.ldc) &&
+          aligned16(p.A) && aligned16(p.B)))
+        return false;
     const bool ktail = p.K % DMA_BK != 0;
 #define REGTILE_DMA_MN_NAME(elt, bm, bn)                                                           \
     elt "_mfma32x32x16_dma_tr_" bm "x" bn "x" REGTILE_STR(DMA_BK) "_w" REGTILE_STR(DMA_WM) "x"       \
@@ -724,31 +714,28 @@ hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char *
 #define REGTILE_MN_LAUNCH(F16_, KT_)                                                               \
     (small ? launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, 2, 0, F16_, 5, 0, KT_, 3>(p, s)             \
            : launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, 0, KT_, 3>(p, s))
-    if (f16) return ktail ? REGTILE_MN_LAUNCH(true, true) : REGTILE_MN_LAUNCH(true, false);
-    return ktail ? REGTILE_MN_LAUNCH(false, true) : REGTILE_MN_LAUNCH(false, false);
+    if (f16)
+        *err = ktail ? REGTILE_MN_LAUNCH(true, true) : REGTILE_MN_LAUNCH(true, false);
+    else
+        *err = ktail ? REGTILE_MN_LAUNCH(false, true) : REGTILE_MN_LAUNCH(false, false);
+    return true;
 #undef REGTILE_MN_LAUNCH
 }
 
 // One operand M- or N-contiguous, the other K-contiguous: "n n" (A row-major, B stored K x N)
 // or "t t" (A stored K x M, B stored N x K). The K-contiguous operand goes over LDS DMA, the
 // other as 8-byte row runs through registers, transposed into the slab. Up to 128 tiles
-// of 256x256 run on 128x128 tiles. Returns hipErrorNotSupported (launching nothing) unless K
-// is a multiple of 8, the DMA operand's rows are 16-byte aligned within 32-bit tile offsets,
-// and the row operand's rows are 8-byte aligned within 32-bit offsets over all of K. M, N and
-// K may end inside a tile.
-hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16) {
+// of 256x256 run on 128x128 tiles. Takes (and launches, status in *err) a problem only when
+// K is a multiple of 8, the DMA operand's rows are 16-byte aligned within 32-bit tile offsets,
+// and the row operand's leading dimension and column count are multiples of 4 with 8-byte
+// aligned rows within 32-bit offsets over all of K (addr::rows_dma_takes); returns false,
+// launching nothing, otherwise. M, N and K may end inside a tile.
+bool launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16, hipError_t *err) {
     const bool nn = !p.ta && !p.tb, tt = p.ta && p.tb;
-    const int64_t tiles = (int64_t)((p.M + DMA_BM - 1) / DMA_BM) * ((p.N + DMA_BN - 1) / DMA_BN);
-    const bool small = tiles <= 128;  // 128x128 tiles, as in the K-contiguous kernel
-    const int64_t bm = small ? 128 : DMA_BM, bn = small ? 128 : DMA_BN;
-    const bool dma_ok = nn ? (p.lda % 8 == 0 && aligned16(p.A) && bm * p.lda * 2 < (int64_t(1) << 31))
-                           : (p.ldb % 8 == 0 && aligned16(p.B) && bn * p.ldb * 2 < (int64_t(1) << 31));
-    const int64_t ld_row = nn ? p.ldb : p.lda;
-    const bool rows_ok = ld_row % 4 == 0 && aligned8(nn ? p.B : p.A) &&
-                         ((int64_t)p.K + 128) * ld_row * 2 + 512 < (int64_t(1) << 31);
-    const bool ok = (nn || tt) && DMA_RING32 == 5 && dma_ok && rows_ok && p.K % 8 == 0 && p.K > 0 &&
-                    bm * p.ldc * 4 < (int64_t(1) << 31);
-    if (!ok) return hipErrorNotSupported;
+    const bool small = addr::dma_tile(p.M, p.N) == 128;  // 128x128 tiles, as in the K-contiguous kernel
+    if (!((nn || tt) && DMA_RING32 == 5 && addr::rows_dma_takes(nn, p.M, p.N, p.K, p.lda, p.ldb, p.ldc) &&
+          aligned16(nn ? p.A : p.B) && aligned8(nn ? p.B : p.A)))
+        return false;
     const bool ktail = p.K % DMA_BK != 0;
 #define REGTILE_DMA_ROWS_NAME(elt, bm, bn, lay)                                                   \
     elt "_mfma32x32x16_dma_" bm "x" bn "x" REGTILE_STR(DMA_BK) "_w" REGTILE_STR(DMA_WM) "x"        \
@@ -771,11 +758,13 @@ hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char
     (small ? launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, 2, 0, F16_, 5, ROWS_, KT_>(p, s)            \
            : launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16_, 5, ROWS_, KT_>(p, s))
     if (f16) {
-        if (nn) return ktail ? REGTILE_ROWS_LAUNCH(true, 1, true) : REGTILE_ROWS_LAUNCH(true, 1, false);
-        return ktail ? REGTILE_ROWS_LAUNCH(true, 2, true) : REGTILE_ROWS_LAUNCH(true, 2, false);
+        if (nn) *err = ktail ? REGTILE_ROWS_LAUNCH(true, 1, true) : REGTILE_ROWS_LAUNCH(true, 1, false);
+        else *err = ktail ? REGTILE_ROWS_LAUNCH(true, 2, true) : REGTILE_ROWS_LAUNCH(true, 2, false);
+    } else {
+        if (nn) *err = ktail ? REGTILE_ROWS_LAUNCH(false, 1, true) : REGTILE_ROWS_LAUNCH(false, 1, false);
+        else *err = ktail ? REGTILE_ROWS_LAUNCH(false, 2, true) : REGTILE_ROWS_LAUNCH(false, 2, false);
     }
-    if (nn) return ktail ? REGTILE_ROWS_LAUNCH(false, 1, true) : REGTILE_ROWS_LAUNCH(false, 1, false);
-    return ktail ? REGTILE_ROWS_LAUNCH(false, 2, true) : REGTILE_ROWS_LAUNCH(false, 2, false);
+    return true;
 #undef REGTILE_ROWS_LAUNCH
 }
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tile_addressing.h"
+
 namespace regtile {
 namespace mfma {
 
@@ -13,19 +15,8 @@ typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
-// Swizzle of a slab whose rows are KCH chunks of 16 bytes: chunk c of row r sits in slot
-// c ^ slab_key(r). Each key was chosen with LDS bank-conflict counters on the fragment read
-// of its MFMA shape (ds_read_b128: 4.07 LDS cycles conflict-free, 8.00 for a 2-way conflict):
-//   MF = 32 (lane l reads row l % 32 at chunk c + l / 32): (r & 7) ^ (r >> 3 & 1);
-//   MF = 16 (lane l reads row l % 16 at chunk c + l / 16): (r >> 1 & 7) ^ ((r & 1) << 2).
-// The second is conflict-free for both reads, the first only for MF = 32, where it measured
-// 0.5% faster end to end. Both depend on r & 15 only. 64-byte rows: (r >> 2) & 3.
-template <int KCH, int MF = 32>
-__device__ __forceinline__ int slab_key(int row) {
-    static_assert(KCH == 4 || KCH == 8, "slab rows of 64 or 128 bytes");
-    if (KCH == 8) return MF == 16 ? (((row >> 1) & 7) ^ ((row & 1) << 2)) : ((row & 7) ^ ((row >> 3) & 1));
-    return (row >> 2) & 3;
-}
+// The K-contiguous slab swizzle (tile_addressing.h).
+using addr::slab_key;
 
 // One 16-byte-per-lane DMA load: global `src` -> LDS at `dst` + lane * 16 (dst wave-uniform).
 // The body exists only in the device pass: the host pass cannot form LDS-space pointers.
@@ -180,8 +171,8 @@ struct Frag<32, F16> {
         else
             return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
-    __device__ static int row_lane(int lane) { return (lane >> 5) * 4; }
-    __device__ static constexpr int row_acc(int v) { return (v >> 2) * 8 + (v & 3); }
+    __device__ static int row_lane(int lane) { return addr::c_row_lane<32>(lane); }
+    __device__ static constexpr int row_acc(int v) { return addr::c_row_acc<32>(v); }
 };
 template <bool F16>
 struct Frag<16, F16> {
@@ -194,8 +185,8 @@ struct Frag<16, F16> {
         else
             return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
-    __device__ static int row_lane(int lane) { return (lane >> 4) * 4; }
-    __device__ static constexpr int row_acc(int v) { return v; }
+    __device__ static int row_lane(int lane) { return addr::c_row_lane<16>(lane); }
+    __device__ static constexpr int row_acc(int v) { return addr::c_row_acc<16>(v); }
 };
 
 // Workgroup barrier without the memory fence that __syncthreads() adds: the fence makes

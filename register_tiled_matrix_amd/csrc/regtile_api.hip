@@ -84,6 +84,9 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // an error left pending by an earlier, unrelated runtime call would otherwise be reported
+    // as this launch's status
+    (void)hipGetLastError();
     int status;
     if (quick_return(p, s, &status)) return status;
     const char *name = "none";
@@ -124,6 +127,9 @@ int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // an error left pending by an earlier, unrelated runtime call would otherwise be reported
+    // as this launch's status
+    (void)hipGetLastError();
     int status;
     if (quick_return(p, s, &status)) return status;
     const char *name = "none";

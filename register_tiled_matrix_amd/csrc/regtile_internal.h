@@ -36,19 +36,21 @@ hipError_t launch_bf16_naive(const Problem &p, hipStream_t s, const char **name,
 // kernel only; problems it does not take keep the 32x32x16 register-staged kernel).
 hipError_t launch_bf16_mfma(const Problem &p, hipStream_t s, const char **name, int shape,
                             bool f16);
+// The LDS-DMA kernel's three operand arrangements. Each returns false, launching nothing,
+// for a problem it does not take (tile_addressing.h states which it takes); otherwise it
+// launches and stores the launch status in *err.
 // K-contiguous A and B with 16-byte aligned rows and K a multiple of 8 (M, N and K may end
-// inside a tile; 256x256 tiles, or 128x128 up to 128 tiles of 256x256);
-// hipErrorNotSupported without launching otherwise.
-hipError_t launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape,
-                                bool f16);
+// inside a tile; 256x256 tiles, or 128x128 up to 128 tiles of 256x256).
+bool launch_bf16_mfma_dma(const Problem &p, hipStream_t s, const char **name, int shape, bool f16,
+                          hipError_t *err);
 // "n n" (A M x K, B K x N, both row-major) or "t t" (A stored K x M, B stored N x K) with K a
-// multiple of 8 (256x256 tiles, or 128x128 up to 128 tiles of 256x256); hipErrorNotSupported
-// without launching otherwise.
-hipError_t launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16);
+// multiple of 8 and the M/N-contiguous operand's column count a multiple of 4.
+bool launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **name, bool f16,
+                               hipError_t *err);
 // "t n" (A stored K x M, B stored K x N) with both operands in their own storage in LDS (DMA)
-// and transposing fragment reads (256x256 tiles, or 128x128 up to 128 tiles of 256x256);
-// 16-byte aligned rows; hipErrorNotSupported without launching otherwise.
-hipError_t launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16);
+// and transposing fragment reads; M and N multiples of 8, 16-byte aligned rows.
+bool launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16,
+                             hipError_t *err);
 
 // Host-side launch checks.
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
