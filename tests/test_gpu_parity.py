@@ -3,8 +3,9 @@
 Bar: every compared element satisfies |C_gpu - C_ref| <= 1e-5 * (|alpha| sum_k |a_ik b_kj|
 + |beta c_ij|) (oracle.check), and integer-valued inputs, whose every partial sum is exact
 in fp32, must match bitwise. Small and ragged problems are compared in full; the full-size
-workloads run in the launch configuration the benchmark times and are compared on a
-stratified sample the oracle computes entry by entry.
+workloads run in the launch configuration the benchmark times and are compared in full too;
+larger or rarer cases use a stratified sample (a whole leading tile, the whole last tile row
+and column, 65536 seeded positions) that the oracle computes entry by entry.
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import gemm_inputs as gi
 import oracle
 import register_tiled_matrix_amd as rt
 from gpu_util import (announce, assert_parity_full, assert_parity_sampled, device_operands, run,
-                      sample_positions)
+                      sample_positions, workload_reference)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -51,39 +52,63 @@ def test_f32_ragged_full(algo):
     assert_parity_full(inp, got, f"f32_ragged algo {algo} ({rt.last_kernel()})")
 
 
-def test_f32_4096_sampled():
-    inp = gi.workload_inputs(gi.WORKLOADS["f32_4096"])
-    announce("f32_4096 default entry point")
-    got = run(inp, torch).cpu().numpy()
-    assert "regtile" in rt.last_kernel()
-    assert_parity_sampled(inp, got, "f32_4096")
+# The full-size workloads through the entry point and launch configuration the benchmark
+# times, compared with the oracle over all of C. The exact kernel is asserted, so a change of
+# the default dispatch cannot leave the timed kernel untested. Cases of one workload are
+# adjacent, so its oracle is computed once.
+BENCH_KERNELS = [
+    ("f32_4096", rt.ALGO_F32_AUTO, "f32_regtile_128x256x16_8x16_va_vb_vc"),
+    ("f32_tall", rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x128x8_8x16"),
+    ("f32_8192", rt.ALGO_F32_AUTO, "f32_regtile_128x256x16_8x16_va_vb_vc"),
+    ("bf16_8192", rt.ALGO_BF16_AUTO, "bf16_mfma32x32x16_dma_256x256x64_w2x2"),
+    ("bf16_8192", rt.ALGO_BF16_MFMA_16X16, "bf16_mfma16x16x32_dma_256x256x64_w2x2"),
+    ("f16_8192", rt.ALGO_BF16_AUTO, "f16_mfma32x32x16_dma_256x256x64_w2x2"),
+    ("f16_8192", rt.ALGO_BF16_MFMA_16X16, "f16_mfma16x16x32_dma_256x256x64_w2x2"),
+]
 
 
-def test_f32_8192_sampled():
-    inp = gi.workload_inputs(gi.WORKLOADS["f32_8192"])
-    announce("f32_8192 default entry point")
-    got = run(inp, torch).cpu().numpy()
-    assert rt.last_kernel().startswith("f32_regtile_128x256x16_8x16"), rt.last_kernel()
-    assert_parity_sampled(inp, got, "f32_8192")
-
-
-def test_f32_tall_sampled():
-    inp = gi.workload_inputs(gi.WORKLOADS["f32_tall"])
-    announce("f32_tall default entry point")
-    got = run(inp, torch).cpu().numpy()
-    # 128 tiles of 128x128 and a long K: the split-K kernel (64x64 tiles, 8x8 micro-tiles)
-    assert "splitk" in rt.last_kernel(), rt.last_kernel()
-    assert_parity_sampled(inp, got, "f32_tall")
-
-
-@pytest.mark.parametrize("algo", [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16])
-def test_bf16_8192_sampled(algo):
-    inp = gi.workload_inputs(gi.WORKLOADS["bf16_8192"])
-    announce(f"bf16_8192 algo={algo}")
+@pytest.mark.parametrize("wname,algo,kernel", BENCH_KERNELS, ids=[f"{w}-{a}" for w, a, _ in BENCH_KERNELS])
+def test_workload_full(wname, algo, kernel):
+    inp, ref, mag = workload_reference(wname)
+    announce(f"{wname} algo={algo} full comparison")
     got = run(inp, torch, algo).cpu().numpy()
-    shape = "16x16x32" if algo == rt.ALGO_BF16_MFMA_16X16 else "32x32x16"
-    assert f"mfma{shape}_dma" in rt.last_kernel()
-    assert_parity_sampled(inp, got, f"bf16_8192 ({rt.last_kernel()})", n_random=30000)
+    assert rt.last_kernel() == kernel, rt.last_kernel()
+    ok, worst = oracle.check(got, ref, mag)
+    assert ok, f"{wname} ({kernel}): worst |err|/bound = {worst:.3g} over all {got.size} entries"
+
+
+def test_f32_ragged_default_kernel():
+    inp = gi.workload_inputs(gi.WORKLOADS["f32_ragged"])
+    announce("f32_ragged default entry point")
+    got = run(inp, torch).cpu().numpy()
+    assert rt.last_kernel() == "f32_regtile_splitk8_64x128x8_8x16_guard", rt.last_kernel()
+    assert_parity_full(inp, got, "f32_ragged default")
+
+
+def _integer_inputs(wname, seed):
+    """A workload's shape and layout with integer entries in [-16, 16]: every product and
+    partial sum is an integer below 2^24 in magnitude (K <= 8192), so any summation order is
+    exact in fp32 and the result must equal the oracle bitwise."""
+    w = gi.WORKLOADS[wname]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = rng.integers(-16, 17, (w.M, w.K)).astype(np.float32)
+    if w.dtype == "f32":
+        return gi.GemmInputs(w.M, w.N, w.K, 1.0, 0.0, "f32", False, A, rng.integers(-16, 17, (w.K, w.N)).astype(np.float32), None)
+    to_bits = gi.f32_to_bf16_bits if w.dtype == "bf16" else gi.f32_to_f16_bits
+    Bt = rng.integers(-16, 17, (w.N, w.K)).astype(np.float32)
+    return gi.GemmInputs(w.M, w.N, w.K, 1.0, 0.0, w.dtype, True, to_bits(A.ravel()).reshape(w.M, w.K),
+                         to_bits(Bt.ravel()).reshape(w.N, w.K), None)
+
+
+@pytest.mark.parametrize("wname,kernel", [("f32_4096", "f32_regtile_128x256x16_8x16_va_vb_vc"),
+                                          ("bf16_8192", "bf16_mfma32x32x16_dma_256x256x64_w2x2")])
+def test_workload_integer_inputs_bitwise_full(wname, kernel):
+    inp = _integer_inputs(wname, 4242)
+    announce(f"{wname} integer inputs, full bitwise comparison")
+    got = run(inp, torch).cpu().numpy()
+    assert rt.last_kernel() == kernel, rt.last_kernel()
+    ref, _ = oracle.gemm_inputs(inp)
+    assert np.array_equal(got.astype(np.float64), ref)
 
 
 # ---- bf16 at a size the oracle finishes in full -----------------------------------------
@@ -192,7 +217,7 @@ def test_16bit_dma_kernel_on_ragged_m_n(dtype, shape, alpha, beta, mode):
     if mode == "full":
         assert_parity_full(inp, got, f"{dtype} {shape} ({name})")
     else:
-        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})", n_random=30000)
+        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})")
 
 
 # K ending inside the last 64-deep slab (K a multiple of 8): that slab's chunks past K load as
@@ -214,7 +239,7 @@ def test_16bit_dma_kernel_k_tail(dtype, algo, shape):
     if M * N * K <= 5_000_000_000:
         assert_parity_full(inp, got, f"{dtype} {shape} ({name})")
     else:
-        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})", n_random=30000)
+        assert_parity_sampled(inp, got, f"{dtype} {shape} ({name})")
 
 
 def test_16bit_dma_kernel_k_tail_integer_bitwise():
@@ -227,7 +252,7 @@ def test_16bit_dma_kernel_k_tail_integer_bitwise():
     announce("bf16 DMA K tail integer bitwise")
     got = run(inp, torch).cpu().numpy()
     assert rt.last_kernel().endswith("_ktail"), rt.last_kernel()
-    I, J = sample_positions(M, N, n_random=50000, seed=3)
+    I, J = sample_positions(M, N, seed=3)
     ref, _ = oracle.gemm_inputs_entries(inp, I, J)
     assert np.array_equal(got[I, J].astype(np.float64), ref)
 
@@ -269,7 +294,7 @@ def test_bf16_full_tile_integer_inputs_are_bitwise_exact(algo):
     announce(f"bf16 full-tile integer bitwise algo={algo}")
     got = run(inp, torch, algo).cpu().numpy()
     assert "_dma_" in rt.last_kernel()
-    I, J = sample_positions(M, N, n_random=50000, seed=3)
+    I, J = sample_positions(M, N, seed=3)
     ref, _ = oracle.gemm_inputs_entries(inp, I, J)
     assert np.array_equal(got[I, J].astype(np.float64), ref)
 
@@ -292,16 +317,6 @@ def test_closed_forms_on_gpu():
 
 # ---- fp16 operands (the pages' half-precision GEMM) on the same MFMA kernels -----------------
 F16_ALGOS = [rt.ALGO_BF16_NAIVE, rt.ALGO_BF16_MFMA, rt.ALGO_BF16_MFMA_16X16, rt.ALGO_BF16_AUTO]
-
-
-@pytest.mark.parametrize("algo", [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16])
-def test_f16_8192_sampled(algo):
-    inp = gi.workload_inputs(gi.WORKLOADS["f16_8192"])
-    announce(f"f16_8192 algo={algo}")
-    got = run(inp, torch, algo).cpu().numpy()
-    shape = "16x16x32" if algo == rt.ALGO_BF16_MFMA_16X16 else "32x32x16"
-    assert f"f16_mfma{shape}_dma" in rt.last_kernel()
-    assert_parity_sampled(inp, got, f"f16_8192 ({rt.last_kernel()})", n_random=30000)
 
 
 @pytest.mark.parametrize("algo", F16_ALGOS)
@@ -337,7 +352,7 @@ def test_f16_integer_inputs_are_bitwise_exact(M, N, K):
     inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "f16", True, A, Bt, None)
     announce(f"f16 integer bitwise {M}x{N}x{K}")
     got = run(inp, torch, rt.ALGO_BF16_MFMA).cpu().numpy()
-    I, J = sample_positions(M, N, n_random=50000, seed=4)
+    I, J = sample_positions(M, N, seed=4)
     ref, _ = oracle.gemm_inputs_entries(inp, I, J)
     assert np.array_equal(got[I, J].astype(np.float64), ref)
 
