@@ -149,9 +149,12 @@ int regtile_gemm_f16_algo(int algo, int M, int N, int K, float alpha, const uint
  * Every layout runs on the register-tiled kernels (fp32) or the MFMA kernels (16-bit). The
  * 16-bit LDS-DMA kernel takes (0, 1) whenever K is a multiple of 8 and rows are 16-byte
  * aligned; (0, 0) / (1, 1) when in addition the M- or N-contiguous operand's rows are 8-byte
- * aligned (that operand staged through registers); and (1, 0) with 16-byte aligned rows (both
- * operands in their own storage, transposing LDS reads). Other problems gather M- or
- * N-contiguous operands into K-contiguous LDS slabs with 8-byte loads.
+ * aligned and its leading dimension and column count (N for (0, 0), M for (1, 1)) are
+ * multiples of 4 (that operand staged through registers); and (1, 0) with 16-byte aligned
+ * rows and M, N, lda and ldb multiples of 8 (both operands in their own storage, transposing
+ * LDS reads). Other problems gather M- or N-contiguous operands into K-contiguous LDS slabs
+ * with 8-byte loads. No kernel reads or writes outside the caller's matrices: every access
+ * stays within the first to last element of A, B and C.
  */
 int regtile_gemm_f32_ex(int algo, int trans_a, int trans_b, int M, int N, int K, float alpha,
                         const float *A, int lda, const float *B, int ldb, float beta, float *C,
@@ -166,6 +169,31 @@ int regtile_gemm_f16_ex(int algo, int trans_a, int trans_b, int M, int N, int K,
 /* Name of the kernel the calling thread launched last ("none" before the first launch,
  * "quick-return" when nothing was launched). Static storage; do not free. */
 const char *regtile_last_kernel(void);
+
+/*
+ * regtile_last_kernel_info -- resources of the kernel the calling thread launched last, as the
+ * HIP runtime reports them from its code object (the budget the pages weigh: registers per
+ * thread against resident waves, "寄存器Tiling跨架构解析" sections 2.4 and 7.2):
+ *   workgroup_size     threads per workgroup;
+ *   registers          vector registers per lane (hipFuncAttributes::numRegs);
+ *   lds_bytes          static LDS per workgroup;
+ *   scratch_bytes      private (spill) memory per lane, 0 when nothing spills;
+ *   workgroups_per_cu  resident workgroups per compute unit
+ *                      (hipOccupancyMaxActiveBlocksPerMultiprocessor);
+ *   waves_per_simd     workgroups_per_cu * workgroup_size / 64 / 4 (4 SIMDs per CU).
+ * `info` (arg 1) is caller-owned host memory; -1 if NULL. Returns REGTILE_OK, or a
+ * hipError_t (> 0) from the queries; hipErrorInvalidDeviceFunction when this thread has
+ * launched no kernel yet (the fields are then 0). Makes no launch and no allocation.
+ */
+typedef struct regtile_kernel_info {
+    int workgroup_size;
+    int registers;
+    int lds_bytes;
+    int scratch_bytes;
+    int workgroups_per_cu;
+    int waves_per_simd;
+} regtile_kernel_info;
+int regtile_last_kernel_info(regtile_kernel_info *info);
 
 /* Human-readable text for a status code returned by the entry points. Static storage. */
 const char *regtile_strerror(int status);

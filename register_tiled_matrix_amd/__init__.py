@@ -18,7 +18,8 @@ Entry points (same names as the C ABI):
   float16 A and B (IEEE binary16); the algorithm values are the bf16 ones.
 * ``gemm_f32_raw`` / ``gemm_bf16_raw`` / ``gemm_f16_raw`` take the C arguments verbatim
   (integers for pointers).
-* ``last_kernel()``, ``strerror(status)``, ``version()``.
+* ``last_kernel()``, ``last_kernel_info()`` (registers, LDS, scratch and occupancy of that
+  kernel, from the HIP runtime), ``strerror(status)``, ``version()``.
 
 The library must be built (``python -m register_tiled_matrix_amd.build``); importing this
 package does not build it, and every call raises ``RegtileLibraryMissing`` when it is absent.
@@ -37,7 +38,7 @@ __all__ = [
     "gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_raw", "gemm_bf16_raw", "gemm_f16_raw",
     "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
     "regtile_gemm_f32_ex", "regtile_gemm_bf16_ex", "regtile_gemm_f16_ex",
-    "last_kernel", "strerror", "version", "EXPORTED_SYMBOLS",
+    "last_kernel", "last_kernel_info", "strerror", "version", "EXPORTED_SYMBOLS",
 ]
 
 ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE, ALGO_F32_SPLITK = 0, 1, 2, 3, 4
@@ -47,12 +48,20 @@ ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA, ALGO_BF16_MFMA_16X16 = 0, 1, 2,
 EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "gemm_f16", "regtile_gemm_f32_algo",
                     "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo", "regtile_gemm_f32_ex",
                     "regtile_gemm_bf16_ex", "regtile_gemm_f16_ex",
-                    "regtile_last_kernel", "regtile_strerror", "regtile_version")
+                    "regtile_last_kernel", "regtile_last_kernel_info", "regtile_strerror",
+                    "regtile_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libregtile.so")
 _lib = None
 _lock = threading.Lock()
+
+
+class KernelInfo(ctypes.Structure):
+    """regtile_kernel_info of include/regtile.h."""
+    _fields_ = [("workgroup_size", ctypes.c_int), ("registers", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("scratch_bytes", ctypes.c_int), ("workgroups_per_cu", ctypes.c_int),
+                ("waves_per_simd", ctypes.c_int)]
 
 
 class RegtileError(RuntimeError):
@@ -93,6 +102,8 @@ def load():
             f.restype = I
         lib.regtile_last_kernel.argtypes = []
         lib.regtile_last_kernel.restype = ctypes.c_char_p
+        lib.regtile_last_kernel_info.argtypes = [ctypes.POINTER(KernelInfo)]
+        lib.regtile_last_kernel_info.restype = I
         lib.regtile_strerror.argtypes = [I]
         lib.regtile_strerror.restype = ctypes.c_char_p
         lib.regtile_version.argtypes = []
@@ -103,6 +114,13 @@ def load():
 
 def last_kernel() -> str:
     return load().regtile_last_kernel().decode()
+
+
+def last_kernel_info() -> dict:
+    """Resources of the kernel this thread launched last (regtile_last_kernel_info)."""
+    info = KernelInfo()
+    _check(load().regtile_last_kernel_info(ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in KernelInfo._fields_}
 
 
 def strerror(status: int) -> str:

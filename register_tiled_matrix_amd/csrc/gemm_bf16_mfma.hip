@@ -305,6 +305,8 @@ template <int BM, int BN, int WM, int WN, bool EDGE, bool VEC, bool F16, bool A_
           bool B_MN = false>
 hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    note_launch(reinterpret_cast<const void *>(&bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16, A_MN, B_MN>),
+                WM * WN * 64);
     hipLaunchKernelGGL((bf16_mfma_kernel<BM, BN, WM, WN, EDGE, VEC, false, F16, A_MN, B_MN>),
                        dim3(tiles_m * tiles_n), dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha,
                        (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C,

@@ -605,6 +605,9 @@ template <int BM, int BN, int BK, int WM, int WN, int MF, int WINDOWS, int STAGG
           int ROWS = 0, bool KTAIL = false, int MN = 0>
 hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    note_launch(reinterpret_cast<const void *>(
+                    &bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS, KTAIL, MN>),
+                WM * WN * 64);
     hipLaunchKernelGGL((bf16_mfma_dma_kernel<BM, BN, BK, WM, WN, MF, WINDOWS, STAGGER, F16, RING, ROWS, KTAIL, MN>), dim3(tiles_m * tiles_n),
                        dim3(WM * WN * 64), 0, s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A,
                        p.lda, (const uint16_t *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);

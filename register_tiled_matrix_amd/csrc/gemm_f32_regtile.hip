@@ -316,6 +316,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
 
 template <class CFG, bool TA, bool TB, bool EDGE, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tiles_m, int tiles_n) {
+    note_launch(reinterpret_cast<const void *>(&f32_regtile_kernel<CFG, TA, TB, EDGE, VA, VB, VC>), NT);
     hipLaunchKernelGGL((f32_regtile_kernel<CFG, TA, TB, EDGE, VA, VB, VC>), dim3(tiles_m * tiles_n),
                        dim3(NT), 0, s, p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda,
                        (const float *)p.B, p.ldb, p.beta, p.C, p.ldc, tiles_m, tiles_n);

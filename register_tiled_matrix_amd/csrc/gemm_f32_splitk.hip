@@ -266,6 +266,7 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 template <class CFG, bool G, bool VA, bool VB, bool VC>
 hipError_t launch_variant(const Problem &p, hipStream_t s, int tm, int tn, int spw) {
+    note_launch(reinterpret_cast<const void *>(&f32_splitk_kernel<CFG, G, VA, VB, VC>), CFG::NT);
     hipLaunchKernelGGL((f32_splitk_kernel<CFG, G, VA, VB, VC>), dim3(tm * tn), dim3(CFG::NT), 0, s,
                        p.M, p.N, p.K, p.alpha, (const float *)p.A, p.lda, (const float *)p.B,
                        p.ldb, p.beta, p.C, p.ldc, tm, tn, spw);

@@ -28,6 +28,7 @@ hipError_t launch_scale_c(const Problem &p, hipStream_t s, const char **name) {
     const int64_t total = (int64_t)p.M * p.N;
     const int64_t blocks = (total + 255) / 256;
     const int grid = (int)(blocks < 65536 ? blocks : 65536);
+    note_launch(reinterpret_cast<const void *>(&scale_c_kernel), 256);
     hipLaunchKernelGGL(scale_c_kernel, dim3(grid), dim3(256), 0, s, p.M, p.N, p.beta, p.C, p.ldc);
     *name = "scale_c";
     return hipGetLastError();
@@ -82,6 +83,11 @@ hipError_t launch_naive(const Problem &p, hipStream_t s) {
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const T *A = (const T *)p.A, *B = (const T *)p.B;
+    note_launch(p.ta ? (p.tb ? reinterpret_cast<const void *>(&naive_kernel<T, true, true>)
+                             : reinterpret_cast<const void *>(&naive_kernel<T, true, false>))
+                     : (p.tb ? reinterpret_cast<const void *>(&naive_kernel<T, false, true>)
+                             : reinterpret_cast<const void *>(&naive_kernel<T, false, false>)),
+                256);
     if (p.ta && p.tb)
         hipLaunchKernelGGL((naive_kernel<T, true, true>), grid, dim3(256), 0, s, p.M, p.N, p.K,
                            p.alpha, A, p.lda, B, p.ldb, p.beta, p.C, p.ldc, col_blocks);
@@ -149,6 +155,7 @@ hipError_t launch_f32_lds(const Problem &p, hipStream_t s, const char **name) {
     const int col_blocks = (p.N + LDS_TILE - 1) / LDS_TILE;
     const int64_t blocks = (int64_t)col_blocks * ((p.M + LDS_TILE - 1) / LDS_TILE);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    note_launch(reinterpret_cast<const void *>(&f32_lds_kernel), LDS_TILE * LDS_TILE);
     hipLaunchKernelGGL(f32_lds_kernel, dim3((unsigned)blocks), dim3(LDS_TILE * LDS_TILE), 0, s, p.M,
                        p.N, p.K, p.alpha, (const float *)p.A, p.lda, (const float *)p.B, p.ldb,
                        p.beta, p.C, p.ldc, col_blocks);

@@ -10,6 +10,8 @@
 namespace {
 
 thread_local const char *g_last_kernel = "none";
+thread_local const void *g_last_fn = nullptr;  // the kernel behind g_last_kernel, if one ran
+thread_local unsigned g_last_threads = 0;
 
 // LAPACK-style validation. `shift` counts the arguments before M (1 for the *_algo entry
 // points, 3 for the *_ex ones), so the returned -i always names the position in the called
@@ -61,6 +63,7 @@ regtile::Problem make_problem(int M, int N, int K, float alpha, const void *A, i
 bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
     if (p.M == 0 || p.N == 0) {
         g_last_kernel = "quick-return";
+        g_last_fn = nullptr;
         *status = REGTILE_OK;
         return true;
     }
@@ -144,6 +147,13 @@ int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K
 
 }  // namespace
 
+namespace regtile {
+void note_launch(const void *kernel, unsigned threads) {
+    g_last_fn = kernel;
+    g_last_threads = threads;
+}
+}  // namespace regtile
+
 extern "C" {
 
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -207,6 +217,25 @@ int regtile_gemm_f16_ex(int algo, int trans_a, int trans_b, int M, int N, int K,
 }
 
 const char *regtile_last_kernel(void) { return g_last_kernel; }
+
+int regtile_last_kernel_info(regtile_kernel_info *info) {
+    if (info == nullptr) return -1;
+    *info = regtile_kernel_info{};
+    if (g_last_fn == nullptr) return (int)hipErrorInvalidDeviceFunction;
+    hipFuncAttributes a;
+    hipError_t e = hipFuncGetAttributes(&a, g_last_fn);
+    if (e != hipSuccess) return (int)e;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, g_last_fn, (int)g_last_threads, 0);
+    if (e != hipSuccess) return (int)e;
+    info->workgroup_size = (int)g_last_threads;
+    info->registers = a.numRegs;
+    info->lds_bytes = (int)a.sharedSizeBytes;
+    info->scratch_bytes = (int)a.localSizeBytes;
+    info->workgroups_per_cu = per_cu;
+    info->waves_per_simd = per_cu * (int)((g_last_threads + 63) / 64) / 4;
+    return REGTILE_OK;
+}
 
 const char *regtile_strerror(int status) {
     if (status == REGTILE_OK) return "success";

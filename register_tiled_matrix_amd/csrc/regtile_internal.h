@@ -23,6 +23,10 @@ struct Problem {
     bool ta = false, tb = false;
 };
 
+// Every launch records the kernel it starts and its workgroup size just before launching it
+// (regtile_last_kernel_info queries that kernel's resources).
+void note_launch(const void *kernel, unsigned threads);
+
 // A launch reports the kernel it chose through `name` (static storage).
 hipError_t launch_scale_c(const Problem &p, hipStream_t s, const char **name);
 hipError_t launch_f32_naive(const Problem &p, hipStream_t s, const char **name);

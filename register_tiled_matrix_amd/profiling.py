@@ -296,6 +296,25 @@ def summarize_ladder_sq(prof, out_md):
                   f"{1000 * lds / valu if valu else 0:.1f} | {conf} |")
     with open(out_md, "w") as f:
         f.write("\n".join(md) + "\n")
+    # the same means as JSON, for the counter-invariant test (tests/test_counter_invariants.py):
+    # fp32 kernels ran on f32_4096, 16-bit kernels on bf16_8192
+    rec = {"about": "rocprofv3 --pmc means per dispatch over the ladder run named in `command`; fp32 "
+                    "kernels at 4096^3, 16-bit kernels at 8192^3 (bf16 operands)",
+           "command": cmd[0], "kernels": {}}
+    for k, m in sorted(per.items(), key=lambda kv: _short_kernel(kv[0])):
+        if "regtile" not in k:
+            continue
+        waves = m.get("SQ_WAVES", 0) or 1
+        rec["kernels"][_short_kernel(k)] = {
+            "workload": "bf16_8192" if ("bf16" in k or "unsigned short" in k) else "f32_4096",
+            "waves": m.get("SQ_WAVES", 0),
+            "lds_instructions_per_wave": m.get("SQ_INSTS_LDS", 0) / waves,
+            "valu_instructions_per_wave": m.get("SQ_INSTS_VALU", 0) / waves,
+            "mfma_instructions_per_wave": m.get("SQ_INSTS_MFMA", 0) / waves,
+            "lds_bank_conflict_cycles": m.get("SQ_LDS_BANK_CONFLICT", 0),
+            "lds_active_cycles": m.get("SQ_LDS_IDX_ACTIVE", 0)}
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
 
 
 def summarize(prof) -> int:

@@ -12,8 +12,6 @@ ladder (algorithm 2).
     python -m register_tiled_matrix_amd.tune run  > sweep.jsonl   # GPU: time every variant
     python -m register_tiled_matrix_amd.tune report sweep.jsonl  # markdown summary
     python -m register_tiled_matrix_amd.tune ladder > ladder.jsonl   # GPU: every rung, every config
-    python -m register_tiled_matrix_amd.tune probe --build none   # CPU: build the gfx950 probes
-    python -m register_tiled_matrix_amd.tune probe valu           # GPU: FMA issue rate, VGPR banks
     python -m register_tiled_matrix_amd.tune datadep              # GPU: bf16 rate against input data
     python -m register_tiled_matrix_amd.tune shapes               # GPU: fp32 / bf16 on more shapes
 
@@ -439,31 +437,6 @@ def cmd_report(args) -> int:
     return 0
 
 
-PROBE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "gfx950_probe.hip")
-PROBE_BIN = os.path.join(_build.BUILD_DIR, "probes", "gfx950_probe")
-
-
-def build_probe() -> None:
-    """Compile the gfx950 probe program with the library's flags (raises on failure)."""
-    os.makedirs(os.path.dirname(PROBE_BIN), exist_ok=True)
-    flags = [f for f in _build.COMMON_FLAGS if f != "-fPIC"]
-    res = subprocess.run([_build._hipcc(), *flags, PROBE_SRC, "-o", PROBE_BIN],
-                         capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"probe build failed:\n{res.stderr}")
-    print(f"# built {PROBE_BIN}", file=sys.stderr)
-
-
-def cmd_probe(args) -> int:
-    """Build (on the CPU, with the library's flags) and/or run the gfx950 probe program."""
-    if args.build or not os.path.exists(PROBE_BIN):
-        build_probe()
-    if args.what == "none":
-        return 0
-    sys.stdout.flush()
-    return subprocess.run([PROBE_BIN, args.what]).returncode
-
-
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -481,10 +454,6 @@ def main(argv=None) -> int:
     lad.add_argument("--workloads", default="f32_256,f32_4096,f32_ragged,f32_tall,bf16_8192,f16_8192")
     lad.add_argument("--steps", type=int, default=30)
     lad.add_argument("--warmup", type=int, default=50)
-    pr = sub.add_parser("probe", help="gfx950 facts: FP32 FMA issue rate and VGPR banks, "
-                                       "MFMA rate, LDS access patterns")
-    pr.add_argument("what", nargs="?", default="all", choices=["all", "valu", "valu_sustained", "mfma", "mfma_sustained", "lds", "lds_tr", "none"])
-    pr.add_argument("--build", action="store_true", help="recompile the probe program first")
     sh = sub.add_parser("shapes", help="fp32 and bf16 default entry points on more shapes")
     sh.add_argument("--steps", type=int, default=20)
     sh.add_argument("--warmup", type=int, default=40)
@@ -501,7 +470,7 @@ def main(argv=None) -> int:
         sys.path.insert(0, root)
     t0 = time.time()
     rc = {"build": cmd_build, "run": cmd_run, "ladder": cmd_ladder, "report": cmd_report,
-          "probe": cmd_probe, "datadep": cmd_datadep, "shapes": cmd_shapes}[args.cmd](args)
+          "datadep": cmd_datadep, "shapes": cmd_shapes}[args.cmd](args)
     print(f"# {args.cmd} done in {time.time() - t0:.1f} s", file=sys.stderr)
     return rc
 
