@@ -24,7 +24,6 @@ import argparse
 import hashlib
 import json
 import os
-import platform
 import sys
 import time
 
@@ -118,10 +117,20 @@ def _steady_median(torch, step):
     return float(np.median(kern))
 
 
-def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
+def _kernel_info(rt):
+    """Resources of the kernel launched last, as the HIP runtime reports them."""
+    try:
+        return rt.last_kernel_info()
+    except rt.RegtileError:
+        return None
+
+
+def _configs(torch, gi, rt, acc, dev, stream, with_16bit, with_cpu):
     """Every configuration through the default entry points: at least 50 warm-up launches and
     100 ms, then 30 timed launches; TFLOP/s from the median event time, and the fraction of the
-    peak that bounds it."""
+    peak that bounds it. Then one more launch from the original C, compared in full with the
+    fp64 oracle (max |err| / bound), and with `with_cpu` the oracle's and the blocked CPU GEMM's
+    times on the same workload."""
     res = {}
     names = ["f32_256", "f32_4096", "f32_ragged", "f32_tall", "f32_8192"] + (["bf16_8192"] if with_16bit else [])
     for wname in names:
@@ -147,12 +156,56 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit):
 
         step()
         kname = rt.last_kernel()
+        info = _kernel_info(rt)
         med = _steady_median(torch, step)
         tf = wc.flop / (med * 1e-3) / 1e12
         res[wname] = {"shape": [wc.M, wc.N, wc.K], "kernel": kname, "kernel_ms_median": round(med, 4),
-                      "TFLOP/s": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4)}
+                      "TFLOP/s": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4),
+                      "kernel_resources": info}
+        if with_cpu and wname != "f32_8192":  # the five configurations; 8192^3 fp32 is extra
+            if ic.C is not None:
+                C.copy_(torch.from_numpy(ic.C).to(dev))
+            step()
+            torch.cuda.synchronize()
+            res[wname].update(_cpu_and_check(ic, C.cpu().numpy()))
         del A, B, C
     return res
+
+
+def _cpu_and_check(inp, got):
+    """The fp64 oracle on the whole workload (timed: the oracle CPU baseline), the GPU result's
+    worst |err| / bound against it, and the blocked fp32 CPU GEMM on the same workload (16-bit
+    operands widened to fp32 first, outside its timing)."""
+    import cpu_baseline
+    import gemm_inputs as gi
+    import oracle
+
+    t0 = time.perf_counter()
+    ref, mag = oracle.gemm_inputs(inp)
+    t_oracle = time.perf_counter() - t0
+    ok, worst = oracle.check(got, ref, mag)
+    del ref, mag
+    if inp.dtype == "f32":
+        A32, B32 = inp.A, inp.B
+    else:
+        def widen(bits):
+            if inp.dtype == "bf16":
+                return gi.bf16_bits_to_f32(bits)
+            return np.ascontiguousarray(bits).view(np.float16).astype(np.float32)
+
+        A32 = widen(inp.A)
+        B32 = np.ascontiguousarray(widen(inp.B).T)  # N x K storage of column-major B -> K x N
+    t0 = time.perf_counter()
+    cpu_baseline.sgemm(A32, B32)
+    t_blocked = time.perf_counter() - t0
+    flop = 2.0 * inp.M * inp.N * inp.K
+    return {"err_over_bound": round(worst, 4), "parity_ok": bool(ok),
+            "cpu_oracle": {"seconds": round(t_oracle, 3), "TFLOP/s": round(flop / t_oracle / 1e12, 5),
+                           "cores": oracle.num_threads(), "sample": "whole workload"},
+            "cpu_blocked": {"seconds": round(t_blocked, 3), "TFLOP/s": round(flop / t_blocked / 1e12, 4),
+                            "cores": cpu_baseline.num_threads(),
+                            "sample": "whole workload" + ("" if inp.dtype == "f32" else
+                                                          f", {inp.dtype} operands widened to fp32")}}
 
 
 def _sources_digest(files):
@@ -210,7 +263,7 @@ def _cpu_baseline(inp, target_s):
             "sample": f"rows 0..{rows - 1} of the {inp.M}x{inp.N}x{inp.K} fp32 workload "
                       f"({rows}x{inp.N}x{inp.K} fp64 multiply-adds, {dt:.1f} s)",
             "seconds": dt,
-            "host_cpu": platform.processor() or _cpu_model(),
+            "host_cpu": _cpu_model(),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
@@ -276,7 +329,8 @@ def _only(args, torch, gi, rt, dev):
             raise rt.RegtileError(st, rt.strerror(st))
 
     wms, kms, kmin = _time(torch, step, args.steps, args.warmup)
-    print(json.dumps({"only": args.only, "kernel": rt.last_kernel(), "kernel_ms_mean": kms,
+    print(json.dumps({"only": args.only, "kernel": rt.last_kernel(), "kernel_resources": _kernel_info(rt),
+                      "kernel_ms_mean": kms,
                       "kernel_ms_min": kmin, "TFLOP/s": w.flop / (kms * 1e-3) / 1e12}),
           flush=True)
     return 0
@@ -320,6 +374,7 @@ def main():
 
     step_f32()
     kernel_name = rt.last_kernel()
+    kernel_info = _kernel_info(rt)
     torch.cuda.synchronize()
     wall_ms, region_ms, kern_ms, kern_min = _time_steps(torch, step_f32, args.steps, args.warmup)
     flop = w.flop
@@ -349,6 +404,9 @@ def main():
             "peak": acc.PEAK_FP32_VECTOR_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / acc.PEAK_FP32_VECTOR_TFLOPS, 4),
+            "frac_basis": "achieved = flop per launch / mean per-launch HIP event duration on the launch stream",
+            "achieved_wall": round(value, 3),
+            "frac_wall": round(value / acc.PEAK_FP32_VECTOR_TFLOPS, 4),
             "traffic": _traffic(kernel_name),
             "algorithmic_hbm_bytes": work.hbm_bytes,
             "kernel": kernel_name,
@@ -356,6 +414,7 @@ def main():
             "kernel_ms_min": round(kern_min, 4),
             "flop_per_launch": flop,
             "back_to_back_ms_per_launch": round(region_ms, 4),
+            "kernel_resources": kernel_info,
         },
     }
 
@@ -376,6 +435,7 @@ def main():
 
         step_16()
         kname = rt.last_kernel()
+        kinfo = _kernel_info(rt)
         wms, rms, kms, kmin = _time_steps(torch, step_16, args.steps, args.warmup)
         v = wb.flop / (wms * 1e-3) / 1e12
         a = wb.flop / (kms * 1e-3) / 1e12
@@ -386,6 +446,9 @@ def main():
             "percent_of_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
             "roofline": {"bound": "mfma", "achieved": round(a, 2), "peak": acc.PEAK_BF16_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(a / acc.PEAK_BF16_MFMA_TFLOPS, 4),
+                         "frac_basis": "achieved = flop per launch / mean per-launch HIP event duration",
+                         "achieved_wall": round(v, 2), "frac_wall": round(v / acc.PEAK_BF16_MFMA_TFLOPS, 4),
+                         "kernel_resources": kinfo,
                          "traffic": _traffic(kname),
                          "algorithmic_hbm_bytes": acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes,
                          "kernel": kname, "kernel_ms_mean": round(kms, 4),
@@ -476,7 +539,7 @@ def main():
         out["ladder"] = ladder
 
     # ---- every configuration, median of 30 launches ------------------------------------------
-    out["configs"] = _configs(torch, gi, rt, acc, dev, stream, not args.no_bf16)
+    out["configs"] = _configs(torch, gi, rt, acc, dev, stream, not args.no_bf16, not args.no_cpu)
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------
     if not args.no_cpu:

@@ -7,7 +7,8 @@
 this process never touches the GPU), one pass at a time, each under its own time limit, and
 stops at the first pass that fails. The passes:
 
-  trace      --kernel-trace --stats over `bench.py --no-cpu` (per-kernel durations);
+  trace_*    --kernel-trace --stats over `bench.py --only <workload>`, one workload per run
+             (per-dispatch durations of that workload's kernel alone);
   pmc_*      FETCH_SIZE, then WRITE_SIZE, one counter per run, over `bench.py --only <workload>`
              for the fp32 4096^3, bf16 8192^3 and fp32 16384x128x4096 kernels and for a plain
              1 GiB device copy (the calibration: bytes moved / counter bytes);
@@ -50,6 +51,9 @@ KERNELS = {
                  ["gemm_f32_splitk.hip", "regtile_internal.h"], (16384 * 4096 + 4096 * 128 + 16384 * 128) * 4),
 }
 PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "copy"]
+# one kernel trace per workload, so that each summary's statistics are that workload's alone
+TRACE_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged"]
+TRACE_STEPS, TRACE_WARMUP = 200, 50
 SQ_WORKLOADS = ["f32_4096", "bf16_8192"]
 
 
@@ -59,8 +63,10 @@ def _bench_cmd(*extra):
 
 def passes(out):
     """(name, rocprofv3 argv, seconds allowed) for every pass, in order."""
-    p = [("trace", ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out, "trace"), "-o", "trace",
-                    "--output-format", "csv", "--", *_bench_cmd("--no-cpu", "--steps", "20", "--warmup", "50")], 420)]
+    p = [(f"trace_{w}", ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out, f"trace_{w}"), "-o",
+                         "trace", "--output-format", "csv", "--",
+                         *_bench_cmd("--only", w, "--steps", str(TRACE_STEPS), "--warmup", str(TRACE_WARMUP))], 300)
+         for w in TRACE_WORKLOADS]
     for w in PMC_WORKLOADS:
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             p.append((f"pmc_{c}_{w}", ["rocprofv3", "--pmc", c, "-d", os.path.join(out, f"pmc_{c}_{w}"), "-o", "pmc",
@@ -166,42 +172,49 @@ def _resource_rows(trace_csv):
     return out
 
 
-def summarize_trace(prof, out_md):
-    with open(os.path.join(prof, "trace", "trace_kernel_stats.csv")) as f:
-        rows = list(csv.DictReader(f))
-    lines = ["# Kernel trace: fp32 4096^3 and bf16 8192^3 bench run (rocprofv3 --kernel-trace --stats)", ""]
-    lines += _cmd_block([_display(passes(prof)[0][1], prof)])
+def summarize_trace(prof, workload, out_md):
+    """Kernel trace of `bench.py --only <workload>`: the workload's kernel, its statistics over
+    every dispatch (warm-up included) and over the timed launches alone (the last TRACE_STEPS),
+    the roofline fraction each gives, and the same run's HIP-event mean."""
+    d = os.path.join(prof, f"trace_{workload}")
+    with open(os.path.join(d, "trace_kernel_stats.csv")) as f:
+        rows = [r for r in csv.DictReader(f) if "regtile::" in r["Name"]]
     durs = collections.defaultdict(list)
-    with open(os.path.join(prof, "trace", "trace_kernel_trace.csv")) as f:
-        for r in csv.DictReader(f):
-            durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    med = {k: statistics.median(v) for k, v in durs.items()}
-    lines += ["The average includes the warm-up launches and the first launches after idle gaps, which run "
-              "at a lower clock; the median is over the same dispatches.", "",
-              "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
-              "|---|---|---|---|---|---|---|"]
-    for r in rows:
-        m = med.get(r["Name"])
-        lines.append(f"| `{r['Name'][:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{'-' if m is None else f'{m:.1f}'} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} % |")
-    lines += _resource_rows(os.path.join(prof, "trace", "trace_kernel_trace.csv"))
-    bench_line = None
-    with open(os.path.join(prof, "trace.out")) as f:
+    with open(os.path.join(d, "trace_kernel_trace.csv")) as f:
+        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    for r in recs:
+        durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    only = None
+    with open(os.path.join(prof, f"trace_{workload}.out")) as f:
         for line in f:
-            if line.startswith("{") and '"metric"' in line:
-                bench_line = json.loads(line)
-    if bench_line:
-        lines += ["", "The same run's bench line (HIP events around each launch on the launch stream):", ""]
-        def agree(label, r, sub):
-            m = [v for k, v in med.items() if sub in k]
-            tail = f"; trace median {m[0]:.1f} us ({(r['kernel_ms_mean'] * 1e3 / m[0] - 1) * 100:+.1f}%)" if m else ""
-            lines.append(f"- {label} `{r['kernel']}`: event mean {r['kernel_ms_mean'] * 1e3:.1f} us, "
-                         f"achieved {r['achieved']} TFLOP/s{tail}")
+            if line.startswith("{") and '"only"' in line:
+                only = json.loads(line)
+    import gemm_inputs as gi
+    from . import accounting as acc
 
-        agree("fp32 4096^3", bench_line["roofline"], KERNELS["f32_4096"][1] + ", false, false, false")
-        if "bf16_8192" in bench_line:
-            agree("bf16 8192^3", bench_line["bf16_8192"]["roofline"], KERNELS["bf16_8192"][1] + ", 1, 1, false, 5, 0, false, 0>")
+    w = gi.WORKLOADS[workload]
+    peak = acc.PEAK_FP32_VECTOR_TFLOPS if w.dtype == "f32" else acc.PEAK_BF16_MFMA_TFLOPS
+    argv = [a for n, a, _ in passes(prof) if n == f"trace_{workload}"][0]
+    lines = [f"# Kernel trace: {workload} ({w.description}), rocprofv3 --kernel-trace --stats", ""]
+    lines += _cmd_block([_display(argv, prof)])
+    lines += [f"The run makes {TRACE_WARMUP} warm-up launches, then {TRACE_STEPS} timed launches, each with a HIP "
+              f"event pair (the bench's per-launch timing). Algorithmic work {w.flop:.4g} flop per launch; "
+              f"peak {peak} TFLOP/s.", "",
+              "| kernel | calls | average (us) | min (us) | max (us) | timed launches: mean (us) | median (us) | "
+              "TFLOP/s (timed mean) | frac |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        ds = durs.get(r["Name"], [])
+        timed = ds[-TRACE_STEPS:]
+        mean_t = statistics.mean(timed) if timed else float("nan")
+        tf = w.flop / (mean_t * 1e-6) / 1e12 if timed else float("nan")
+        lines.append(f"| `{_short_kernel(r['Name'])[:140]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {mean_t:.1f} | "
+                     f"{statistics.median(timed) if timed else float('nan'):.1f} | {tf:.1f} | {tf / peak:.4f} |")
+    if only:
+        lines += ["", f"The same run's HIP-event mean over the timed launches: {only['kernel_ms_mean'] * 1e3:.1f} us "
+                      f"({only['TFLOP/s']:.1f} TFLOP/s, frac {only['TFLOP/s'] / peak:.4f}); kernel `{only['kernel']}`; "
+                      f"resources {json.dumps(only.get('kernel_resources'))}."]
+    lines += _resource_rows(os.path.join(d, "trace_kernel_trace.csv"))
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -319,10 +332,14 @@ def summarize_ladder_sq(prof, out_md):
 
 def summarize(prof) -> int:
     prof = os.path.abspath(prof)
-    summarize_trace(prof, os.path.join(PROFILES, "kernel_trace_f32_4096_bf16_8192.md"))
-    summarize_traffic(prof, os.path.join(PROFILES, "pmc_traffic.json"),
-                      os.path.join(PROFILES, "hbm_traffic_f32_4096_bf16_8192.md"))
-    summarize_sq(prof, os.path.join(PROFILES, "sq_counters_f32_4096_bf16_8192.md"))
+    for w in TRACE_WORKLOADS:
+        if os.path.exists(os.path.join(prof, f"trace_{w}", "trace_kernel_stats.csv")):
+            summarize_trace(prof, w, os.path.join(PROFILES, f"kernel_trace_{w}.md"))
+    if os.path.exists(os.path.join(prof, "pmc_FETCH_SIZE_copy")):
+        summarize_traffic(prof, os.path.join(PROFILES, "pmc_traffic.json"),
+                          os.path.join(PROFILES, "hbm_traffic_f32_4096_bf16_8192.md"))
+    if os.path.exists(os.path.join(prof, "sq_f32_4096")):
+        summarize_sq(prof, os.path.join(PROFILES, "sq_counters_f32_4096_bf16_8192.md"))
     if os.path.exists(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv")):
         summarize_ladder_sq(prof, os.path.join(PROFILES, "lds_counters_ladder_f32_4096_bf16_8192.md"))
     return 0
