@@ -6,11 +6,13 @@
 // tile over its own share of K, with the register micro-tile of the square kernel
 // ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA / regB per
 // k, TM x TN FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
-// tile size against the number of resident waves). Two shapes:
+// tile size against the number of resident waves). Three shapes:
 //   * 64x64 tile, 4 waves, 8x8 micro-tiles, BK 16 (splitk4);
 //   * 64x128 tile, 8 waves, 8x16 micro-tiles (the square kernel's), BK 8 (splitk8): one
 //     workgroup of two waves per SIMD per CU, and three quarters of the LDS reads per FMA of
-//     8x8.
+//     8x8;
+//   * 64x96 tile, 8 waves, 8x12 micro-tiles, BK 8: the same with three column groups, for
+//     shapes whose 64x128 tiles fill only part of a round of 256 workgroups.
 // The partial tiles are summed through LDS in a fixed order, so results are deterministic;
 // the summation order differs from the square kernel's single k sweep.
 //
@@ -28,16 +30,25 @@ namespace {
 
 constexpr int APAD = 4;
 
-template <int NW_, int TM_, int TN_, int BK_>
+#ifndef SPLIT96_DEPTH
+#define SPLIT96_DEPTH 1
+#endif
+
+template <int NW_, int TM_, int TN_, int BK_, int DEPTH_ = 1>
 struct SplitCfg {
-    static constexpr int NW = NW_, TM = TM_, TN = TN_, BK = BK_;
+    // DEPTH: slabs of global loads in flight ahead of the slab being computed (1 or 2; 2 holds
+    // a second set of staging registers)
+    static constexpr int NW = NW_, TM = TM_, TN = TN_, BK = BK_, DEPTH = DEPTH_;
+    static_assert(DEPTH == 1 || DEPTH == 2, "one or two slabs of loads in flight");
     static constexpr int NT = NW * 64;
     static constexpr int TILE_M = 8 * TM, TILE_N = 8 * TN;  // 8 x 8 lanes per wave
     static constexpr int AS = TILE_M + APAD;                // A slab row stride (floats), k-major
     static constexpr int NA4 = TILE_M * BK / 256;           // A float4 per lane per slab
     static constexpr int NB4 = BK * TILE_N / 256;           // B float4 per lane per slab
     static constexpr int NPART = NW < 4 ? NW : 4;           // partial tiles held in LDS at once
-    static_assert(TM == 8 && (TN == 8 || TN == 16), "micro-tile rows in two groups of 4");
+    static constexpr int SW = TILE_M * TILE_N / NT;         // epilogue columns per thread
+    static_assert(TM == 8 && (TN == 8 || TN == 12 || TN == 16), "micro-tile rows in two groups of 4");
+    static_assert(SW % 4 == 0 && TILE_N % SW == 0, "whole float4 strips in the epilogue");
     static_assert(NW == 4 || NW == 8, "four waves, or eight summed pairwise first");
     static_assert(NA4 >= 1 && NB4 >= 1 && TILE_M * BK % 256 == 0 && BK * TILE_N % 256 == 0,
                   "whole float4 per lane");
@@ -54,6 +65,7 @@ struct SplitCfg {
 };
 using Split4 = SplitCfg<4, 8, 8, 16>;
 using Split8 = SplitCfg<8, 8, 16, 8>;
+using Split8n96 = SplitCfg<8, 8, 12, 8, SPLIT96_DEPTH>;  // 64x96 tiles: 1000 x 1500 is 256 of them
 
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ float4 load4(const float *__restrict__ p, bool row_ok, int cols_left) {
@@ -94,44 +106,82 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int m0 = tm * TILE_M, n0 = tn * TILE_N;
     const int kb = wave * slabs_per_wave * BK;  // this wave's k range [kb, ke)
     const int ke = min(K, kb + slabs_per_wave * BK);
+    // This wave's own slab count: only slabs that reach into [kb, ke) (the last waves of a K
+    // that does not fill NW equal ranges run fewer; the loop has no workgroup barrier).
+    const int spw_w = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
     // Staging: float4 q of the A slab (TILE_M rows x BK k) is row q / AQ, k (q % AQ) * 4;
-    // float4 q of the B slab (BK k x TILE_N columns) is k q / BQ, column (q % BQ) * 4.
-    float4 ra[NA4], rb[NB4];
-    auto load_slab = [&](int k0) {
+    // float4 q of the B slab (BK k x TILE_N columns) is k q / BQ, column (q % BQ) * 4. With
+    // DEPTH 2 a second register set (ra2, rb2) holds the slab after next.
+    //
+    // Edges: an A row past M reads row M - 1 instead, and a B column chunk wholly past N reads
+    // the tile's first chunk instead; both only feed outputs that are never stored, so they
+    // need no zeros. What must be zero is every k at or past ke (other waves' k, or past K),
+    // and the columns past N of a chunk that straddles N (its real columns are kept). A slab
+    // wholly inside [kb, ke) with no straddling chunk in the wave therefore takes plain vector
+    // loads; only the others take the element-checked loads.
+    const float *a_src[NA4];
+    const float *b_src[NB4];
+    int b_cols_left[NB4];
+    bool straddle = false;
 #pragma unroll
-        for (int i = 0; i < NA4; ++i) {
-            const int q = lane + 64 * i;
-            const int ar = q / AQ, ak = (q % AQ) * 4;
-            ra[i] = load4<GUARD, VEC_A>(A + (int64_t)(m0 + ar) * lda + k0 + ak, m0 + ar < M,
-                                        ke - (k0 + ak));
-        }
+    for (int i = 0; i < NA4; ++i) {
+        const int q = lane + 64 * i;
+        const int ar = q / AQ, ak = (q % AQ) * 4;
+        const int row = GUARD ? min(m0 + ar, M - 1) : m0 + ar;
+        a_src[i] = A + (int64_t)row * lda + ak;
+    }
 #pragma unroll
-        for (int i = 0; i < NB4; ++i) {
-            const int q = lane + 64 * i;
-            const int bk = q / BQ, bc = (q % BQ) * 4;
-            rb[i] = load4<GUARD, VEC_B>(B + (int64_t)(k0 + bk) * ldb + n0 + bc, k0 + bk < ke,
-                                        N - (n0 + bc));
+    for (int i = 0; i < NB4; ++i) {
+        const int q = lane + 64 * i;
+        const int bk = q / BQ, bc = (q % BQ) * 4;
+        const int col = GUARD && n0 + bc >= N ? n0 : n0 + bc;
+        b_src[i] = B + (int64_t)bk * ldb + col;
+        b_cols_left[i] = N - col;
+        straddle |= GUARD && N - col < 4;
+    }
+    // (wave-uniform: one vote for the whole kernel)
+    const bool any_straddle = GUARD && __any(straddle);
+    float4 ra[NA4], rb[NB4], ra2[NA4], rb2[NB4];
+    auto load_into = [&](int k0, float4 (&xa)[NA4], float4 (&xb)[NB4]) {
+        if (!GUARD || (!any_straddle && k0 + BK <= ke)) {
+#pragma unroll
+            for (int i = 0; i < NA4; ++i) xa[i] = load4<false, VEC_A>(a_src[i] + k0, true, 4);
+#pragma unroll
+            for (int i = 0; i < NB4; ++i) xb[i] = load4<false, VEC_B>(b_src[i] + (int64_t)k0 * ldb, true, 4);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NA4; ++i) {
+                const int ak = ((lane + 64 * i) % AQ) * 4;
+                xa[i] = load4<true, VEC_A>(a_src[i] + k0, true, ke - (k0 + ak));
+            }
+#pragma unroll
+            for (int i = 0; i < NB4; ++i) {
+                const int bk = (lane + 64 * i) / BQ;
+                xb[i] = load4<true, VEC_B>(b_src[i] + (int64_t)k0 * ldb, k0 + bk < ke, b_cols_left[i]);
+            }
         }
     };
-    auto store_slab = [&](int buf) {
+    auto load_slab = [&](int k0) { load_into(k0, ra, rb); };
+    auto store_from = [&](int buf, const float4 (&xa)[NA4], const float4 (&xb)[NB4]) {
         auto &w = sm.st[wave][buf];
 #pragma unroll
         for (int i = 0; i < NA4; ++i) {
             const int q = lane + 64 * i;
             const int ar = q / AQ, ak = (q % AQ) * 4;
-            w.a[ak + 0][ar] = ra[i].x;
-            w.a[ak + 1][ar] = ra[i].y;
-            w.a[ak + 2][ar] = ra[i].z;
-            w.a[ak + 3][ar] = ra[i].w;
+            w.a[ak + 0][ar] = xa[i].x;
+            w.a[ak + 1][ar] = xa[i].y;
+            w.a[ak + 2][ar] = xa[i].z;
+            w.a[ak + 3][ar] = xa[i].w;
         }
 #pragma unroll
         for (int i = 0; i < NB4; ++i) {
             const int q = lane + 64 * i;
             const int bk = q / BQ, bc = (q % BQ) * 4;
-            *reinterpret_cast<float4 *>(&w.b[bk][bc]) = rb[i];
+            *reinterpret_cast<float4 *>(&w.b[bk][bc]) = xb[i];
         }
     };
+    auto store_slab = [&](int buf) { store_from(buf, ra, rb); };
 
     float acc[TM][TN];
 #pragma unroll
@@ -176,17 +226,71 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
     };
 
-    // Every wave runs the same number of slabs; a wave whose range is shorter loads zeros
-    // past ke (GUARD).
-    if (slabs_per_wave > 0) {
-        load_slab(kb);
-        store_slab(0);
-        for (int s = 0; s + 1 < slabs_per_wave; ++s) {
-            load_slab(kb + (s + 1) * BK);
-            compute_slab(s & 1);
-            store_slab((s + 1) & 1);
+    // Each wave runs the slabs of its own range; the last of them may reach past ke (loads
+    // past ke are zeros).
+    const int spw = spw_w;
+    if constexpr (CFG::DEPTH == 1) {
+        if (spw > 0) {
+            load_slab(kb);
+            store_slab(0);
+            for (int s = 0; s + 1 < spw; ++s) {
+                load_slab(kb + (s + 1) * BK);
+                compute_slab(s & 1);
+                store_slab((s + 1) & 1);
+            }
+            compute_slab((spw - 1) & 1);
         }
-        compute_slab((slabs_per_wave - 1) & 1);
+    } else {
+        // Two register sets, two LDS buffers. Slab t's loads go out while slab t - 2 is
+        // computed and reach LDS after slab t - 1 has been: two slabs of latency covered.
+        // Set (ra, rb) carries the even slabs and buffer 0, set (ra2, rb2) the odd slabs and
+        // buffer 1; the loop body is one pair of slabs so both sets stay in fixed registers.
+        if (spw > 0) {
+            load_into(kb, ra, rb);
+            if (spw > 1) load_into(kb + BK, ra2, rb2);
+            store_from(0, ra, rb);
+            int s = 0;
+            for (; s + 2 < spw; s += 2) {
+                // slab s (even): buffer 0; slab s + 1 waits in (ra2, rb2)
+                load_into(kb + (s + 2) * BK, ra, rb);
+                compute_slab(0);
+                store_from(1, ra2, rb2);
+                // slab s + 1 (odd): buffer 1; slab s + 2 waits in (ra, rb)
+                if (s + 3 < spw) load_into(kb + (s + 3) * BK, ra2, rb2);
+                compute_slab(1);
+                store_from(0, ra, rb);
+            }
+            // the last one or two slabs: s even, s + 1 < spw iff a slab waits in (ra2, rb2)
+            compute_slab(0);
+            if (s + 1 < spw) {
+                store_from(1, ra2, rb2);
+                compute_slab(1);
+            }
+        }
+    }
+    // The epilogue's strip of C (beta != 0) is read now, so its latency overlaps the reduction
+    // below rather than following it: thread t owns row t / (TILE_N / SW), columns
+    // (t % (TILE_N / SW)) * SW .. +SW-1 (SW = 16, or 12 for 96-column tiles).
+    constexpr int SW = CFG::SW, TPR = TILE_N / SW;  // strip width, threads per row
+    static_assert(NT == TILE_M * TPR, "one strip per thread");
+    const int row = tid / TPR, col0 = (tid % TPR) * SW;
+    const int grow = m0 + row;
+    float4 cold[SW / 4];
+    if (beta != 0.0f && (!GUARD || grow < M)) {
+        const float *crow_in = C + (int64_t)grow * ldc + n0 + col0;
+#pragma unroll
+        for (int c4 = 0; c4 < SW / 4; ++c4) {
+            const int gcol = n0 + col0 + c4 * 4;
+            if (VEC_C && (!GUARD || gcol + 3 < N)) {
+                cold[c4] = *reinterpret_cast<const float4 *>(crow_in + c4 * 4);
+            } else {
+                float e[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (!GUARD || gcol + u < N) e[u] = crow_in[c4 * 4 + u];
+                cold[c4] = make_float4(e[0], e[1], e[2], e[3]);
+            }
+        }
     }
     __syncthreads();  // all waves are done with their stages: the union turns into partials
 
@@ -223,16 +327,11 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (wave < NPART) write_part(wave);
     __syncthreads();
 
-    // Fixed-order sum of the NPART partials and epilogue: thread t owns row t / (TILE_N / 16),
-    // columns (t % (TILE_N / 16)) * 16 .. +15.
-    constexpr int TPR = TILE_N / 16;  // threads per row
-    static_assert(NT == TILE_M * TPR, "one 16-column strip per thread");
-    const int row = tid / TPR, col0 = (tid % TPR) * 16;
-    const int grow = m0 + row;
+    // Fixed-order sum of the NPART partials and epilogue on the strip read above.
     if (GUARD && grow >= M) return;
     float *crow = C + (int64_t)grow * ldc;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
+    for (int c4 = 0; c4 < SW / 4; ++c4) {
         const int col = col0 + c4 * 4;
         float4 s = *reinterpret_cast<const float4 *>(&sm.part[0][row][col]);
 #pragma unroll
@@ -245,21 +344,21 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         const int gcol = n0 + col;
         float *c = crow + gcol;
+        float4 v;
+        if (beta == 0.0f) {  // C is never read
+            v = make_float4(alpha * s.x, alpha * s.y, alpha * s.z, alpha * s.w);
+        } else {
+            const float4 old = cold[c4];
+            v = make_float4(fmaf(alpha, s.x, beta * old.x), fmaf(alpha, s.y, beta * old.y),
+                            fmaf(alpha, s.z, beta * old.z), fmaf(alpha, s.w, beta * old.w));
+        }
         if (VEC_C && (!GUARD || gcol + 3 < N)) {
-            float4 v;
-            if (beta == 0.0f) {
-                v = make_float4(alpha * s.x, alpha * s.y, alpha * s.z, alpha * s.w);
-            } else {
-                const float4 old = *reinterpret_cast<const float4 *>(c);
-                v = make_float4(fmaf(alpha, s.x, beta * old.x), fmaf(alpha, s.y, beta * old.y),
-                                fmaf(alpha, s.z, beta * old.z), fmaf(alpha, s.w, beta * old.w));
-            }
             *reinterpret_cast<float4 *>(c) = v;
         } else {
-            const float sv[4] = {s.x, s.y, s.z, s.w};
+            const float sv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (!GUARD || gcol + e < N) c[e] = epilogue_value(sv[e], alpha, beta, c + e);
+                if (!GUARD || gcol + e < N) c[e] = sv[e];
         }
     }
 }
@@ -304,6 +403,15 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name, const 
 
 }  // namespace
 
+// The 8-wave kernel runs one workgroup per CU, so the tile count in rounds of 256 workgroups
+// times the tile's area estimates its time. 64x96 tiles (8x12 micro-tiles) win where they fill
+// a round that 64x128 tiles leave partly idle (1000 x 1500: 256 tiles against 192).
+static bool split8_prefers_96(int M, int N) {
+    const int64_t tm64 = (M + 63) / 64;
+    const int64_t t128 = tm64 * ((N + 127) / 128), t96 = tm64 * ((N + 95) / 96);
+    return ((t96 + 255) / 256) * 96 < ((t128 + 255) / 256) * 128;
+}
+
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name) {
     // 8 waves x 8x16 once 64x128 tiles give most CUs a workgroup (two waves per SIMD), unless
     // the 4-wave kernel's 64x64 tiles already fill the chip and K is short enough that the
@@ -311,9 +419,13 @@ hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name)
     // 64 <= K <= 8192; the 8-wave kernel lost at 16384 x 128 x 1024 and won at x 4096).
     const int64_t tm64 = (p.M + 63) / 64;
     const int64_t t128 = tm64 * ((p.N + 127) / 128), t64 = tm64 * ((p.N + 63) / 64);
-    if (t128 >= 192 && (p.K >= 1280 || t64 < 448))
+    if (t128 >= 192 && (p.K >= 1280 || t64 < 448)) {
+        if (split8_prefers_96(p.M, p.N))
+            return launch_cfg<Split8n96>(p, s, name, "f32_regtile_splitk8_64x96x8_8x12",
+                                         "f32_regtile_splitk8_64x96x8_8x12_guard");
         return launch_cfg<Split8>(p, s, name, "f32_regtile_splitk8_64x128x8_8x16",
                                   "f32_regtile_splitk8_64x128x8_8x16_guard");
+    }
     return launch_cfg<Split4>(p, s, name, "f32_regtile_splitk4_64x64x16_8x8",
                               "f32_regtile_splitk4_64x64x16_8x8_guard");
 }

@@ -81,7 +81,8 @@ def test_f32_ragged_default_kernel():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_ragged"])
     announce("f32_ragged default entry point")
     got = run(inp, torch).cpu().numpy()
-    assert rt.last_kernel() == "f32_regtile_splitk8_64x128x8_8x16_guard", rt.last_kernel()
+    # 1000 x 1500 is 256 tiles of 64x96 (one per CU) against 192 of 64x128
+    assert rt.last_kernel() == "f32_regtile_splitk8_64x96x8_8x12_guard", rt.last_kernel()
     assert_parity_full(inp, got, "f32_ragged default")
 
 
@@ -141,22 +142,25 @@ def test_f32_regtile_edges(shape, algo):
     assert_parity_full(inp, got, f"f32 edges {shape} ({rt.last_kernel()})")
 
 
-# Split-K shapes with at least 192 tiles of 64x128, which take the 8-wave 64x128 kernel:
-# ragged M, N and K; K below the 8 waves x 8 of one slab each (waves past K add zeros);
-# N below one tile; exact multiples (no bounds checks).
-SPLITK8_SHAPES = [(13000, 50, 37), (12289, 130, 1283), (8192, 256, 1300), (12800, 128, 1536),
-                  (12352, 1, 7)]
+# Split-K shapes with at least 192 tiles of 64x128, which take an 8-wave kernel: 64x128 tiles
+# of 8x16 micro-tiles, or 64x96 tiles of 8x12 where those need fewer rounds of 256 workgroups
+# times tile area. Ragged M, N and K; K below the 8 waves x 8 of one slab each (waves past K
+# add zeros); N below one tile; exact multiples (no bounds checks).
+SPLITK8_SHAPES = [(13000, 50, 37, 96), (12289, 130, 1283, 96), (8192, 256, 1300, 128),
+                  (12800, 128, 1536, 128), (12352, 1, 7, 96), (16384, 96, 2048, 96), (1000, 1500, 777, 96),
+                  (12288, 192, 2048, 96)]
 
 
-@pytest.mark.parametrize("shape", SPLITK8_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK8_SHAPES])
+@pytest.mark.parametrize("shape", SPLITK8_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k, _ in SPLITK8_SHAPES])
 def test_f32_splitk8_edges(shape):
-    M, N, K = shape
+    M, N, K, tile_n = shape
     inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=-1.25, beta=0.75, seed=M + N + K)
     announce(f"f32 split-K 8 waves {shape}")
     got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
     name = rt.last_kernel()
-    assert name.startswith("f32_regtile_splitk8_64x128x8_8x16"), name
-    assert name.endswith("_guard") == (M % 64 != 0 or N % 128 != 0 or K % 64 != 0), name
+    micro = {128: "8x16", 96: "8x12"}[tile_n]
+    assert name.startswith(f"f32_regtile_splitk8_64x{tile_n}x8_{micro}"), name
+    assert name.endswith("_guard") == (M % 64 != 0 or N % tile_n != 0 or K % 64 != 0), name
     assert_parity_full(inp, got, f"f32 split-K {shape} ({name})")
 
 
