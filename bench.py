@@ -104,9 +104,11 @@ def _time_steps(torch, fn, steps, warmup):
     return wall_ms, region_ms, float(np.mean(kern)), float(np.min(kern))
 
 
-def _steady_median(torch, step):
+def _steady_median(torch, step, with_region=False):
     """Median kernel time (ms) of 30 event-timed launches after warming up for at least 50
-    launches and 100 ms (small problems ramp the clock slowly)."""
+    launches and 100 ms (small problems ramp the clock slowly). With `with_region`, also the
+    time per launch of 30 back-to-back launches inside one event pair (for kernels of tens of
+    microseconds the per-launch event pair adds a few microseconds of its own)."""
     t_end, n = time.perf_counter() + 0.1, 0
     while n < 50 or time.perf_counter() < t_end:
         step()
@@ -114,7 +116,15 @@ def _steady_median(torch, step):
         if n % 50 == 0:
             torch.cuda.synchronize()
     _, kern = _kernel_times(torch, step, 30, 0)
-    return float(np.median(kern))
+    if not with_region:
+        return float(np.median(kern))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(30):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return float(np.median(kern)), e0.elapsed_time(e1) / 30
 
 
 def _kernel_info(rt):
@@ -157,10 +167,14 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit, with_cpu):
         step()
         kname = rt.last_kernel()
         info = _kernel_info(rt)
-        med = _steady_median(torch, step)
+        med, region = _steady_median(torch, step, with_region=True)
         tf = wc.flop / (med * 1e-3) / 1e12
+        tf_b2b = wc.flop / (region * 1e-3) / 1e12
         res[wname] = {"shape": [wc.M, wc.N, wc.K], "kernel": kname, "kernel_ms_median": round(med, 4),
                       "TFLOP/s": round(tf, 3), "peak": peak, "frac": round(tf / peak, 4),
+                      "basis": "median of 30 launches, each timed by its own HIP event pair",
+                      "back_to_back_ms_per_launch": round(region, 4),
+                      "TFLOP/s_back_to_back": round(tf_b2b, 3), "frac_back_to_back": round(tf_b2b / peak, 4),
                       "kernel_resources": info}
         if with_cpu and wname != "f32_8192":  # the five configurations; 8192^3 fp32 is extra
             if ic.C is not None:
