@@ -305,7 +305,9 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
     };
     if constexpr (NW == 8) {
-        // waves 4..7 hand their partials to waves 0..3, which add them (acc_w + acc_{w+4})
+        // waves 4..7 hand their partials to waves 0..3, which add them (acc_w + acc_{w+4}) and
+        // write the sum back into the same slot: slot w is touched only by waves w + 4 (before
+        // the barrier) and w (after it), so no second barrier is needed before that write
         if (wave >= 4) write_part(wave - 4);
         __syncthreads();
         if (wave < 4) {
@@ -321,10 +323,11 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     acc[m][4 * g + 3] += p.w;
                 }
             }
+            write_part(wave);
         }
-        __syncthreads();
+    } else {
+        write_part(wave);
     }
-    if (wave < NPART) write_part(wave);
     __syncthreads();
 
     // Fixed-order sum of the NPART partials and epilogue on the strip read above.
