@@ -175,7 +175,7 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit, with_cpu):
                       "basis": "median of 30 launches, each timed by its own HIP event pair",
                       "back_to_back_ms_per_launch": round(region, 4),
                       "TFLOP/s_back_to_back": round(tf_b2b, 3), "frac_back_to_back": round(tf_b2b / peak, 4),
-                      "kernel_resources": info}
+                      "kernel_resources": info, "counters": _sq_record(kname), "traffic": _traffic(kname)}
         if with_cpu and wname != "f32_8192":  # the five configurations; 8192^3 fp32 is extra
             if ic.C is not None:
                 C.copy_(torch.from_numpy(ic.C).to(dev))
@@ -250,6 +250,21 @@ def _traffic(kernel_name):
     except (OSError, KeyError):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _sq_record(kernel_name):
+    """LDS bank-conflict rate and wave-state shares of `kernel_name` from the committed
+    rocprofv3 --pmc summary (profiles/sq_counters_bench_kernels.json), or None when absent or
+    when the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "sq_counters_bench_kernels.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get("kernels", {}).get(kernel_name)
+        if not rec or rec.get("sources_digest") != _sources_digest(rec["sources"]):
+            return None
+    except (OSError, ValueError, KeyError):
+        return None
+    return {k: rec[k] for k in ("lds_bank_conflict_rate", "valu_active_share", "waiting_share") if k in rec}
 
 
 def _cpu_baseline(inp, target_s):
@@ -429,6 +444,7 @@ def main():
             "flop_per_launch": flop,
             "back_to_back_ms_per_launch": round(region_ms, 4),
             "kernel_resources": kernel_info,
+            "counters": _sq_record(kernel_name),
         },
     }
 
@@ -462,7 +478,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(a / acc.PEAK_BF16_MFMA_TFLOPS, 4),
                          "frac_basis": "achieved = flop per launch / mean per-launch HIP event duration",
                          "achieved_wall": round(v, 2), "frac_wall": round(v / acc.PEAK_BF16_MFMA_TFLOPS, 4),
-                         "kernel_resources": kinfo,
+                         "kernel_resources": kinfo, "counters": _sq_record(kname),
                          "traffic": _traffic(kname),
                          "algorithmic_hbm_bytes": acc.GemmWork(wb.M, wb.N, wb.K, 2).hbm_bytes,
                          "kernel": kname, "kernel_ms_mean": round(kms, 4),

@@ -12,7 +12,8 @@ stops at the first pass that fails. The passes:
   pmc_*      FETCH_SIZE, then WRITE_SIZE, one counter per run, over `bench.py --only <workload>`
              for the fp32 4096^3, bf16 8192^3 and fp32 16384x128x4096 kernels and for a plain
              1 GiB device copy (the calibration: bytes moved / counter bytes);
-  sq_*       LDS, VALU and MFMA instruction and cycle counters per kernel.
+  sq_*       LDS, VALU and MFMA instruction and cycle counters per kernel;
+  state_*    where the waves' time goes (VALU / LDS / VMEM issue, waiting) per kernel.
 
 `summarize` turns the CSV files into the short tables under profiles/ and writes
 profiles/pmc_traffic.json, from which bench.py reports `roofline.traffic` (HBM bytes per
@@ -37,6 +38,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_MFMA "
                "SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES")
 LADDER_COUNTERS = "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAVES"
+# where the waves' time goes: issuing VALU / LDS / VMEM instructions, or waiting (any counter or
+# barrier), against the waves' lifetime
+STATE_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM "
+                  "SQ_WAVES")
 COPY_BYTES = 1 << 30
 
 # workload -> (kernel label as regtile_last_kernel() names it, substring of the kernel's symbol,
@@ -45,16 +50,19 @@ KERNELS = {
     "f32_4096": ("f32_regtile_128x256x16_8x16_va_vb_vc", "f32_regtile_kernel<regtile::(anonymous namespace)::SquareCfg",
                  ["gemm_f32_regtile.hip", "regtile_internal.h"], 3 * 4096 * 4096 * 4),
     "bf16_8192": ("bf16_mfma32x32x16_dma_256x256x64_w2x2", "bf16_mfma_dma_kernel<256, 256, 64, 2, 2, 32",
-                  ["gemm_bf16_mfma_dma.hip", "mfma_common.h", "regtile_internal.h"],
+                  ["gemm_bf16_mfma_dma.hip", "mfma_common.h", "tile_addressing.h", "regtile_internal.h"],
                   2 * 8192 * 8192 * 2 + 8192 * 8192 * 4),
-    "f32_tall": ("f32_regtile_splitk8_64x128x8_8x16", "SplitCfg<8, 8, 16, 8>, false",
+    "f32_tall": ("f32_regtile_splitk8_64x128x8_8x16", "SplitCfg<8, 8, 16, 8, 1>, false",
                  ["gemm_f32_splitk.hip", "regtile_internal.h"], (16384 * 4096 + 4096 * 128 + 16384 * 128) * 4),
+    # beta != 0: C is read and written
+    "f32_ragged": ("f32_regtile_splitk8_64x96x8_8x12_guard", "SplitCfg<8, 8, 12, 8, 1>, true",
+                   ["gemm_f32_splitk.hip", "regtile_internal.h"], (1000 * 777 + 777 * 1500 + 2 * 1000 * 1500) * 4),
 }
-PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "copy"]
+PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged", "copy"]
 # one kernel trace per workload, so that each summary's statistics are that workload's alone
 TRACE_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged"]
 TRACE_STEPS, TRACE_WARMUP = 200, 50
-SQ_WORKLOADS = ["f32_4096", "bf16_8192"]
+SQ_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged"]
 
 
 def _bench_cmd(*extra):
@@ -76,6 +84,10 @@ def passes(out):
         p.append((f"sq_{w}", ["rocprofv3", "--pmc", *SQ_COUNTERS.split(), "-d", os.path.join(out, f"sq_{w}"), "-o", "sq",
                               "--output-format", "csv", "--",
                               *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    for w in SQ_WORKLOADS:
+        p.append((f"state_{w}", ["rocprofv3", "--pmc", *STATE_COUNTERS.split(), "-d", os.path.join(out, f"state_{w}"),
+                                 "-o", "st", "--output-format", "csv", "--",
+                                 *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
     p.append(("sq_ladder", ["rocprofv3", "--pmc", *LADDER_COUNTERS.split(), "-d", os.path.join(out, "sq_ladder"),
                             "-o", "sq", "--output-format", "csv", "--", "python3", "-m",
                             "register_tiled_matrix_amd.tune", "ladder", "--workloads", "f32_4096,bf16_8192",
@@ -251,30 +263,61 @@ def summarize_traffic(prof, out_json, out_md):
         f.write("\n".join(md) + "\n")
 
 
-def summarize_sq(prof, out_md):
-    cmds = [_display(a, prof) for n, a, _ in passes(prof) if n.startswith("sq_")]
-    md = ["# SQ counters: LDS instructions, bank conflicts, VALU/MFMA instructions", ""] + _cmd_block(cmds)
+def _kernel_means(path, sub):
+    d = _pmc(path)
+    vals = collections.defaultdict(list)
+    for (k, c), vs in d.items():
+        if sub in k:
+            vals[c].extend(vs)
+    return {c: sum(vs) / len(vs) for c, vs in vals.items()}
+
+
+def summarize_sq(prof, out_md, out_json):
+    """SQ instruction and LDS counters, and the wave-state split, per workload's kernel. The
+    JSON record (stamped with a digest of the kernel's sources) gives bench.py the LDS
+    bank-conflict rate and the VALU-active share of the kernel it times."""
+    cmds = [_display(a, prof) for n, a, _ in passes(prof) if n.startswith("sq_") or n.startswith("state_")]
+    md = ["# SQ counters: LDS instructions, bank conflicts, VALU/MFMA instructions, wave states", ""] + _cmd_block(cmds)
+    md += ["Means per dispatch. The wave-state shares divide by SQ_WAVE_CYCLES (the waves' summed lifetime): "
+           "`VALU-active` is SQ_ACTIVE_INST_VALU (cycles a wave spends issuing VALU instructions, MFMA "
+           "included), `waiting` SQ_WAIT_ANY (cycles waiting on a counter or the barrier).", ""]
+    rec = {"about": "SQ counter means per dispatch, one record per benchmarked kernel (rocprofv3 --pmc)",
+           "kernels": {}}
     for w in SQ_WORKLOADS:
-        label, sub = KERNELS[w][0], KERNELS[w][1]
-        d = _pmc(os.path.join(prof, f"sq_{w}", "sq_counter_collection.csv"))
-        vals = collections.defaultdict(list)
-        for (k, c), vs in d.items():
-            if sub in k:
-                vals[c].extend(vs)
-        m = {c: sum(vs) / len(vs) for c, vs in vals.items()}
-        md += [f"## {w} (`{label}`), mean per dispatch", ""]
+        label, sub, sources, _ = KERNELS[w]
+        m = _kernel_means(os.path.join(prof, f"sq_{w}", "sq_counter_collection.csv"), sub)
+        md += [f"## {w} (`{label}`)", ""]
         md += [f"- {c}: {m[c]:.0f}" for c in sorted(m)]
         waves = m.get("SQ_WAVES", 0)
+        entry = {"workload": w, "sources": sources, "sources_digest": _digest(sources)}
         if waves:
             md.append(f"- per wave: {m['SQ_INSTS_LDS'] / waves:.0f} LDS instructions, "
                       f"{m['SQ_INSTS_VALU'] / waves:.0f} VALU instructions, "
                       f"{m.get('SQ_INSTS_MFMA', 0) / waves:.0f} MFMA instructions")
         if m.get("SQ_LDS_IDX_ACTIVE"):
-            md.append(f"- bank-conflict rate SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = "
-                      f"{100 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.1f} %")
+            rate = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"]
+            entry["lds_bank_conflict_rate"] = round(rate, 4)
+            md.append(f"- bank-conflict rate SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = {100 * rate:.1f} %")
+        st_path = os.path.join(prof, f"state_{w}", "st_counter_collection.csv")
+        if os.path.exists(st_path):
+            st = _kernel_means(st_path, sub)
+            wc = st.get("SQ_WAVE_CYCLES", 0)
+            if wc:
+                shares = {k: st.get(c, 0) / wc for k, c in (("valu_active", "SQ_ACTIVE_INST_VALU"),
+                                                             ("lds_active", "SQ_ACTIVE_INST_LDS"),
+                                                             ("vmem_active", "SQ_ACTIVE_INST_VMEM"),
+                                                             ("waiting", "SQ_WAIT_ANY"))}
+                entry.update({f"{k}_share": round(v, 4) for k, v in shares.items()})
+                md.append(f"- wave states: VALU-active {100 * shares['valu_active']:.1f} %, LDS-issue "
+                          f"{100 * shares['lds_active']:.1f} %, VMEM-issue {100 * shares['vmem_active']:.1f} %, "
+                          f"waiting {100 * shares['waiting']:.1f} % of SQ_WAVE_CYCLES "
+                          f"({st.get('SQ_WAVES', 0):.0f} waves)")
+        rec["kernels"][label] = entry
         md.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(md) + "\n")
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
 
 
 def _short_kernel(name):
@@ -311,9 +354,11 @@ def summarize_ladder_sq(prof, out_md):
         f.write("\n".join(md) + "\n")
     # the same means as JSON, for the counter-invariant test (tests/test_counter_invariants.py):
     # fp32 kernels ran on f32_4096, 16-bit kernels on bf16_8192
+    srcs = ["gemm_simple.hip", "gemm_f32_regtile.hip", "gemm_f32_splitk.hip", "gemm_bf16_mfma.hip",
+            "gemm_bf16_mfma_dma.hip", "mfma_common.h", "tile_addressing.h", "regtile_internal.h"]
     rec = {"about": "rocprofv3 --pmc means per dispatch over the ladder run named in `command`; fp32 "
                     "kernels at 4096^3, 16-bit kernels at 8192^3 (bf16 operands)",
-           "command": cmd[0], "kernels": {}}
+           "command": cmd[0], "sources": srcs, "sources_digest": _digest(srcs), "kernels": {}}
     for k, m in sorted(per.items(), key=lambda kv: _short_kernel(kv[0])):
         if "regtile" not in k:
             continue
@@ -339,7 +384,8 @@ def summarize(prof) -> int:
         summarize_traffic(prof, os.path.join(PROFILES, "pmc_traffic.json"),
                           os.path.join(PROFILES, "hbm_traffic_f32_4096_bf16_8192.md"))
     if os.path.exists(os.path.join(prof, "sq_f32_4096")):
-        summarize_sq(prof, os.path.join(PROFILES, "sq_counters_f32_4096_bf16_8192.md"))
+        summarize_sq(prof, os.path.join(PROFILES, "sq_counters_bench_kernels.md"),
+                     os.path.join(PROFILES, "sq_counters_bench_kernels.json"))
     if os.path.exists(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv")):
         summarize_ladder_sq(prof, os.path.join(PROFILES, "lds_counters_ladder_f32_4096_bf16_8192.md"))
     return 0
