@@ -77,7 +77,7 @@ def test_split_k_8_waves(kernels):
     # and 8 x 128 of B), then the fixed-order reduction of the 64 x 128 partials (32 float4
     # per lane each): waves 4-7 write, waves 0-3 read; waves 0-3 write, all 8 waves read their
     # eighth of the four partials (16 float4 per lane)
-    r = _find(kernels, "f32_splitk_kernel<SplitCfg<8, 8, 16, 8>")
+    r = _find(kernels, "f32_splitk_kernel<SplitCfg<8, 8, 16, 8,")
     k_wave = K["f32_4096"] // 8
     per_slab = (8 // 4 + 16 // 4) * 8 + 2 * (64 * 8 // (4 * 64)) + 8 * 128 // (4 * 64)
     reduction = (4 * 32 + 4 * 32 + 4 * 32 + 8 * 16) / 8
