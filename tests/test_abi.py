@@ -107,6 +107,29 @@ def test_null_operands_allowed_when_not_read(lib):
     assert rt.last_kernel() == "quick-return"
 
 
+def test_kernel_info_without_a_launch_makes_no_hip_call(lib):
+    # NULL -> -1; on a thread that has launched nothing (or whose last call was a quick return)
+    # -> hipErrorInvalidDeviceFunction (98), both before any HIP call
+    import ctypes
+    import threading
+
+    assert lib.regtile_last_kernel_info(None) == -1
+    out = {}
+
+    def fresh_thread():
+        info = rt.KernelInfo()
+        out["fresh"] = lib.regtile_last_kernel_info(ctypes.byref(info))
+        rt.gemm_f32_raw(0, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, 0)  # quick return
+        out["after_quick_return"] = lib.regtile_last_kernel_info(ctypes.byref(info))
+        out["fields"] = [getattr(info, n) for n, _ in rt.KernelInfo._fields_]
+
+    t = threading.Thread(target=fresh_thread)
+    t.start()
+    t.join()
+    assert out["fresh"] == 98 and out["after_quick_return"] == 98
+    assert out["fields"] == [0] * 6
+
+
 def test_binding_rejects_host_tensors_and_bad_layouts(lib):
     import torch
     a = torch.zeros(4, 4)

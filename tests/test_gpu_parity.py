@@ -77,6 +77,25 @@ def test_workload_full(wname, algo, kernel):
     assert ok, f"{wname} ({kernel}): worst |err|/bound = {worst:.3g} over all {got.size} entries"
 
 
+# The benchmarked kernels' resources as the HIP runtime reports them: no spills, and the
+# occupancy each design states (two waves per SIMD for the fp32 kernels, whose FMA issue needs
+# two; one for the bf16 kernel, whose 256 accumulators per lane fill the AGPRs).
+BENCH_RESOURCES = [("f32_4096", 256, 2), ("f32_tall", 512, 2), ("f32_ragged", 512, 2), ("bf16_8192", 256, 1)]
+
+
+@pytest.mark.parametrize("wname,threads,waves", BENCH_RESOURCES, ids=[w for w, _, _ in BENCH_RESOURCES])
+def test_benchmarked_kernels_resources(wname, threads, waves):
+    w = gi.WORKLOADS[wname]
+    inp = gi.make_inputs(w.M, w.N, w.K, dtype=w.dtype, dist="normal", alpha=w.alpha, beta=w.beta, seed=1)
+    announce(f"{wname} kernel resources")
+    run(inp, torch)
+    info = rt.last_kernel_info()
+    assert info["scratch_bytes"] == 0, info
+    assert info["workgroup_size"] == threads, info
+    assert info["waves_per_simd"] == waves, info
+    assert info["registers"] <= 512 // waves, info
+
+
 def test_f32_ragged_default_kernel():
     inp = gi.workload_inputs(gi.WORKLOADS["f32_ragged"])
     announce("f32_ragged default entry point")
