@@ -29,12 +29,23 @@ namespace regtile {
 namespace {
 
 constexpr int APAD = 4;
+// 1: one LDS wait per k step in the split-K loop (the compiler otherwise waits fragment by
+// fragment); 0: the compiler's waits
+#ifndef SPLIT_ONE_WAIT
+#define SPLIT_ONE_WAIT 1
+#endif
+#ifndef SPLIT96_BK
+#define SPLIT96_BK 8
+#endif
+#ifndef SPLIT96_APAD
+#define SPLIT96_APAD 4
+#endif
 
 #ifndef SPLIT96_DEPTH
 #define SPLIT96_DEPTH 1
 #endif
 
-template <int NW_, int TM_, int TN_, int BK_, int DEPTH_ = 1>
+template <int NW_, int TM_, int TN_, int BK_, int DEPTH_ = 1, int PAD_ = APAD>
 struct SplitCfg {
     // DEPTH: slabs of global loads in flight ahead of the slab being computed (1 or 2; 2 holds
     // a second set of staging registers)
@@ -42,7 +53,7 @@ struct SplitCfg {
     static_assert(DEPTH == 1 || DEPTH == 2, "one or two slabs of loads in flight");
     static constexpr int NT = NW * 64;
     static constexpr int TILE_M = 8 * TM, TILE_N = 8 * TN;  // 8 x 8 lanes per wave
-    static constexpr int AS = TILE_M + APAD;                // A slab row stride (floats), k-major
+    static constexpr int AS = TILE_M + PAD_;                // A slab row stride (floats), k-major
     static constexpr int NA4 = TILE_M * BK / 256;           // A float4 per lane per slab
     static constexpr int NB4 = BK * TILE_N / 256;           // B float4 per lane per slab
     static constexpr int NPART = NW < 4 ? NW : 4;           // partial tiles held in LDS at once
@@ -65,7 +76,7 @@ struct SplitCfg {
 };
 using Split4 = SplitCfg<4, 8, 8, 16>;
 using Split8 = SplitCfg<8, 8, 16, 8>;
-using Split8n96 = SplitCfg<8, 8, 12, 8, SPLIT96_DEPTH>;  // 64x96 tiles: 1000 x 1500 is 256 of them
+using Split8n96 = SplitCfg<8, 8, 12, SPLIT96_BK, SPLIT96_DEPTH, SPLIT96_APAD>;  // 64x96 tiles: 1000 x 1500 is 256 of them
 
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ float4 load4(const float *__restrict__ p, bool row_ok, int cols_left) {
@@ -207,7 +218,13 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * TILE_N + 32 * g);
+                // one wait for all of step k's fragments: only step k+1's reads may still be in
+                // flight (LDS operations of a wave complete in order, the slab's stores included)
+                if constexpr (SPLIT_ONE_WAIT) wait_lgkmcnt<2 + NG>();
+            } else if constexpr (SPLIT_ONE_WAIT) {
+                wait_lgkmcnt<0>();
             }
+            if constexpr (SPLIT_ONE_WAIT) __builtin_amdgcn_sched_barrier(0);  // no FMA above the wait
             const float a_[8] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
                                  fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
             float b_[TN];
