@@ -59,7 +59,10 @@ regtile::Problem make_problem(int M, int N, int K, float alpha, const void *A, i
     return p;
 }
 
-// Quick returns shared by both element types. Returns true when the call is complete.
+// Quick returns shared by both element types. Returns true when the call is complete. Every
+// path that launches first clears any error left pending by an earlier, unrelated runtime
+// call, which would otherwise be reported as this launch's status; M == 0 or N == 0 makes no
+// HIP call at all.
 bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
     if (p.M == 0 || p.N == 0) {
         g_last_kernel = "quick-return";
@@ -67,6 +70,7 @@ bool quick_return(const regtile::Problem &p, hipStream_t s, int *status) {
         *status = REGTILE_OK;
         return true;
     }
+    (void)hipGetLastError();
     if (p.K == 0 || p.alpha == 0.0f) {
         const char *name = "scale_c";
         *status = finish(regtile::launch_scale_c(p, s, &name), name);
@@ -87,9 +91,6 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // an error left pending by an earlier, unrelated runtime call would otherwise be reported
-    // as this launch's status
-    (void)hipGetLastError();
     int status;
     if (quick_return(p, s, &status)) return status;
     const char *name = "none";
@@ -130,9 +131,6 @@ int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // an error left pending by an earlier, unrelated runtime call would otherwise be reported
-    // as this launch's status
-    (void)hipGetLastError();
     int status;
     if (quick_return(p, s, &status)) return status;
     const char *name = "none";
