@@ -52,10 +52,10 @@ KERNELS = {
     "bf16_8192": ("bf16_mfma32x32x16_dma_256x256x64_w2x2", "bf16_mfma_dma_kernel<256, 256, 64, 2, 2, 32",
                   ["gemm_bf16_mfma_dma.hip", "mfma_common.h", "tile_addressing.h", "regtile_internal.h"],
                   2 * 8192 * 8192 * 2 + 8192 * 8192 * 4),
-    "f32_tall": ("f32_regtile_splitk8_64x128x8_8x16", "SplitCfg<8, 8, 16, 8, 1>, false",
+    "f32_tall": ("f32_regtile_splitk8_64x128x8_8x16", "SplitCfg<8, 8, 16, 8, 1, 4>, false",
                  ["gemm_f32_splitk.hip", "regtile_internal.h"], (16384 * 4096 + 4096 * 128 + 16384 * 128) * 4),
     # beta != 0: C is read and written
-    "f32_ragged": ("f32_regtile_splitk8_64x96x8_8x12_guard", "SplitCfg<8, 8, 12, 8, 1>, true",
+    "f32_ragged": ("f32_regtile_splitk8_64x96x8_8x12_guard", "SplitCfg<8, 8, 12, 8, 1, 4>, true",
                    ["gemm_f32_splitk.hip", "regtile_internal.h"], (1000 * 777 + 777 * 1500 + 2 * 1000 * 1500) * 4),
 }
 PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged", "copy"]
