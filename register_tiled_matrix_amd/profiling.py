@@ -13,7 +13,9 @@ stops at the first pass that fails. The passes:
              for the fp32 4096^3, bf16 8192^3 and fp32 16384x128x4096 kernels and for a plain
              1 GiB device copy (the calibration: bytes moved / counter bytes);
   sq_*       LDS, VALU and MFMA instruction and cycle counters per kernel;
-  state_*    where the waves' time goes (VALU / LDS / VMEM issue, waiting) per kernel.
+  state_*    where the waves' time goes (VALU / LDS / VMEM issue, waiting) per kernel;
+  clock_datadep  the shader clock and MFMA busy share of the bf16 kernel on six input data
+             sets (tune datadep).
 
 `summarize` turns the CSV files into the short tables under profiles/ and writes
 profiles/pmc_traffic.json, from which bench.py reports `roofline.traffic` (HBM bytes per
@@ -43,6 +45,11 @@ LADDER_COUNTERS = "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INSTS_
 STATE_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM "
                   "SQ_WAVES")
 COPY_BYTES = 1 << 30
+# the shader clock and the MFMA pipes' busy share per dispatch, for the same bf16 kernel on
+# different input data (tune datadep)
+CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES"
+DD_STEPS, DD_ROUNDS, DD_WARMUP = 10, 2, 20
+N_XCD, N_SIMD = 8, 1024
 
 # workload -> (kernel label as regtile_last_kernel() names it, substring of the kernel's symbol,
 #              sources whose digest stamps the record, algorithmic HBM bytes per launch)
@@ -88,6 +95,10 @@ def passes(out):
         p.append((f"state_{w}", ["rocprofv3", "--pmc", *STATE_COUNTERS.split(), "-d", os.path.join(out, f"state_{w}"),
                                  "-o", "st", "--output-format", "csv", "--",
                                  *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    p.append(("clock_datadep", ["rocprofv3", "--kernel-trace", "--pmc", *CLOCK_COUNTERS.split(), "-d",
+                                 os.path.join(out, "clock_datadep"), "-o", "clk", "--output-format", "csv", "--",
+                                 "python3", "-m", "register_tiled_matrix_amd.tune", "datadep",
+                                 "--steps", str(DD_STEPS), "--rounds", str(DD_ROUNDS), "--warmup", str(DD_WARMUP)], 300))
     p.append(("sq_ladder", ["rocprofv3", "--pmc", *LADDER_COUNTERS.split(), "-d", os.path.join(out, "sq_ladder"),
                             "-o", "sq", "--output-format", "csv", "--", "python3", "-m",
                             "register_tiled_matrix_amd.tune", "ladder", "--workloads", "f32_4096,bf16_8192",
@@ -375,6 +386,59 @@ def summarize_ladder_sq(prof, out_md):
         json.dump(rec, f, indent=1)
 
 
+def summarize_datadep(prof, out_md):
+    """Clock and MFMA busy share of the bf16 8192^3 kernel per input data set. tune datadep
+    launches DD_WARMUP warm-up launches of the first set, then DD_ROUNDS rounds over the sets,
+    each set 10 untimed and DD_STEPS timed launches; the dispatches are labelled in that order."""
+    d = os.path.join(prof, "clock_datadep")
+    rows = [r for r in csv.DictReader(open(os.path.join(d, "clk_counter_collection.csv")))
+            if "bf16_mfma_dma_kernel" in r["Kernel_Name"]]
+    per = collections.OrderedDict()
+    for r in rows:
+        per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(d, "clk_kernel_trace.csv"))):
+        if "bf16_mfma_dma_kernel" in r["Kernel_Name"]:
+            dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    sets = []
+    with open(os.path.join(prof, "clock_datadep.out")) as f:
+        for line in f:
+            if line.startswith("| ") and not line.startswith("| A, B data") and "---" not in line:
+                sets.append(line.split("|")[1].strip())
+    order = [sets[0]] * DD_WARMUP
+    for _ in range(DD_ROUNDS):
+        for k in sets:
+            order += [k] * (10 + DD_STEPS)
+    ids = sorted(per)
+    if len(ids) != len(order):
+        raise ValueError(f"{len(ids)} bf16 dispatches against {len(order)} expected")
+    import gemm_inputs as gi
+
+    flop = gi.WORKLOADS["bf16_8192"].flop
+    stats = collections.OrderedDict((k, []) for k in sets)
+    for i, k in zip(ids, order[:len(ids)]):
+        c = per[i]
+        cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+        t = dur[i]
+        stats[k].append((t, cycles / t / 1e9, c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cycles, flop / t / 1e12))
+    argv = [a for n, a, _ in passes(prof) if n == "clock_datadep"][0]
+    md = ["# bf16 8192^3: clock and MFMA busy share against the input data (rocprofv3 --pmc, GRBM and SQ cycles)", ""]
+    md += _cmd_block([_display(argv, prof)])
+    md += ["The same kernel and the same instruction stream on six input data sets, interleaved. Per dispatch: "
+           "the duration from the kernel trace; the shader clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; the "
+           "MFMA busy share = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / those cycles. Medians over the timed "
+           "and untimed launches of both rounds (the counters serialise the dispatches, so durations run a "
+           "little longer than in the benchmark).", "",
+           "| A, B data | dispatches | duration (ms) | clock (GHz) | MFMA busy | TFLOP/s |", "|---|---|---|---|---|---|"]
+    for k, v in stats.items():
+        if not v:
+            continue
+        med = [statistics.median(x[j] for x in v) for j in range(4)]
+        md.append(f"| {k} | {len(v)} | {med[0] * 1e3:.4f} | {med[1]:.2f} | {100 * med[2]:.0f} % | {med[3]:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(prof) -> int:
     prof = os.path.abspath(prof)
     for w in TRACE_WORKLOADS:
@@ -386,6 +450,8 @@ def summarize(prof) -> int:
     if os.path.exists(os.path.join(prof, "sq_f32_4096")):
         summarize_sq(prof, os.path.join(PROFILES, "sq_counters_bench_kernels.md"),
                      os.path.join(PROFILES, "sq_counters_bench_kernels.json"))
+    if os.path.exists(os.path.join(prof, "clock_datadep", "clk_counter_collection.csv")):
+        summarize_datadep(prof, os.path.join(PROFILES, "clock_datadep_bf16_8192.md"))
     if os.path.exists(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv")):
         summarize_ladder_sq(prof, os.path.join(PROFILES, "lds_counters_ladder_f32_4096_bf16_8192.md"))
     return 0
