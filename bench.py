@@ -7,9 +7,11 @@ resident in HBM before the timed region. The same JSON line also carries the bf1
 MFMA paths at 8192^3 (A row-major, B column-major, N(0,1) rounded to the 16-bit type) and the
 kernel ladder (naive -> LDS-tiled -> register-tiled -> MFMA), each timed the same way.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-ladder] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--settle-ms 200] [--no-ladder] [--no-cpu]
 
-Timing: W untimed warm-up steps, then the timed region: K back-to-back steps between two
+Timing: untimed launches for --settle-ms of wall time (the clock ramps up over the first 20-50
+large launches after idle; reported as clock_settle), W untimed warm-up steps, then the timed
+region: K back-to-back steps between two
 torch.cuda.synchronize() calls (wall clock -> ms_per_step and value; one HIP event pair
 around the region -> back_to_back_ms_per_launch). A second pass of K launches puts a HIP
 event pair around every launch on the stream the library launches on (the caller's current
@@ -41,8 +43,11 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=50,
-                   help="untimed launches before each timed region (after idle the GPU needs "
-                        "about 20 fp32 4096^3 or 50 bf16 8192^3 launches to reach its steady clock)")
+                   help="untimed launches before each timed region")
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="before each headline leg's warmup, untimed launches for at least this "
+                        "long: after idle the GPU needs about 20 fp32 4096^3 or 50 bf16 8192^3 "
+                        "launches to reach its steady clock (reported as clock_settle; 0 skips)")
     p.add_argument("--no-ladder", action="store_true", help="skip the naive/LDS rungs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 and fp16 8192^3 legs")
@@ -81,6 +86,19 @@ def _time(torch, fn, steps, warmup):
     """(wall ms per step, mean per-launch kernel ms from event pairs, fastest launch ms)."""
     wall_ms, kern = _kernel_times(torch, fn, steps, warmup)
     return wall_ms, float(np.mean(kern)), float(np.min(kern))
+
+
+def _settle(torch, fn, settle_ms):
+    """Untimed launches for at least `settle_ms` of wall time (synchronising every 10 launches),
+    so that a timed region that follows sees the steady clock. Returns {"ms", "launches"}."""
+    n, t0 = 0, time.perf_counter()
+    while settle_ms > 0 and (time.perf_counter() - t0) * 1e3 < settle_ms:
+        fn()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "launches": n}
 
 
 def _time_steps(torch, fn, steps, warmup):
@@ -405,6 +423,7 @@ def main():
     kernel_name = rt.last_kernel()
     kernel_info = _kernel_info(rt)
     torch.cuda.synchronize()
+    settle = _settle(torch, step_f32, args.settle_ms)
     wall_ms, region_ms, kern_ms, kern_min = _time_steps(torch, step_f32, args.steps, args.warmup)
     flop = w.flop
     value = flop / (wall_ms * 1e-3) / 1e12
@@ -417,6 +436,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": settle,
         "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -466,11 +486,13 @@ def main():
         step_16()
         kname = rt.last_kernel()
         kinfo = _kernel_info(rt)
+        settle16 = _settle(torch, step_16, args.settle_ms)
         wms, rms, kms, kmin = _time_steps(torch, step_16, args.steps, args.warmup)
         v = wb.flop / (wms * 1e-3) / 1e12
         a = wb.flop / (kms * 1e-3) / 1e12
         res = {
             "value": round(v, 2), "unit": "TFLOP/s", "ms_per_step": round(wms, 4),
+            "clock_settle": settle16,
             "dtype": f"{label} in, f32 accumulate",
             "workload": f"{wname}: {wb.description}, seed {wb.seed}, alpha=1, beta=0",
             "percent_of_mfma_peak": round(100 * v / acc.PEAK_BF16_MFMA_TFLOPS, 2),
