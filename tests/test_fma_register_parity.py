@@ -1,12 +1,14 @@
-"""The fp32 register-tiled loops contain no FMA whose three VGPRs are all even-numbered (CPU).
+"""The fp32 register-tiled loops keep their FMAs off same-parity registers (CPU).
 
-On gfx950 a `v_fmac_f32` whose accumulator, src0 and src1 all sit in even-numbered VGPRs
-issues at about two thirds of the FMA rate (3.26 against 2.22 SIMD cycles per wave64 FMA at
-two waves per SIMD, `profiles/probe_valu_lds_gfx950.md`). The fragment quads read from LDS
-start at even registers, so the kernels tie each accumulator quad into one register tuple with
-its pairs swapped, which leaves every FMA at least one odd register. Register allocation is
-the compiler's, so this test disassembles the gfx950 code object of the in-tree build (our own
-objects only) and checks every fp32 register-tiled and split-K kernel.
+On gfx950 a `v_fmac_f32` whose accumulator, src0 and src1 are all even-numbered VGPRs, or all
+odd-numbered, issues at about two thirds of the FMA rate (3.5 against 2.5 SIMD cycles per
+wave64 FMA at two waves per SIMD, measured with a register-pinned FMA loop). The fragment quads
+read from LDS start at even registers, so the kernels tie each accumulator quad into one
+register tuple with its pairs swapped, which gives every FMA of the main loop mixed parity.
+Register allocation is the compiler's, so this test disassembles the gfx950 code object of the
+in-tree build (our own objects only) and checks every fp32 register-tiled and split-K kernel:
+no all-even FMA, and at most 1% all-odd ones (a few left by the compiler's copies; before the
+fix a quarter of the FMAs of the affected kernels were all-even and another quarter all-odd).
 """
 from __future__ import annotations
 
@@ -39,23 +41,24 @@ def _disassemble(obj):
         m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
         if m:
             cur = m.group(1)
-            kernels[cur] = [0, 0]
+            kernels[cur] = [0, 0, 0]
             continue
         f = FMA.search(line)
         if f and cur is not None:
             regs = [int(x) for x in f.groups()]
             kernels[cur][0] += 1
             kernels[cur][1] += all(r % 2 == 0 for r in regs)
+            kernels[cur][2] += all(r % 2 == 1 for r in regs)
     return kernels
 
 
 @pytest.mark.parametrize("obj", SOURCES)
-def test_no_fma_reads_three_even_registers(obj):
+def test_no_fma_reads_three_same_parity_registers(obj):
     path = os.path.join(BUILD, obj)
     if not os.path.exists(path) or not os.path.exists(OBJDUMP):
         pytest.skip("needs the in-tree build and llvm-objdump")
     kernels = {k: v for k, v in _disassemble(path).items()
                if ("f32_regtile_kernel" in k or "f32_splitk_kernel" in k) and v[0] > 0}
     assert kernels, "no fp32 register-tiled kernels found"
-    bad = {k: v for k, v in kernels.items() if v[1]}
-    assert not bad, {k[:90]: f"{v[1]} of {v[0]} FMAs all-even" for k, v in bad.items()}
+    bad = {k: v for k, v in kernels.items() if v[1] or v[2] > v[0] // 100}
+    assert not bad, {k[:90]: f"{v[1]} all-even and {v[2]} all-odd of {v[0]} FMAs" for k, v in bad.items()}
