@@ -629,16 +629,16 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 #define DMA_WIN32 1
 #define DMA_STAG32 1
 #define DMA_WIN16 1
-#define DMA_STAG16 0
+#define DMA_STAG16 1
 #endif
-// LDS layout per fragment shape: a ring of five half-stages for 32x32x16 (+3.5% at 8192^3
-// against two stages, same box and run), two stages for 16x16x32 (the ring measured 5.7%
-// slower there)
+// LDS layout per fragment shape: a ring of five half-stages for both (32x32x16: +3.5% at
+// 8192^3 against two stages; 16x16x32 with the stagger: 1234 against 1045 TFLOP/s at 8192^3
+// and 1173 against 985 at 4096^3, same box, interleaved)
 #ifndef DMA_RING32
 #define DMA_RING32 5
 #endif
 #ifndef DMA_RING16
-#define DMA_RING16 2
+#define DMA_RING16 5
 #endif
 
 template <bool F16, bool KTAIL>
