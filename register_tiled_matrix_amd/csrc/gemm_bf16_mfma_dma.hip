@@ -634,6 +634,10 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 // LDS layout per fragment shape: a ring of five half-stages for both (32x32x16: +3.5% at
 // 8192^3 against two stages; 16x16x32 with the stagger: 1234 against 1045 TFLOP/s at 8192^3
 // and 1173 against 985 at 4096^3, same box, interleaved)
+#ifndef DMA_SMALL_WIN
+#define DMA_SMALL_WIN 2
+#define DMA_SMALL_STAG 0
+#endif
 #ifndef DMA_RING32
 #define DMA_RING32 5
 #endif
@@ -644,9 +648,11 @@ hipError_t launch_dma_cfg(const Problem &p, hipStream_t s) {
 template <bool F16, bool KTAIL>
 hipError_t launch_dma_shape(const Problem &p, hipStream_t s, int shape, bool small) {
     // small: 128x128 tiles (64x64 per wave, 80 KB of LDS, two workgroups per CU), two DMA
-    // windows per slab and no stagger (best of three window / stagger settings measured at
-    // 2048x2048x8192, 2048x1024x8192, 1536x1536x8192 and 3000x2000x2000)
-    if (small) return launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, 2, 0, F16, 5, 0, KTAIL>(p, s);
+    // windows per slab and no stagger (best of the four window / stagger settings that fit,
+    // two or three windows with or without the stagger, measured at 2048x2048x8192,
+    // 2048x1024x8192, 1536x1536x8192, 3000x2000x2000 and 2048x4096x4096: the others lost up
+    // to 19%; one window needs more DMA issue slots per k step than the 4 MFMAs give)
+    if (small) return launch_dma_cfg<128, 128, DMA_BK, 2, 2, 32, DMA_SMALL_WIN, DMA_SMALL_STAG, F16, 5, 0, KTAIL>(p, s);
     if (shape == 16)
         return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 16, DMA_WIN16, DMA_STAG16, F16, DMA_RING16, 0, KTAIL>(p, s);
     return launch_dma_cfg<DMA_BM, DMA_BN, DMA_BK, DMA_WM, DMA_WN, 32, DMA_WIN32, DMA_STAG32, F16, DMA_RING32, 0, KTAIL>(p, s);
