@@ -269,13 +269,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
         }
     };
 
-    // Software pipeline, last slab peeled. Interior tiles (no EDGE guards): registers hold slab s+1 when slab s starts; it goes to
-    // the stage slab s-1 used (free since the last barrier) before the loads of slab s+2 are
-    // issued and slab s is consumed, so the slab boundary is only the barrier (each wave's
-    // stores completed long before) and the first fragment reads. Measured against storing
-    // after the compute (next loop): +1.6-2.1% at 4096^3 and +1.0-1.4% at 8192^3 in
-    // interleaved A/B runs on two boxes, outputs bitwise equal; with the EDGE guards it lost
-    // up to 5% (4000^3), so edge tiles keep that order.
+    // Software pipeline, last slab peeled. Launches without edge guards: registers hold slab
+    // s+1 when slab s starts; it goes to the stage slab s-1 used (free since the last barrier)
+    // before the loads of slab s+2 are issued and slab s is consumed, so the slab boundary is
+    // only the barrier (each wave's stores completed long before) and the first fragment
+    // reads. Measured against storing after the compute (next loop): +1.6-2.1% at 4096^3 and
+    // +1.0-1.4% at 8192^3 in interleaved A/B runs on two boxes, outputs bitwise equal; with
+    // the edge guards it lost up to 5% (4000^3), so edge launches keep that order. (Choosing
+    // the order per tile inside an edge launch did not help either: its guarded tiles finish
+    // last and set its time.)
     const int nslabs = (K + BK - 1) / BK;
     if constexpr (F32_EARLY_STORE && !EDGE) {
         if (nslabs > 0) {
