@@ -47,6 +47,12 @@ constexpr int APAD = 4;
 #ifndef SPLIT96_DEPTH
 #define SPLIT96_DEPTH 1
 #endif
+// 1: wave w runs slabs w, w + NW, w + 2 NW, ... of K (the waves of a workgroup sweep K side by
+// side, so at any time they read neighbouring k of the same A rows and share its cache lines);
+// 0: wave w runs one contiguous range of slabs
+#ifndef SPLIT_INTERLEAVE
+#define SPLIT_INTERLEAVE 1
+#endif
 
 template <int NW_, int TM_, int TN_, int BK_, int DEPTH_ = 1, int PAD_ = APAD>
 struct SplitCfg {
@@ -118,11 +124,16 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     int tm, tn;
     grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * TILE_M, n0 = tn * TILE_N;
-    const int kb = wave * slabs_per_wave * BK;  // this wave's k range [kb, ke)
-    const int ke = min(K, kb + slabs_per_wave * BK);
-    // This wave's own slab count: only slabs that reach into [kb, ke) (the last waves of a K
-    // that does not fill NW equal ranges run fewer; the loop has no workgroup barrier).
-    const int spw_w = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+    // This wave's slabs: slab t of the wave starts at k = kslab(t). Interleaved, wave w runs
+    // slabs w, w + NW, ... of the K sweep and every load stops at K; in ranges, it runs a
+    // contiguous range [kb, ke). Waves may run different slab counts: the main loop has no
+    // workgroup barrier.
+    const int nslabs = (K + BK - 1) / BK;
+    const int kb = SPLIT_INTERLEAVE ? 0 : wave * slabs_per_wave * BK;
+    const int ke = SPLIT_INTERLEAVE ? K : min(K, kb + slabs_per_wave * BK);
+    const int spw_w = SPLIT_INTERLEAVE ? (nslabs > wave ? (nslabs - wave + NW - 1) / NW : 0)
+                                       : (ke > kb ? (ke - kb + BK - 1) / BK : 0);
+    auto kslab = [&](int t) { return SPLIT_INTERLEAVE ? (t * NW + wave) * BK : kb + t * BK; };
 
     // Staging: float4 q of the A slab (TILE_M rows x BK k) is row q / AQ, k (q % AQ) * 4;
     // float4 q of the B slab (BK k x TILE_N columns) is k q / BQ, column (q % BQ) * 4. With
@@ -246,15 +257,15 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
     };
 
-    // Each wave runs the slabs of its own range; the last of them may reach past ke (loads
+    // Each wave runs its own slabs; the last slab of the sweep may reach past ke = K (loads
     // past ke are zeros).
     const int spw = spw_w;
     if constexpr (CFG::DEPTH == 1) {
         if (spw > 0) {
-            load_slab(kb);
+            load_slab(kslab(0));
             store_slab(0);
             for (int s = 0; s + 1 < spw; ++s) {
-                load_slab(kb + (s + 1) * BK);
+                load_slab(kslab(s + 1));
                 compute_slab(s & 1);
                 store_slab((s + 1) & 1);
             }
@@ -266,17 +277,17 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // Set (ra, rb) carries the even slabs and buffer 0, set (ra2, rb2) the odd slabs and
         // buffer 1; the loop body is one pair of slabs so both sets stay in fixed registers.
         if (spw > 0) {
-            load_into(kb, ra, rb);
-            if (spw > 1) load_into(kb + BK, ra2, rb2);
+            load_into(kslab(0), ra, rb);
+            if (spw > 1) load_into(kslab(1), ra2, rb2);
             store_from(0, ra, rb);
             int s = 0;
             for (; s + 2 < spw; s += 2) {
                 // slab s (even): buffer 0; slab s + 1 waits in (ra2, rb2)
-                load_into(kb + (s + 2) * BK, ra, rb);
+                load_into(kslab(s + 2), ra, rb);
                 compute_slab(0);
                 store_from(1, ra2, rb2);
                 // slab s + 1 (odd): buffer 1; slab s + 2 waits in (ra, rb)
-                if (s + 3 < spw) load_into(kb + (s + 3) * BK, ra2, rb2);
+                if (s + 3 < spw) load_into(kslab(s + 3), ra2, rb2);
                 compute_slab(1);
                 store_from(0, ra, rb);
             }
@@ -419,8 +430,10 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name, const 
     const int tiles_n = (p.N + CFG::TILE_N - 1) / CFG::TILE_N;
     const int nslabs = (p.K + CFG::BK - 1) / CFG::BK;
     const int spw = (nslabs + CFG::NW - 1) / CFG::NW;  // slabs per wave
+    // Interleaved slabs need the element checks only for a partial last slab; ranges also
+    // for a K that does not fill NW equal ranges.
     const bool guard = (p.M % CFG::TILE_M) != 0 || (p.N % CFG::TILE_N) != 0 ||
-                       (p.K % (CFG::NW * CFG::BK)) != 0;
+                       (p.K % ((SPLIT_INTERLEAVE ? 1 : CFG::NW) * CFG::BK)) != 0;
     const bool va = (p.lda % 4) == 0 && aligned16(p.A);
     const bool vb = (p.ldb % 4) == 0 && aligned16(p.B);
     const bool vc = (p.ldc % 4) == 0 && aligned16(p.C);
