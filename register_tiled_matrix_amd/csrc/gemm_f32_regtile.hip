@@ -49,11 +49,18 @@ namespace {
 #ifndef F32_WAVES_PER_EU
 #define F32_WAVES_PER_EU 2
 #endif
+// LDS stages of A and B slabs: 2 (double buffering), 1 (one stage; the next slab waits in
+// registers and is stored between two barriers) or 3 (a slab is stored two slabs before the one
+// that last read its stage)
+#ifndef F32_STAGES
+#define F32_STAGES 2
+#endif
 struct SquareCfg {
-    static constexpr int TM = F32_TM, TN = F32_TN, BK = F32_BK, WAVES = F32_WAVES_PER_EU;
+    static constexpr int TM = F32_TM, TN = F32_TN, BK = F32_BK, WAVES = F32_WAVES_PER_EU,
+                         STAGES = F32_STAGES;
 };
 struct SmallCfg {
-    static constexpr int TM = 4, TN = 4, BK = 32, WAVES = 4;
+    static constexpr int TM = 4, TN = 4, BK = 32, WAVES = 4, STAGES = 2;
 };
 
 constexpr int NT = 256;
@@ -71,10 +78,10 @@ struct Shape {
 };
 
 // B rows get the same padding when B is staged by transposed stores (B stored N x K).
-template <int BM, int BN, int BK, int BPAD>
+template <int BM, int BN, int BK, int BPAD, int ST>
 struct alignas(16) Smem {
-    float a[2][BK][BM + APAD];
-    float b[2][BK][BN + BPAD];
+    float a[ST][BK][BM + APAD];
+    float b[ST][BK][BN + BPAD];
 };
 
 // Global -> register staging of one slab. A: BM x BK as BK/4 float4 chunks per row;
@@ -118,7 +125,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
     constexpr int CHB = BK * BN / (4 * NT);  // B float4 chunks per thread per slab
     constexpr int BPAD = TB ? APAD : 0;
     constexpr int BLD = BN + BPAD;           // LDS row stride of the B slab
-    __shared__ Smem<BM, BN, BK, BPAD> sm;
+    constexpr int ST = CFG::STAGES;
+    static_assert(ST >= 1 && ST <= 3, "one to three LDS stages");
+    __shared__ Smem<BM, BN, BK, BPAD, ST> sm;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -279,16 +288,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
     // the order per tile inside an edge launch did not help either: its guarded tiles finish
     // last and set its time.)
     const int nslabs = (K + BK - 1) / BK;
-    if constexpr (F32_EARLY_STORE && !EDGE) {
+    auto stage = [](int slab) { return (int)((unsigned)slab % (unsigned)ST); };
+    if constexpr (ST == 1) {
+        // One stage: the loads of slab s+1 are in flight while slab s is consumed; a barrier
+        // frees the stage, the registers are stored, a second barrier publishes them.
+        if (nslabs > 0) {
+            load_slab(0);
+            store_slab(0);
+            __syncthreads();
+            for (int s = 0; s + 1 < nslabs; ++s) {
+                load_slab((s + 1) * BK);
+                compute_slab(0);
+                __syncthreads();
+                store_slab(0);
+                __syncthreads();
+            }
+            compute_slab(0);
+        }
+    } else if constexpr (F32_EARLY_STORE && !EDGE) {
         if (nslabs > 0) {
             load_slab(0);
             store_slab(0);
             if (nslabs > 1) load_slab(BK);
             __syncthreads();
             for (int s = 0; s + 1 < nslabs; ++s) {
-                store_slab((s + 1) & 1);
+                store_slab(stage(s + 1));
                 if (s + 2 < nslabs) load_slab((s + 2) * BK);
-                compute_slab(s & 1);
+                compute_slab(stage(s));
                 // this wave's stores of slab s+1 are complete; the barrier without a fence
                 // leaves the loads of slab s+2 in flight
                 wait_lgkmcnt<0>();
@@ -298,21 +324,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("" ::: "memory");
             }
-            compute_slab((nslabs - 1) & 1);
+            compute_slab(stage(nslabs - 1));
         }
     } else if (nslabs > 0) {
         // issue the global loads of slab s+1, consume slab s from LDS, store slab s+1 to the
-        // other stage, one barrier
+        // next stage, one barrier
         load_slab(0);
         store_slab(0);
         __syncthreads();
         for (int s = 0; s + 1 < nslabs; ++s) {
             load_slab((s + 1) * BK);
-            compute_slab(s & 1);
-            store_slab((s + 1) & 1);
+            compute_slab(stage(s));
+            store_slab(stage(s + 1));
             __syncthreads();
         }
-        compute_slab((nslabs - 1) & 1);
+        compute_slab(stage(nslabs - 1));
     }
 
     // Register parity of the accumulators. Each fragment quad from LDS starts at an even

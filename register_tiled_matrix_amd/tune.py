@@ -4,8 +4,8 @@ The trade the pages put at the centre of register tiling ("寄存器Tiling跨架
 6.2 and 7.1-7.4; "Understanding Register Tiling", the accounting of registers against reuse):
 a bigger TM x TN micro-tile reads LDS less per FMA but holds more registers, so fewer waves
 fit a SIMD, and past the register file the compiler spills. Every variant is the same kernel
-source built with other compile-time values (F32_TM, F32_TN, F32_BK, F32_WAVES_PER_EU), so the
-sweep measures the trade itself. The one-output-per-thread ablation is the LDS rung of the
+source built with other compile-time values (F32_TM, F32_TN, F32_BK, F32_WAVES_PER_EU and the
+LDS stage count F32_STAGES), so the sweep measures the trade itself. The one-output-per-thread ablation is the LDS rung of the
 ladder (algorithm 2).
 
     python -m register_tiled_matrix_amd.tune build            # CPU: compile every variant
@@ -34,35 +34,40 @@ from . import build as _build
 
 VARIANT_DIR = os.path.join(_build.BUILD_DIR, "variants")
 
-# name -> (TM, TN, BK, waves per SIMD requested)
+# name -> (TM, TN, BK, waves per SIMD requested, LDS stages)
 VARIANTS = {}
 for _bk in (8, 16, 32):
     for _w in (2, 3, 4):
-        VARIANTS[f"8x8_bk{_bk}_w{_w}"] = (8, 8, _bk, _w)
+        VARIANTS[f"8x8_bk{_bk}_w{_w}"] = (8, 8, _bk, _w, 2)
     for _w in (1, 2):
-        VARIANTS[f"8x16_bk{_bk}_w{_w}"] = (8, 16, _bk, _w)
+        VARIANTS[f"8x16_bk{_bk}_w{_w}"] = (8, 16, _bk, _w, 2)
 for _bk in (8, 16):
     for _w in (1, 2):
-        VARIANTS[f"16x8_bk{_bk}_w{_w}"] = (16, 8, _bk, _w)
+        VARIANTS[f"16x8_bk{_bk}_w{_w}"] = (16, 8, _bk, _w, 2)
 for _bk in (16, 32):
     for _w in (2, 4, 8):
-        VARIANTS[f"4x4_bk{_bk}_w{_w}"] = (4, 4, _bk, _w)
-VARIANTS["8x16_bk16_w4"] = (8, 16, 16, 4)  # past the register file: the spill cliff
+        VARIANTS[f"4x4_bk{_bk}_w{_w}"] = (4, 4, _bk, _w, 2)
+VARIANTS["8x16_bk16_w4"] = (8, 16, 16, 4, 2)  # past the register file: the spill cliff
+# LDS stages: one (two barriers per slab) and three, beside the default two
+for _tm, _tn, _bk, _w in ((8, 16, 16, 2), (8, 16, 8, 2), (16, 8, 16, 2), (8, 8, 16, 2), (8, 8, 8, 4),
+                          (4, 4, 32, 4)):
+    for _st in (1, 3):
+        VARIANTS[f"{_tm}x{_tn}_bk{_bk}_w{_w}_s{_st}"] = (_tm, _tn, _bk, _w, _st)
 
 F32_SRC = "gemm_f32_regtile.hip"
 
 
-def _variant_flags(tm, tn, bk, w):
-    return [f"-DF32_TM={tm}", f"-DF32_TN={tn}", f"-DF32_BK={bk}", f"-DF32_WAVES_PER_EU={w}"]
+def _variant_flags(tm, tn, bk, w, st):
+    return [f"-DF32_TM={tm}", f"-DF32_TN={tn}", f"-DF32_BK={bk}", f"-DF32_WAVES_PER_EU={w}",
+            f"-DF32_STAGES={st}"]
 
 
 def build_variant(name: str) -> dict:
     """Compile the fp32 kernel with the variant's values and link it with the default objects
     of every other translation unit (from the in-tree build)."""
-    tm, tn, bk, w = VARIANTS[name]
     out = os.path.join(VARIANT_DIR, name)
     os.makedirs(out, exist_ok=True)
-    obj, log = _build._compile(F32_SRC, _variant_flags(tm, tn, bk, w), out)
+    obj, log = _build._compile(F32_SRC, _variant_flags(*VARIANTS[name]), out)
     others = [os.path.join(_build.BUILD_DIR, s + ".o") for s in _build.SOURCES if s != F32_SRC]
     missing = [o for o in others if not os.path.exists(o)]
     if missing:
@@ -112,6 +117,14 @@ def cmd_run(args) -> int:
     stream = torch.cuda.current_stream().cuda_stream
 
     def timed(fn, steps, warmup):
+        # untimed launches for settle_ms of wall time first: after a kernel change or idle the
+        # clock takes 20-50 large launches to reach its steady value, so without this the
+        # variants timed first would run at a lower clock than the later ones
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
         for _ in range(warmup):
             fn()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -393,6 +406,16 @@ def _ladder_report(rows, src) -> str:
     return "\n".join(out) + "\n"
 
 
+def _workload_mn(wl: str):
+    """(M, N) of a named workload, or (0, 0) when unknown."""
+    try:
+        import gemm_inputs as gi
+        w = gi.WORKLOADS[wl]
+        return w.M, w.N
+    except (ImportError, KeyError):
+        return 0, 0
+
+
 def cmd_report(args) -> int:
     rows = [json.loads(l) for l in open(args.jsonl) if l.strip().startswith("{")]
     src = os.path.relpath(os.path.abspath(args.jsonl), _build.ROOT)
@@ -407,24 +430,35 @@ def cmd_report(args) -> int:
     out = ["# fp32 micro-tile / occupancy sweep", "",
            "Commands (repository root; the variants are built on the CPU first):", "", "```",
            "python -m register_tiled_matrix_amd.tune build",
-           f"python -m register_tiled_matrix_amd.tune run --workloads f32_4096,f32_tall > {src}",
+           "python -m register_tiled_matrix_amd.tune run --workloads "
+           f"{','.join(dict.fromkeys(r['workload'] for r in rows))} > {src}",
            f"python -m register_tiled_matrix_amd.tune report {src}", "```", "",
            "Each variant is the same kernel source with other compile-time values: micro-tile TM x TN "
-           "per lane (workgroup tile 16TM x 16TN, 256 threads), slab depth BK, and the waves per SIMD "
-           "requested from the compiler (`amdgpu_waves_per_eu`). VGPRs, scratch and occupancy are the "
+           "per lane (workgroup tile 16TM x 16TN, 256 threads), slab depth BK, the number of LDS stages "
+           "(2: double-buffered; 1: one stage, two barriers per slab; 3: a slab is stored two slabs "
+           "ahead of its stage's last reader), and the waves per SIMD requested from the compiler "
+           "(`amdgpu_waves_per_eu`). `tiles` is the workload's workgroup count. VGPRs, scratch and "
+           "occupancy are the "
            "compiler's own report. `exact` = output bitwise equal to the naive rung (fmaf over k in "
-           "natural order). LDS floats read per FMA = (TM + TN) / (TM TN).", ""]
+           "natural order). LDS floats read per FMA = (TM + TN) / (TM TN). Each variant is timed "
+           "after 150 ms of untimed launches (so that every variant runs at the steady clock) and 3 "
+           "warm-up launches: mean of 20 launches, each timed by its own HIP event pair.", ""]
     for wl in dict.fromkeys(r["workload"] for r in rows):
-        out += [f"## {wl}", "", "| variant | TM x TN | BK | VGPRs | scratch B/lane | waves/SIMD | LDS B | "
-                "LDS floats/FMA | exact | mean ms | TFLOP/s |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        out += [f"## {wl}", "", "| variant | TM x TN | BK | stages | tiles | VGPRs | scratch B/lane | "
+                "waves/SIMD | LDS B | LDS floats/FMA | exact | mean ms | TFLOP/s |",
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        wm, wn = _workload_mn(wl)
         for r in sorted((r for r in rows if r["workload"] == wl), key=lambda r: -r["tflops"]):
             name = r["variant"]
             if name in VARIANTS:
-                tm, tn, bk, _ = VARIANTS[name]
+                tm, tn, bk, _, st = VARIANTS[name]
                 shape, bks, lf = f"{tm}x{tn}", str(bk), f"{(tm + tn) / (tm * tn):.3f}"
+                sts = str(st)
+                tiles = str(-(-wm // (16 * tm)) * -(-wn // (16 * tn))) if wm else "-"
             else:
                 shape, bks, lf = ("1x1", "32", "2.000") if "lds" in name else ("-", "-", "-")
-            out.append(f"| {name} (`{r['kernel']}`) | {shape} | {bks} | {r.get('vgprs', '-')} | "
+                sts, tiles = "-", "-"
+            out.append(f"| {name} (`{r['kernel']}`) | {shape} | {bks} | {sts} | {tiles} | {r.get('vgprs', '-')} | "
                        f"{r.get('scratch_bytes', '-')} | {r.get('waves_per_simd', '-')} | {r.get('lds_bytes', '-')} | "
                        f"{lf} | {r['bitwise_equal_naive']} | {r['ms_mean']} | {r['tflops']} |")
         out.append("")
@@ -445,8 +479,10 @@ def main(argv=None) -> int:
     r = sub.add_parser("run")
     r.add_argument("--variants", default="")
     r.add_argument("--workloads", default="f32_4096,f32_tall")
-    r.add_argument("--steps", type=int, default=10)
+    r.add_argument("--steps", type=int, default=20)
     r.add_argument("--warmup", type=int, default=3)
+    r.add_argument("--settle-ms", type=float, default=150.0,
+                   help="untimed launches for this long before each variant's warm-up")
     r.add_argument("--no-rungs", action="store_true",
                    help="time only the variants (for counter runs, where the default library's "
                         "kernels would share the variants' names)")
