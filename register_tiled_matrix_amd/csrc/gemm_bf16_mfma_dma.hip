@@ -39,6 +39,14 @@
 #include "mfma_common.h"
 #include "regtile_internal.h"
 
+// 1: each k step's MFMAs walk the wave tile's fragment grid row by row in alternating
+// column order, so consecutive MFMAs always share one operand (fewer operand bits switch from
+// one MFMA to the next; the package's clock on random data is power-bound); 0: row by row,
+// left to right. Either order gives every accumulator the same sequence of k steps.
+#ifndef DMA_SNAKE
+#define DMA_SNAKE 1
+#endif
+
 namespace regtile {
 
 namespace {
@@ -318,7 +326,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+            for (int jj = 0; jj < NI; ++jj) {
+                const int j = (DMA_SNAKE && (i & 1)) ? NI - 1 - jj : jj;
+                acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+            }
         int r_left = reads, d_left = dmas;
 #pragma unroll
         for (int g = 0; g < NMFMA; ++g) {
@@ -347,7 +358,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void bf16_mfma_dma_kernel(
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+            for (int jj = 0; jj < NI; ++jj) {
+                const int j = (DMA_SNAKE && (i & 1)) ? NI - 1 - jj : jj;
+                acc[i][j] = F::mfma(fa[cb][i], fb[cb][j], acc[i][j]);
+            }
 #pragma unroll
         for (int g = 0; g < NMFMA; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
