@@ -6,7 +6,9 @@
 // tile over its own share of K, with the register micro-tile of the square kernel
 // ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA / regB per
 // k, TM x TN FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
-// tile size against the number of resident waves). Three shapes:
+// tile size against the number of resident waves). Four shapes:
+//   * 32x32 tile, 4 waves, 4x4 micro-tiles, BK 16 (splitk4, problems of fewer than 64 tiles
+//     of 64x64);
 //   * 64x64 tile, 4 waves, 8x8 micro-tiles, BK 16 (splitk4);
 //   * 64x128 tile, 8 waves, 8x16 micro-tiles (the square kernel's), BK 8 (splitk8): one
 //     workgroup of two waves per SIMD per CU, and three quarters of the LDS reads per FMA of
@@ -16,7 +18,7 @@
 // The partial tiles are summed through LDS in a fixed order, so results are deterministic;
 // the summation order differs from the square kernel's single k sweep.
 //
-// Per wave: 64 lanes as an 8x8 grid, lane micro-tile rows {r0..r0+3, r0+32..r0+35} and
+// Per wave: 64 lanes as an 8x8 grid, lane micro-tile rows r0 + 32 g + {0..3} for g < TM/4 and
 // columns c0 + 32 g + {0..3} for g < TN/4 (every wave-wide 16-byte fragment read is one
 // contiguous 128-byte run). Each wave stages its own A slab (k-major, padded) and B slab in
 // its own two LDS buffers. No wave reads another wave's buffers, so the main loop needs no
@@ -67,7 +69,8 @@ struct SplitCfg {
     static constexpr int NB4 = BK * TILE_N / 256;           // B float4 per lane per slab
     static constexpr int NPART = NW < 4 ? NW : 4;           // partial tiles held in LDS at once
     static constexpr int SW = TILE_M * TILE_N / NT;         // epilogue columns per thread
-    static_assert(TM == 8 && (TN == 8 || TN == 12 || TN == 16), "micro-tile rows in two groups of 4");
+    static_assert((TM == 4 || TM == 8) && (TN == 4 || TN == 8 || TN == 12 || TN == 16),
+                  "micro-tile rows in one or two groups of 4");
     static_assert(SW % 4 == 0 && TILE_N % SW == 0, "whole float4 strips in the epilogue");
     static_assert(NW == 4 || NW == 8, "four waves, or eight summed pairwise first");
     static_assert(NA4 >= 1 && NB4 >= 1 && TILE_M * BK % 256 == 0 && BK * TILE_N % 256 == 0,
@@ -84,6 +87,7 @@ struct SplitCfg {
     };
 };
 using Split4 = SplitCfg<4, 8, 8, 16>;
+using Split4t = SplitCfg<4, 4, 4, 16>;  // 32x32 tiles for problems of a few 64x64 tiles
 using Split8 = SplitCfg<8, 8, 16, 8>;
 using Split8n96 = SplitCfg<8, 8, 12, SPLIT96_BK, SPLIT96_DEPTH, SPLIT96_APAD>;  // 64x96 tiles: 1000 x 1500 is 256 of them
 
@@ -214,33 +218,40 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int n = 0; n < TN; ++n) acc[m][n] = 0.0f;
 
-    constexpr int NG = TN / 4;  // column groups of 4, 32 apart
+    constexpr int MG = TM / 4, NG = TN / 4;  // row and column groups of 4, 32 apart
     auto compute_slab = [&](int buf) {
         const float *sa = &sm.st[wave][buf].a[0][0] + r0;
         const float *sb = &sm.st[wave][buf].b[0][0] + c0;
-        float4 fa[2][2], fb[2][NG];
-        fa[0][0] = *reinterpret_cast<const float4 *>(sa);
-        fa[0][1] = *reinterpret_cast<const float4 *>(sa + 32);
+        float4 fa[2][MG], fb[2][NG];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) fa[0][g] = *reinterpret_cast<const float4 *>(sa + 32 * g);
 #pragma unroll
         for (int g = 0; g < NG; ++g) fb[0][g] = *reinterpret_cast<const float4 *>(sb + 32 * g);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const int cb = k & 1, nb = cb ^ 1;
             if (k + 1 < BK) {
-                fa[nb][0] = *reinterpret_cast<const float4 *>(sa + (k + 1) * AS);
-                fa[nb][1] = *reinterpret_cast<const float4 *>(sa + (k + 1) * AS + 32);
+#pragma unroll
+                for (int g = 0; g < MG; ++g)
+                    fa[nb][g] = *reinterpret_cast<const float4 *>(sa + (k + 1) * AS + 32 * g);
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     fb[nb][g] = *reinterpret_cast<const float4 *>(sb + (k + 1) * TILE_N + 32 * g);
                 // one wait for all of step k's fragments: only step k+1's reads may still be in
                 // flight (LDS operations of a wave complete in order, the slab's stores included)
-                if constexpr (SPLIT_ONE_WAIT) wait_lgkmcnt<2 + NG>();
+                if constexpr (SPLIT_ONE_WAIT) wait_lgkmcnt<MG + NG>();
             } else if constexpr (SPLIT_ONE_WAIT) {
                 wait_lgkmcnt<0>();
             }
             if constexpr (SPLIT_ONE_WAIT) __builtin_amdgcn_sched_barrier(0);  // no FMA above the wait
-            const float a_[8] = {fa[cb][0].x, fa[cb][0].y, fa[cb][0].z, fa[cb][0].w,
-                                 fa[cb][1].x, fa[cb][1].y, fa[cb][1].z, fa[cb][1].w};
+            float a_[TM];
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                a_[4 * g + 0] = fa[cb][g].x;
+                a_[4 * g + 1] = fa[cb][g].y;
+                a_[4 * g + 2] = fa[cb][g].z;
+                a_[4 * g + 3] = fa[cb][g].w;
+            }
             float b_[TN];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto write_part = [&](int slot) {
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
-            const int row = r0 + (m < 4 ? m : 28 + m);
+            const int row = r0 + (m / 4) * 32 + m % 4;
 #pragma unroll
             for (int g = 0; g < NG; ++g)
                 *reinterpret_cast<float4 *>(&sm.part[slot][row][c0 + 32 * g]) =
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (wave < 4) {
 #pragma unroll
             for (int m = 0; m < TM; ++m) {
-                const int row = r0 + (m < 4 ? m : 28 + m);
+                const int row = r0 + (m / 4) * 32 + m % 4;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     const float4 p = *reinterpret_cast<const float4 *>(&sm.part[wave][row][c0 + 32 * g]);
@@ -450,6 +461,8 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, const char **name, const 
 // The 8-wave kernel runs one workgroup per CU, so the tile count in rounds of 256 workgroups
 // times the tile's area estimates its time. 64x96 tiles (8x12 micro-tiles) win where they fill
 // a round that 64x128 tiles leave partly idle (1000 x 1500: 256 tiles against 192).
+static int64_t tiles_64(const Problem &p) { return (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64); }
+
 static bool split8_prefers_96(int M, int N) {
     const int64_t tm64 = (M + 63) / 64;
     const int64_t t128 = tm64 * ((N + 127) / 128), t96 = tm64 * ((N + 95) / 96);
@@ -457,6 +470,12 @@ static bool split8_prefers_96(int M, int N) {
 }
 
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name) {
+    // Fewer than 64 tiles of 64x64 (a quarter of the CUs): 32x32 tiles of 4x4 micro-tiles, so
+    // that four times as many workgroups share the work (256^3: 64 workgroups, each wave
+    // 1024 FMAs per lane against 4096 on a 64x64 tile).
+    if (tiles_64(p) < 64)
+        return launch_cfg<Split4t>(p, s, name, "f32_regtile_splitk4_32x32x16_4x4",
+                                   "f32_regtile_splitk4_32x32x16_4x4_guard");
     // 8 waves x 8x16 once 64x128 tiles give most CUs a workgroup (two waves per SIMD), unless
     // the 4-wave kernel's 64x64 tiles already fill the chip and K is short enough that the
     // 8-wave kernel's longer reduction does not pay (measured on 13 row-major shapes with

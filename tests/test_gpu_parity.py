@@ -183,13 +183,35 @@ def test_f32_splitk8_edges(shape):
     assert_parity_full(inp, got, f"f32 split-K {shape} ({name})")
 
 
+# Split-K on 32x32 tiles (4 waves, 4x4 micro-tiles), taken for fewer than 64 tiles of 64x64:
+# exact multiples of the tile and of BK 16 (no bounds checks), ragged M, N and K, K below one
+# slab per wave, one row or column, and a long K.
+SPLITK_TINY_SHAPES = [(256, 256, 256), (64, 96, 1024), (255, 257, 255), (1, 500, 300), (500, 1, 300),
+                      (33, 31, 17), (32, 32, 16), (200, 300, 64), (100, 100, 10000), (448, 480, 97)]
+
+
+@pytest.mark.parametrize("shape", SPLITK_TINY_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK_TINY_SHAPES])
+def test_f32_splitk_32x32_tiles(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=1.5, beta=-0.5, seed=M + 3 * N + K)
+    announce(f"f32 split-K 32x32 {shape}")
+    got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
+    name = rt.last_kernel()
+    assert name.startswith("f32_regtile_splitk4_32x32x16_4x4"), name
+    assert name.endswith("_guard") == (M % 32 != 0 or N % 32 != 0 or K % 16 != 0), name
+    assert_parity_full(inp, got, f"f32 split-K 32x32 {shape} ({name})")
+
+
 def test_f32_auto_picks_by_tile_count():
-    # square kernel from 384 tiles of 128x256; split-K below that for a long enough K;
-    # otherwise the small-tile kernel
+    # square kernel from 384 tiles of 128x256; split-K below that for a long enough K, or on
+    # 32x32 tiles for fewer than 64 tiles of 64x64 and K >= 64; otherwise the small-tile kernel
     cases = [((4096, 3072, 64), "f32_regtile_128x256x16_8x16"), ((4096, 2048, 2048), "f32_regtile_splitk8"),
              ((4096, 2048, 1024), "f32_regtile_splitk4"),
              ((1000, 1500, 777), "f32_regtile_splitk8"), ((1024, 1024, 1024), "f32_regtile_splitk4"),
-             ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_64x64x32_4x4")]
+             ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_64x64x32_4x4"),
+             ((256, 256, 256), "f32_regtile_splitk4_32x32x16_4x4"), ((500, 400, 64), "f32_regtile_splitk4_32x32"),
+             ((256, 256, 48), "f32_regtile_64x64x32_4x4"), ((512, 512, 63), "f32_regtile_64x64x32_4x4"),
+             ((512, 512, 256), "f32_regtile_64x64x32_4x4")]
     for (M, N, K), prefix in cases:
         A = torch.zeros((M, K), device="cuda")
         B = torch.zeros((K, N), device="cuda")
