@@ -46,6 +46,11 @@ namespace {
 #ifndef F32_EARLY_STORE
 #define F32_EARLY_STORE 1
 #endif
+// 1: the FMAs of a k step walk the micro-tile row by row in alternating column order
+// (consecutive FMAs always share a source register); 0: row by row, left to right
+#ifndef F32_SNAKE
+#define F32_SNAKE 0
+#endif
 #ifndef F32_WAVES_PER_EU
 #define F32_WAVES_PER_EU 2
 #endif
@@ -273,7 +278,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES, 
 #pragma unroll
             for (int m = 0; m < TM; ++m)
 #pragma unroll
-                for (int n = 0; n < TN; ++n) acc[m][n] = fmaf(ra_[m], rb_[n], acc[m][n]);
+                for (int nn = 0; nn < TN; ++nn) {
+                    const int n = (F32_SNAKE && (m & 1)) ? TN - 1 - nn : nn;
+                    acc[m][n] = fmaf(ra_[m], rb_[n], acc[m][n]);
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
