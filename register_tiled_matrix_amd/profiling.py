@@ -14,6 +14,8 @@ stops at the first pass that fails. The passes:
              1 GiB device copy (the calibration: bytes moved / counter bytes);
   sq_*       LDS, VALU and MFMA instruction and cycle counters per kernel;
   state_*    where the waves' time goes (VALU / LDS / VMEM issue, waiting) per kernel;
+  clock_*    the shader clock and the MFMA busy share per dispatch of the fp32 4096^3 and bf16
+             8192^3 kernels in the benchmark's own launch sequence;
   clock_datadep  the shader clock and MFMA busy share of the bf16 kernel on six input data
              sets (tune datadep).
 
@@ -48,6 +50,8 @@ COPY_BYTES = 1 << 30
 # the shader clock and the MFMA pipes' busy share per dispatch, for the same bf16 kernel on
 # different input data (tune datadep)
 CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES"
+CLOCK_WORKLOADS = ["f32_4096", "bf16_8192"]
+CLOCK_STEPS, CLOCK_WARMUP = 20, 30
 DD_STEPS, DD_ROUNDS, DD_WARMUP = 10, 2, 20
 N_XCD, N_SIMD = 8, 1024
 
@@ -95,6 +99,11 @@ def passes(out):
         p.append((f"state_{w}", ["rocprofv3", "--pmc", *STATE_COUNTERS.split(), "-d", os.path.join(out, f"state_{w}"),
                                  "-o", "st", "--output-format", "csv", "--",
                                  *_bench_cmd("--only", w, "--steps", "3", "--warmup", "1")], 120))
+    for w in CLOCK_WORKLOADS:
+        p.append((f"clock_{w}", ["rocprofv3", "--kernel-trace", "--pmc", *CLOCK_COUNTERS.split(), "-d",
+                                 os.path.join(out, f"clock_{w}"), "-o", "clk", "--output-format", "csv", "--",
+                                 *_bench_cmd("--only", w, "--steps", str(CLOCK_STEPS), "--warmup", str(CLOCK_WARMUP))],
+                  180))
     p.append(("clock_datadep", ["rocprofv3", "--kernel-trace", "--pmc", *CLOCK_COUNTERS.split(), "-d",
                                  os.path.join(out, "clock_datadep"), "-o", "clk", "--output-format", "csv", "--",
                                  "python3", "-m", "register_tiled_matrix_amd.tune", "datadep",
@@ -439,6 +448,52 @@ def summarize_datadep(prof, out_md):
         f.write("\n".join(md) + "\n")
 
 
+def summarize_clock(prof, out_md):
+    """Shader clock, MFMA busy share and (fp32) SIMD cycles per wave64 FMA of the benchmarked
+    fp32 4096^3 and bf16 8192^3 kernels, per dispatch of `bench.py --only <workload>` (its
+    CLOCK_WARMUP warm-up launches, then CLOCK_STEPS timed ones)."""
+    import gemm_inputs as gi
+
+    md = ["# Shader clock, MFMA busy share and FMA issue rate inside the benchmarked kernels "
+          "(rocprofv3 --pmc, GRBM and SQ cycles)", ""]
+    md += _cmd_block([_display(a, prof) for n, a, _ in passes(prof) if n.startswith("clock_") and n != "clock_datadep"])
+    md += ["Per dispatch: the duration from the kernel trace; shader cycles = GRBM_GUI_ACTIVE / 8 XCDs; "
+           "clock = those cycles / the duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / those "
+           "cycles; for the fp32 kernel, SIMD cycles per wave64 FMA = those cycles / (M N K / 64 lanes / 1024 "
+           "SIMDs). Medians over the timed launches (the last "
+           f"{CLOCK_STEPS}); the counters serialise the dispatches, so durations run a little longer than "
+           "in the benchmark.", "",
+           "| workload | kernel | dispatches | duration (ms) | shader cycles per XCD (M) | clock (GHz) | "
+           "MFMA busy | SIMD cycles per wave64 FMA | TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for w in CLOCK_WORKLOADS:
+        d = os.path.join(prof, f"clock_{w}")
+        label, sub = KERNELS[w][0], KERNELS[w][1]
+        per = collections.OrderedDict()
+        for r in csv.DictReader(open(os.path.join(d, "clk_counter_collection.csv"))):
+            if sub in r["Kernel_Name"]:
+                per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        dur = {}
+        for r in csv.DictReader(open(os.path.join(d, "clk_kernel_trace.csv"))):
+            if sub in r["Kernel_Name"]:
+                dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        ids = sorted(i for i in per if i in dur)[-CLOCK_STEPS:]
+        wl = gi.WORKLOADS[w]
+        rows = []
+        for i in ids:
+            cyc = per[i]["GRBM_GUI_ACTIVE"] / N_XCD
+            t = dur[i]
+            mfma = per[i].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / N_SIMD / cyc
+            fma = cyc / (wl.M * wl.N * wl.K / 64 / N_SIMD) if wl.dtype == "f32" else None
+            rows.append((t, cyc, cyc / t / 1e9, mfma, fma, wl.flop / t / 1e12))
+        med = [statistics.median(r[j] for r in rows) if rows[0][j] is not None else None for j in range(6)]
+        md.append(f"| {w} | `{label}` | {len(rows)} | {med[0] * 1e3:.4f} | {med[1] / 1e6:.3f} | {med[2]:.2f} | "
+                  + (f"{100 * med[3]:.0f} %" if wl.dtype != "f32" else "-") + " | "
+                  + (f"{med[4]:.2f}" if med[4] is not None else "-") + f" | {med[5]:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(prof) -> int:
     prof = os.path.abspath(prof)
     for w in TRACE_WORKLOADS:
@@ -450,6 +505,8 @@ def summarize(prof) -> int:
     if os.path.exists(os.path.join(prof, "sq_f32_4096")):
         summarize_sq(prof, os.path.join(PROFILES, "sq_counters_bench_kernels.md"),
                      os.path.join(PROFILES, "sq_counters_bench_kernels.json"))
+    if all(os.path.exists(os.path.join(prof, f"clock_{w}", "clk_counter_collection.csv")) for w in CLOCK_WORKLOADS):
+        summarize_clock(prof, os.path.join(PROFILES, "clock_f32_4096_bf16_8192.md"))
     if os.path.exists(os.path.join(prof, "clock_datadep", "clk_counter_collection.csv")):
         summarize_datadep(prof, os.path.join(PROFILES, "clock_datadep_bf16_8192.md"))
     if os.path.exists(os.path.join(prof, "sq_ladder", "sq_counter_collection.csv")):
