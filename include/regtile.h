@@ -57,8 +57,9 @@ enum regtile_algo_f32 {
     REGTILE_F32_LDS = 2,     /* 32x32 LDS tiles, 1024 threads, one C element per thread */
     REGTILE_F32_REGTILE = 3, /* 128x256 LDS tiles, 256 threads, 8x16 register micro-tiles */
     REGTILE_F32_SPLITK = 4,  /* K split over the waves of a workgroup, partials summed in a
-                                fixed order (shapes with few tiles): 64x128 tiles of 8 waves
-                                with 8x16 micro-tiles, or 64x64 tiles of 4 waves with 8x8 */
+                                fixed order (shapes with few tiles): 64x128 (or 64x96) tiles
+                                of 8 waves with 8x16 (8x12) micro-tiles, 64x64 tiles of 8 or 4
+                                waves with 8x8, or 32x32 tiles of 4 waves with 4x4 */
     REGTILE_F32_REGTILE_SMALL = 5 /* 64x64 tiles, 256 threads, 4x4 register micro-tiles, 4 waves
                                      per SIMD (shapes with few 128x256 tiles) */
 };
@@ -78,8 +79,9 @@ enum regtile_algo_bf16 {
  * kernel ("Understanding Register Tiling", the key loop; "寄存器Tiling跨架构解析" section 1.1):
  * 128x256 workgroup tiles of 8x16 micro-tiles. Problems with fewer than 384 such tiles (1.5
  * per CU) take smaller tiles (section 2.4 / 7.2 of the second page: tile size against resident
- * waves): with K >= 1024, or K >= 384 and fewer than four 64x64 tiles per CU, the split-K
- * kernel (K split over the waves of a workgroup, 64x128 tiles of 8x16 or 64x64 tiles of 8x8
+ * waves): with K >= 1024, K >= 384 and fewer than four 64x64 tiles per CU, K >= 128 and fewer
+ * than 448 such tiles, or K >= 64 and fewer than 64 of them, the split-K kernel (K split over
+ * the waves of a workgroup, 64x128 tiles of 8x16, 64x64 tiles of 8x8 or 32x32 tiles of 4x4
  * micro-tiles, partials summed in a fixed order); otherwise 64x64 tiles of 4x4 micro-tiles at 4
  * waves per SIMD. Every kernel but split-K sums k in natural order, so its results equal the
  * naive rung bitwise; split-K's are deterministic but summed in another order.

@@ -6,9 +6,11 @@
 // tile over its own share of K, with the register micro-tile of the square kernel
 // ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA / regB per
 // k, TM x TN FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
-// tile size against the number of resident waves). Four shapes:
+// tile size against the number of resident waves). Five shapes:
 //   * 32x32 tile, 4 waves, 4x4 micro-tiles, BK 16 (splitk4, problems of fewer than 64 tiles
 //     of 64x64);
+//   * 64x64 tile, 8 waves, 8x8 micro-tiles, BK 16 (splitk8, below 448 such tiles: two waves
+//     per SIMD where the 4-wave form would leave one);
 //   * 64x64 tile, 4 waves, 8x8 micro-tiles, BK 16 (splitk4);
 //   * 64x128 tile, 8 waves, 8x16 micro-tiles (the square kernel's), BK 8 (splitk8): one
 //     workgroup of two waves per SIMD per CU, and three quarters of the LDS reads per FMA of
@@ -88,6 +90,7 @@ struct SplitCfg {
 };
 using Split4 = SplitCfg<4, 8, 8, 16>;
 using Split4t = SplitCfg<4, 4, 4, 16>;  // 32x32 tiles for problems of a few 64x64 tiles
+using Split8s = SplitCfg<8, 8, 8, 16>;  // 64x64 tiles, 8 waves: two waves per SIMD on one tile per CU
 using Split8 = SplitCfg<8, 8, 16, 8>;
 using Split8n96 = SplitCfg<8, 8, 12, SPLIT96_BK, SPLIT96_DEPTH, SPLIT96_APAD>;  // 64x96 tiles: 1000 x 1500 is 256 of them
 
@@ -489,6 +492,12 @@ hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name)
         return launch_cfg<Split8>(p, s, name, "f32_regtile_splitk8_64x128x8_8x16",
                                   "f32_regtile_splitk8_64x128x8_8x16_guard");
     }
+    // Below 448 tiles of 64x64 the 4-wave kernel leaves most CUs with one workgroup, one wave
+    // per SIMD; eight waves per 64x64 tile restore two (1024^3: 47.9 -> 68.9 TFLOP/s,
+    // 1024x1024x8192: 59.6 -> 89.7, 768x768x4096: 33.3 -> 55.6 in same-box A/B runs).
+    if (t64 < 448)
+        return launch_cfg<Split8s>(p, s, name, "f32_regtile_splitk8_64x64x16_8x8",
+                                   "f32_regtile_splitk8_64x64x16_8x8_guard");
     return launch_cfg<Split4>(p, s, name, "f32_regtile_splitk4_64x64x16_8x8",
                               "f32_regtile_splitk4_64x64x16_8x8_guard");
 }

@@ -103,13 +103,15 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
         // operands once K is long enough to pay for its reduction (K >= 1024, or K >= 384
         // while fewer than four 64x64 tiles per CU leave the small-tile kernel under-filled),
         // otherwise 64x64 tiles of 4x4 micro-tiles at 4 waves per SIMD (bitwise equal to the
-        // naive rung). Measured on 30 shapes with 64 <= K <= 8192. Problems of fewer than 64
-        // such tiles (a quarter of the CUs) take split-K on 32x32 tiles once K >= 64.
+        // naive rung). Measured on 30 shapes with 64 <= K <= 8192. Problems of fewer than 448
+        // such tiles take split-K from K >= 128 (eight waves on each 64x64 tile, or 32x32 tiles
+        // below 64 of them from K >= 64): at 1024x1024x256 40.3 against 30.5 TFLOP/s.
         const int64_t sq = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
         const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
         if (sq >= 384)
             algo = REGTILE_F32_REGTILE;
-        else if (!ta && !tb && (K >= 1024 || (tiles64 < 4 * 256 && K >= 384) || (tiles64 < 64 && K >= 64)))
+        else if (!ta && !tb && (K >= 1024 || (tiles64 < 4 * 256 && K >= 384) || (tiles64 < 448 && K >= 128) ||
+                                (tiles64 < 64 && K >= 64)))
             algo = REGTILE_F32_SPLITK;
         else
             algo = REGTILE_F32_REGTILE_SMALL;

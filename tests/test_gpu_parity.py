@@ -190,6 +190,25 @@ SPLITK_TINY_SHAPES = [(256, 256, 256), (64, 96, 1024), (255, 257, 255), (1, 500,
                       (33, 31, 17), (32, 32, 16), (200, 300, 64), (100, 100, 10000), (448, 480, 97)]
 
 
+# Split-K with eight waves on each 64x64 tile (8x8 micro-tiles), taken for 64 to 447 tiles of
+# 64x64 when fewer than 192 tiles of 64x128 exist: whole tiles and slabs, ragged M, N and K, a
+# K below eight slabs, and a long K.
+SPLITK8_64_SHAPES = [(1024, 1024, 1024), (512, 512, 4096), (1000, 1000, 3000), (900, 700, 1500),
+                     (1024, 768, 100), (513, 511, 257), (768, 768, 8192)]
+
+
+@pytest.mark.parametrize("shape", SPLITK8_64_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK8_64_SHAPES])
+def test_f32_splitk8_64x64_tiles(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=1.5, beta=-0.5, seed=M + 5 * N + K)
+    announce(f"f32 split-K 8 waves 64x64 {shape}")
+    got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
+    name = rt.last_kernel()
+    assert name.startswith("f32_regtile_splitk8_64x64x16_8x8"), name
+    assert name.endswith("_guard") == (M % 64 != 0 or N % 64 != 0 or K % 16 != 0), name
+    assert_parity_full(inp, got, f"f32 split-K 8 waves 64x64 {shape} ({name})")
+
+
 @pytest.mark.parametrize("shape", SPLITK_TINY_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK_TINY_SHAPES])
 def test_f32_splitk_32x32_tiles(shape):
     M, N, K = shape
@@ -203,15 +222,18 @@ def test_f32_splitk_32x32_tiles(shape):
 
 
 def test_f32_auto_picks_by_tile_count():
-    # square kernel from 384 tiles of 128x256; split-K below that for a long enough K, or on
-    # 32x32 tiles for fewer than 64 tiles of 64x64 and K >= 64; otherwise the small-tile kernel
+    # square kernel from 384 tiles of 128x256; split-K below that for a long enough K (eight
+    # waves per 64x64 tile below 448 of them from K >= 128, 32x32 tiles below 64 of them from
+    # K >= 64); otherwise the small-tile kernel
     cases = [((4096, 3072, 64), "f32_regtile_128x256x16_8x16"), ((4096, 2048, 2048), "f32_regtile_splitk8"),
              ((4096, 2048, 1024), "f32_regtile_splitk4"),
-             ((1000, 1500, 777), "f32_regtile_splitk8"), ((1024, 1024, 1024), "f32_regtile_splitk4"),
-             ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_64x64x32_4x4"),
+             ((1000, 1500, 777), "f32_regtile_splitk8"), ((1024, 1024, 1024), "f32_regtile_splitk8_64x64x16_8x8"),
+             ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_splitk8_64x96"),
+             ((1000, 1500, 100), "f32_regtile_64x64x32_4x4"), ((1024, 1024, 128), "f32_regtile_splitk8_64x64"),
+             ((1280, 1792, 256), "f32_regtile_64x64x32_4x4"),
              ((256, 256, 256), "f32_regtile_splitk4_32x32x16_4x4"), ((500, 400, 64), "f32_regtile_splitk4_32x32"),
              ((256, 256, 48), "f32_regtile_64x64x32_4x4"), ((512, 512, 63), "f32_regtile_64x64x32_4x4"),
-             ((512, 512, 256), "f32_regtile_64x64x32_4x4")]
+             ((512, 512, 256), "f32_regtile_splitk8_64x64x16_8x8")]
     for (M, N, K), prefix in cases:
         A = torch.zeros((M, K), device="cuda")
         B = torch.zeros((K, N), device="cuda")
@@ -551,8 +573,9 @@ def test_f32_strided_views_every_register_tiled_kernel():
         assert torch.count_nonzero(big_c[:, N + 1:]).item() == 0
 
 
-@pytest.mark.parametrize("shape,prefix", [((4096, 192, 2000), "f32_regtile_splitk4"),
-                                          ((13000, 130, 2000), "f32_regtile_splitk8")])
+@pytest.mark.parametrize("shape,prefix", [((16384, 128, 1024), "f32_regtile_splitk4_64x64"),
+                                          ((4096, 192, 2000), "f32_regtile_splitk8_64x64"),
+                                          ((13000, 130, 2000), "f32_regtile_splitk8_64x96")])
 def test_splitk_is_deterministic_and_matches_oracle_at_tall_shape(shape, prefix):
     inp = gi.make_inputs(*shape, dist="uniform", seed=12)
     announce(f"splitk determinism {shape}")
