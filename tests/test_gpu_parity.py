@@ -209,6 +209,23 @@ def test_f32_splitk8_64x64_tiles(shape):
     assert_parity_full(inp, got, f"f32 split-K 8 waves 64x64 {shape} ({name})")
 
 
+# Split-K with four waves on each 64x64 tile (8x8 micro-tiles): 448 or more such tiles (two
+# workgroups per CU) with K below 1280. Whole tiles and slabs, and ragged M, N and K.
+SPLITK4_64_SHAPES = [(2048, 1024, 1024), (1500, 1300, 700), (1409, 1313, 129)]
+
+
+@pytest.mark.parametrize("shape", SPLITK4_64_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK4_64_SHAPES])
+def test_f32_splitk4_64x64_tiles(shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype="f32", dist="normal", alpha=-0.75, beta=1.25, seed=M + 7 * N + K)
+    announce(f"f32 split-K 4 waves 64x64 {shape}")
+    got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
+    name = rt.last_kernel()
+    assert name.startswith("f32_regtile_splitk4_64x64x16_8x8"), name
+    assert name.endswith("_guard") == (M % 64 != 0 or N % 64 != 0 or K % 16 != 0), name
+    assert_parity_full(inp, got, f"f32 split-K 4 waves 64x64 {shape} ({name})")
+
+
 @pytest.mark.parametrize("shape", SPLITK_TINY_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLITK_TINY_SHAPES])
 def test_f32_splitk_32x32_tiles(shape):
     M, N, K = shape
@@ -449,7 +466,9 @@ def test_beta_zero_never_reads_c(dtype):
 
 F32_EPILOGUE_CASES = [(rt.ALGO_F32_REGTILE, (200, 300, 64), "f32_regtile_128x256"),
                       (rt.ALGO_F32_REGTILE_SMALL, (200, 300, 64), "f32_regtile_64x64x32"),
-                      (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk4"),
+                      (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk4_32x32"),
+                      (rt.ALGO_F32_SPLITK, (1024, 768, 100), "f32_regtile_splitk8_64x64"),
+                      (rt.ALGO_F32_SPLITK, (1500, 1300, 300), "f32_regtile_splitk4_64x64"),
                       (rt.ALGO_F32_SPLITK, (13000, 50, 37), "f32_regtile_splitk8"),
                       (rt.ALGO_F32_SPLITK, (12800, 128, 512), "f32_regtile_splitk8")]
 
