@@ -59,7 +59,7 @@ enum regtile_algo_f32 {
     REGTILE_F32_SPLITK = 4,  /* K split over the waves of a workgroup, partials summed in a
                                 fixed order (shapes with few tiles): 64x128 (or 64x96) tiles
                                 of 8 waves with 8x16 (8x12) micro-tiles, 64x64 tiles of 8 or 4
-                                waves with 8x8, or 32x32 tiles of 4 waves with 4x4 */
+                                waves with 8x8, or 32x32 tiles of 8 waves with 4x4 */
     REGTILE_F32_REGTILE_SMALL = 5 /* 64x64 tiles, 256 threads, 4x4 register micro-tiles, 4 waves
                                      per SIMD (shapes with few 128x256 tiles) */
 };

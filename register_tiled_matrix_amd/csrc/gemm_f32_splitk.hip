@@ -7,8 +7,8 @@
 // ("Understanding Register Tiling" (blog.csdn.net/sweet_ran), the key loop: regA / regB per
 // k, TM x TN FMAs per k held in registers; "寄存器Tiling跨架构解析" section 2.4 / 7.2: trade
 // tile size against the number of resident waves). Five shapes:
-//   * 32x32 tile, 4 waves, 4x4 micro-tiles, BK 16 (splitk4, problems of fewer than 64 tiles
-//     of 64x64);
+//   * 32x32 tile, 8 waves, 4x4 micro-tiles, BK 16 (splitk8, problems of fewer than 64 tiles
+//     of 64x64; the first 256 threads run the epilogue);
 //   * 64x64 tile, 8 waves, 8x8 micro-tiles, BK 16 (splitk8, below 448 such tiles: two waves
 //     per SIMD where the 4-wave form would leave one);
 //   * 64x64 tile, 4 waves, 8x8 micro-tiles, BK 16 (splitk4);
@@ -70,7 +70,10 @@ struct SplitCfg {
     static constexpr int NA4 = TILE_M * BK / 256;           // A float4 per lane per slab
     static constexpr int NB4 = BK * TILE_N / 256;           // B float4 per lane per slab
     static constexpr int NPART = NW < 4 ? NW : 4;           // partial tiles held in LDS at once
-    static constexpr int SW = TILE_M * TILE_N / NT;         // epilogue columns per thread
+    // epilogue columns per thread (at least one float4: with more threads than float4 of the
+    // tile, only the first ET threads run the epilogue)
+    static constexpr int SW = TILE_M * TILE_N / NT < 4 ? 4 : TILE_M * TILE_N / NT;
+    static constexpr int ET = TILE_M * TILE_N / SW;         // threads that run the epilogue
     static_assert((TM == 4 || TM == 8) && (TN == 4 || TN == 8 || TN == 12 || TN == 16),
                   "micro-tile rows in one or two groups of 4");
     static_assert(SW % 4 == 0 && TILE_N % SW == 0, "whole float4 strips in the epilogue");
@@ -89,7 +92,7 @@ struct SplitCfg {
     };
 };
 using Split4 = SplitCfg<4, 8, 8, 16>;
-using Split4t = SplitCfg<4, 4, 4, 16>;  // 32x32 tiles for problems of a few 64x64 tiles
+using Split8t = SplitCfg<8, 4, 4, 16>;  // 32x32 tiles for problems of a few 64x64 tiles
 using Split8s = SplitCfg<8, 8, 8, 16>;  // 64x64 tiles, 8 waves: two waves per SIMD on one tile per CU
 using Split8 = SplitCfg<8, 8, 16, 8>;
 using Split8n96 = SplitCfg<8, 8, 12, SPLIT96_BK, SPLIT96_DEPTH, SPLIT96_APAD>;  // 64x96 tiles: 1000 x 1500 is 256 of them
@@ -316,12 +319,13 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // The epilogue's strip of C (beta != 0) is read now, so its latency overlaps the reduction
     // below rather than following it: thread t owns row t / (TILE_N / SW), columns
     // (t % (TILE_N / SW)) * SW .. +SW-1 (SW = 16, or 12 for 96-column tiles).
-    constexpr int SW = CFG::SW, TPR = TILE_N / SW;  // strip width, threads per row
-    static_assert(NT == TILE_M * TPR, "one strip per thread");
-    const int row = tid / TPR, col0 = (tid % TPR) * SW;
+    constexpr int SW = CFG::SW, TPR = TILE_N / SW, ET = CFG::ET;  // strip width, threads per row
+    static_assert(ET == TILE_M * TPR && ET <= NT, "one strip per epilogue thread");
+    const bool epi = ET == NT || tid < ET;
+    const int row = (epi ? tid : 0) / TPR, col0 = (tid % TPR) * SW;
     const int grow = m0 + row;
     float4 cold[SW / 4];
-    if (beta != 0.0f && (!GUARD || grow < M)) {
+    if (epi && beta != 0.0f && (!GUARD || grow < M)) {
         const float *crow_in = C + (int64_t)grow * ldc + n0 + col0;
 #pragma unroll
         for (int c4 = 0; c4 < SW / 4; ++c4) {
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __syncthreads();
 
     // Fixed-order sum of the NPART partials and epilogue on the strip read above.
-    if (GUARD && grow >= M) return;
+    if (!epi || (GUARD && grow >= M)) return;
     float *crow = C + (int64_t)grow * ldc;
 #pragma unroll
     for (int c4 = 0; c4 < SW / 4; ++c4) {
@@ -474,11 +478,12 @@ static bool split8_prefers_96(int M, int N) {
 
 hipError_t launch_f32_splitk(const Problem &p, hipStream_t s, const char **name) {
     // Fewer than 64 tiles of 64x64 (a quarter of the CUs): 32x32 tiles of 4x4 micro-tiles, so
-    // that four times as many workgroups share the work (256^3: 64 workgroups, each wave
-    // 1024 FMAs per lane against 4096 on a 64x64 tile).
+    // that four times as many workgroups share the work, each split over eight waves (256^3:
+    // 64 workgroups, each wave 512 FMAs per lane against 4096 on a 64x64 tile; 6.8 us against
+    // 7.7 with four waves per tile and 15.7 on 64x64 tiles).
     if (tiles_64(p) < 64)
-        return launch_cfg<Split4t>(p, s, name, "f32_regtile_splitk4_32x32x16_4x4",
-                                   "f32_regtile_splitk4_32x32x16_4x4_guard");
+        return launch_cfg<Split8t>(p, s, name, "f32_regtile_splitk8_32x32x16_4x4",
+                                   "f32_regtile_splitk8_32x32x16_4x4_guard");
     // 8 waves x 8x16 once 64x128 tiles give most CUs a workgroup (two waves per SIMD), unless
     // the 4-wave kernel's 64x64 tiles already fill the chip and K is short enough that the
     // 8-wave kernel's longer reduction does not pay (measured on 13 row-major shapes with

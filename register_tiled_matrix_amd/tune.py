@@ -196,7 +196,7 @@ F32_RUNGS = [("naive", 1, "naive_kernelIfLb0ELb0E"), ("lds_32x32", 2, "f32_lds_k
              ("regtile_8x16", 3, "SquareCfgELb0ELb0E"), ("regtile_small_4x4", 5, "SmallCfgELb0ELb0E"),
              ("splitk", 4, {"splitk8_64x128": "SplitCfgILi8ELi8ELi16ELi8E", "splitk8_64x96": "SplitCfgILi8ELi8ELi12E",
                             "splitk8_64x64": "SplitCfgILi8ELi8ELi8ELi16E", "splitk4_64x64": "SplitCfgILi4ELi8ELi8ELi16E",
-                            "splitk4_32x32": "SplitCfgILi4ELi4ELi4ELi16E"})]
+                            "splitk8_32x32": "SplitCfgILi8ELi4ELi4ELi16E"})]
 R16_RUNGS = [("naive", 1, "naive_kernelI{T}Lb0ELb1E"), ("mfma_32x32x16", 2, "ELi32ELi1ELi1ELb{F}E"),
              ("mfma_16x16x32", 3, "ELi16ELi1ELi0ELb{F}E")]
 

@@ -183,7 +183,7 @@ def test_f32_splitk8_edges(shape):
     assert_parity_full(inp, got, f"f32 split-K {shape} ({name})")
 
 
-# Split-K on 32x32 tiles (4 waves, 4x4 micro-tiles), taken for fewer than 64 tiles of 64x64:
+# Split-K on 32x32 tiles (8 waves, 4x4 micro-tiles), taken for fewer than 64 tiles of 64x64:
 # exact multiples of the tile and of BK 16 (no bounds checks), ragged M, N and K, K below one
 # slab per wave, one row or column, and a long K.
 SPLITK_TINY_SHAPES = [(256, 256, 256), (64, 96, 1024), (255, 257, 255), (1, 500, 300), (500, 1, 300),
@@ -233,7 +233,7 @@ def test_f32_splitk_32x32_tiles(shape):
     announce(f"f32 split-K 32x32 {shape}")
     got = run(inp, torch, rt.ALGO_F32_SPLITK).cpu().numpy()
     name = rt.last_kernel()
-    assert name.startswith("f32_regtile_splitk4_32x32x16_4x4"), name
+    assert name.startswith("f32_regtile_splitk8_32x32x16_4x4"), name
     assert name.endswith("_guard") == (M % 32 != 0 or N % 32 != 0 or K % 16 != 0), name
     assert_parity_full(inp, got, f"f32 split-K 32x32 {shape} ({name})")
 
@@ -248,7 +248,7 @@ def test_f32_auto_picks_by_tile_count():
              ((3000, 2000, 512), "f32_regtile_64x64x32_4x4"), ((1000, 1500, 300), "f32_regtile_splitk8_64x96"),
              ((1000, 1500, 100), "f32_regtile_64x64x32_4x4"), ((1024, 1024, 128), "f32_regtile_splitk8_64x64"),
              ((1280, 1792, 256), "f32_regtile_64x64x32_4x4"),
-             ((256, 256, 256), "f32_regtile_splitk4_32x32x16_4x4"), ((500, 400, 64), "f32_regtile_splitk4_32x32"),
+             ((256, 256, 256), "f32_regtile_splitk8_32x32x16_4x4"), ((500, 400, 64), "f32_regtile_splitk8_32x32"),
              ((256, 256, 48), "f32_regtile_64x64x32_4x4"), ((512, 512, 63), "f32_regtile_64x64x32_4x4"),
              ((512, 512, 256), "f32_regtile_splitk8_64x64x16_8x8")]
     for (M, N, K), prefix in cases:
@@ -466,7 +466,7 @@ def test_beta_zero_never_reads_c(dtype):
 
 F32_EPILOGUE_CASES = [(rt.ALGO_F32_REGTILE, (200, 300, 64), "f32_regtile_128x256"),
                       (rt.ALGO_F32_REGTILE_SMALL, (200, 300, 64), "f32_regtile_64x64x32"),
-                      (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk4_32x32"),
+                      (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk8_32x32"),
                       (rt.ALGO_F32_SPLITK, (1024, 768, 100), "f32_regtile_splitk8_64x64"),
                       (rt.ALGO_F32_SPLITK, (1500, 1300, 300), "f32_regtile_splitk4_64x64"),
                       (rt.ALGO_F32_SPLITK, (13000, 50, 37), "f32_regtile_splitk8"),

@@ -50,7 +50,7 @@ DETERMINISM = [
     ("f32", (4096, 4096, 4096), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_128x256x16_8x16"),
     ("f32", (16384, 128, 4096), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x128x8_8x16"),
     ("f32", (1000, 1500, 777), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x96x8_8x12"),
-    ("f32", (256, 256, 256), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk4_32x32x16_4x4"),
+    ("f32", (256, 256, 256), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_32x32x16_4x4"),
     ("f32", (1024, 1024, 1024), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x64x16_8x8"),
 ]
 
