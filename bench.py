@@ -145,6 +145,33 @@ def _steady_median(torch, step, with_region=False):
     return float(np.median(kern)), e0.elapsed_time(e1) / 30
 
 
+def _graph_ms_per_launch(torch, raw, call, rt, launches=20, replays=25):
+    """Time per launch of `launches` identical calls captured in one HIP graph and replayed
+    `replays` times inside one event pair (after warm-up replays). The library launches on the
+    stream it is given and makes no allocation or synchronisation, so the calls capture as
+    they are; the graph removes the host's per-launch cost, which dominates kernels of a few
+    microseconds."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream().cuda_stream
+        for _ in range(launches):
+            st = raw(*call[:-1], cap)
+            if st:
+                raise rt.RegtileError(st, rt.strerror(st))
+    for _ in range(10):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * launches)
+    del graph
+    return ms
+
+
 def _kernel_info(rt):
     """Resources of the kernel launched last, as the HIP runtime reports them."""
     try:
@@ -194,6 +221,12 @@ def _configs(torch, gi, rt, acc, dev, stream, with_16bit, with_cpu):
                       "back_to_back_ms_per_launch": round(region, 4),
                       "TFLOP/s_back_to_back": round(tf_b2b, 3), "frac_back_to_back": round(tf_b2b / peak, 4),
                       "kernel_resources": info, "counters": _sq_record(kname), "traffic": _traffic(kname)}
+        if med < 0.1:  # launch-bound: also as launches replayed from a captured HIP graph
+            gms = _graph_ms_per_launch(torch, raw, call, rt)
+            tf_g = wc.flop / (gms * 1e-3) / 1e12
+            res[wname].update({"graph_ms_per_launch": round(gms, 4), "TFLOP/s_graph": round(tf_g, 3),
+                               "frac_graph": round(tf_g / peak, 4),
+                               "graph_basis": "20 launches captured in one HIP graph, 25 replays in one event pair"})
         if with_cpu and wname != "f32_8192":  # the five configurations; 8192^3 fp32 is extra
             if ic.C is not None:
                 C.copy_(torch.from_numpy(ic.C).to(dev))
