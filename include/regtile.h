@@ -69,9 +69,14 @@ enum regtile_algo_bf16 {
     REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
     REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
     REGTILE_BF16_MFMA = 2,   /* LDS-tiled, wave-level 32x32x16 MFMA fragments, fp32 accumulators */
-    REGTILE_BF16_MFMA_16X16 = 3 /* the same with 16x16x32 fragments where the LDS-DMA kernel
-                                   runs 256x256 tiles (other problems as REGTILE_BF16_MFMA):
-                                   the shape comparison ("寄存器Tiling跨架构解析" section 3.1) */
+    REGTILE_BF16_MFMA_16X16 = 3, /* the same with 16x16x32 fragments where the LDS-DMA kernel
+                                    runs 256x256 tiles (other problems as REGTILE_BF16_MFMA):
+                                    the shape comparison ("寄存器Tiling跨架构解析" section 3.1) */
+    REGTILE_BF16_MFMA_SPLITK = 4 /* K split over the 4 waves of a workgroup on 64x64 tiles,
+                                    32x32x16 fragments, partials summed in a fixed order (for
+                                    problems with few tiles; "寄存器Tiling跨架构解析" sections 2.4
+                                    and 7.2). K-contiguous A and B with 16-byte aligned rows and
+                                    K a multiple of 8; other problems as REGTILE_BF16_MFMA */
 };
 
 /*

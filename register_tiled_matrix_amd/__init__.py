@@ -33,7 +33,7 @@ import threading
 __all__ = [
     "ALGO_F32_AUTO", "ALGO_F32_NAIVE", "ALGO_F32_LDS", "ALGO_F32_REGTILE", "ALGO_F32_SPLITK",
     "ALGO_F32_REGTILE_SMALL",
-    "ALGO_BF16_AUTO", "ALGO_BF16_NAIVE", "ALGO_BF16_MFMA", "ALGO_BF16_MFMA_16X16",
+    "ALGO_BF16_AUTO", "ALGO_BF16_NAIVE", "ALGO_BF16_MFMA", "ALGO_BF16_MFMA_16X16", "ALGO_BF16_MFMA_SPLITK",
     "RegtileError", "RegtileLibraryMissing", "lib_path", "load",
     "gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_raw", "gemm_bf16_raw", "gemm_f16_raw",
     "regtile_gemm_f32_algo", "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo",
@@ -43,7 +43,7 @@ __all__ = [
 
 ALGO_F32_AUTO, ALGO_F32_NAIVE, ALGO_F32_LDS, ALGO_F32_REGTILE, ALGO_F32_SPLITK = 0, 1, 2, 3, 4
 ALGO_F32_REGTILE_SMALL = 5
-ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA, ALGO_BF16_MFMA_16X16 = 0, 1, 2, 3
+ALGO_BF16_AUTO, ALGO_BF16_NAIVE, ALGO_BF16_MFMA, ALGO_BF16_MFMA_16X16, ALGO_BF16_MFMA_SPLITK = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("gemm_f32", "gemm_bf16", "gemm_f16", "regtile_gemm_f32_algo",
                     "regtile_gemm_bf16_algo", "regtile_gemm_f16_algo", "regtile_gemm_f32_ex",

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libregtile.so")
 ARCH = "gfx950"
 
 SOURCES = ["regtile_api.hip", "gemm_simple.hip", "gemm_f32_regtile.hip", "gemm_f32_splitk.hip",
-           "gemm_bf16_mfma.hip", "gemm_bf16_mfma_dma.hip"]
+           "gemm_bf16_mfma.hip", "gemm_bf16_mfma_dma.hip", "gemm_bf16_mfma_splitk.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

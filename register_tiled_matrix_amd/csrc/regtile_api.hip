@@ -129,7 +129,7 @@ int run_f32(int shift, int algo, bool ta, bool tb, int M, int N, int K, float al
 int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K, float alpha,
             const uint16_t *A, int lda, const uint16_t *B, int ldb, float beta, float *C, int ldc,
             void *stream) {
-    if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA_16X16) return -1;
+    if (algo < REGTILE_BF16_AUTO || algo > REGTILE_BF16_MFMA_SPLITK) return -1;
     const int v = validate(shift, M, N, K, alpha, A, lda, B, ldb, C, ldc, ta, tb);
     if (v != REGTILE_OK) return v;
     const regtile::Problem p = make_problem(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb);
@@ -139,8 +139,16 @@ int run_16b(bool f16, int shift, int algo, bool ta, bool tb, int M, int N, int K
     const char *name = "none";
     hipError_t err;
     switch (algo) {
+        case REGTILE_BF16_AUTO:
+            if (!(regtile::bf16_splitk_preferred(p) && regtile::launch_bf16_mfma_splitk(p, s, &name, f16, &err)))
+                err = regtile::launch_bf16_mfma(p, s, &name, 32, f16);
+            break;
         case REGTILE_BF16_NAIVE: err = regtile::launch_bf16_naive(p, s, &name, f16); break;
         case REGTILE_BF16_MFMA_16X16: err = regtile::launch_bf16_mfma(p, s, &name, 16, f16); break;
+        case REGTILE_BF16_MFMA_SPLITK:
+            if (!regtile::launch_bf16_mfma_splitk(p, s, &name, f16, &err))
+                err = regtile::launch_bf16_mfma(p, s, &name, 32, f16);
+            break;
         default: err = regtile::launch_bf16_mfma(p, s, &name, 32, f16); break;
     }
     return finish(err, name);

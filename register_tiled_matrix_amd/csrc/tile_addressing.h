@@ -101,6 +101,16 @@ REGTILE_HD uint32_t row_block_off(int b, int width, int64_t ld) {
 }
 REGTILE_HD uint32_t row_run_off(int k, int64_t ld) { return (uint32_t)k * (uint32_t)ld * 2u; }
 
+// The split-K kernel (gemm_bf16_mfma_splitk.hip) stages 64x64 tiles in the K-contiguous DMA
+// layout above (kc_dma_lane / kc_dma_instr, 64-row tiles, four waves). It takes K-contiguous A
+// and B with K a multiple of 8 (every chunk lies wholly before or wholly past K), leading
+// dimensions multiples of 8 and 64 rows of either operand within 2^30 bytes, so that a lane
+// offset carrying kPastEnd plus any uniform part stays below 2^32.
+REGTILE_HD bool sk_dma_takes(int K, int64_t lda, int64_t ldb) {
+    const int64_t lim = int64_t(1) << 30;
+    return K > 0 && K % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && 64 * lda * 2 < lim && 64 * ldb * 2 < lim;
+}
+
 // C fragment layout of the two gfx950 MFMA shapes: accumulator v of lane l of an MF x MF
 // block sits at row c_row_lane(l) + c_row_acc(v), column l % MF.
 //   MF = 32 (32x32x16): row (l / 32) * 4 + (v / 4) * 8 + v % 4;

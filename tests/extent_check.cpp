@@ -14,7 +14,7 @@
 //   5. every store inside the C descriptor writes an element of C, each element of the tile
 //      exactly once.
 // Usage:
-//   extent_check one <kc|tn|nn|tt|gather> M N K lda ldb ldc
+//   extent_check one <kc|tn|nn|tt|gather|sk> M N K lda ldb ldc
 //   extent_check force ...                   (the same, also where the launcher would refuse)
 //   extent_check sweep <seed> <count>        (seeded shapes the launchers take, every path)
 // Prints one line per violation (at most 20) and a summary; exit status 1 on any violation.
@@ -327,6 +327,12 @@ bool check_problem(const std::string &path, int M, int N, int K, int64_t lda, in
         check_c<32>(M, N, ldc, t);
         return true;
     }
+    if (path == "sk") {  // split-K kernel: A row-major, B stored N x K, 64x64 tiles
+        if (!addr::sk_dma_takes(K, lda, ldb) && !g_force) return false;
+        check_kc_operand<32>("A", M, K, lda, 64);
+        check_kc_operand<32>("B", N, K, ldb, 64);
+        return true;
+    }
     if (path == "tn") {
         if (!addr::mn_dma_takes(M, N, K, lda, ldb, ldc) && !g_force) return false;
         check_mn_operand("A", M, K, lda, t);
@@ -378,7 +384,7 @@ int main(int argc, char **argv) {
         const int sizes[] = {1, 2, 3, 4, 7, 8, 12, 16, 24, 56, 63, 64, 65, 96, 120, 127, 128, 129, 136, 200,
                              248, 255, 256, 257, 263, 264, 384, 509, 512, 520, 1000, 1088, 1504, 2040};
         const int n_sizes = sizeof sizes / sizeof sizes[0];
-        const char *paths[] = {"kc", "tn", "nn", "tt", "gather"};
+        const char *paths[] = {"kc", "tn", "nn", "tt", "gather", "sk"};
         long taken = 0;
         for (int c = 0; c < count; ++c) {
             const int M = sizes[rng() % n_sizes], N = sizes[rng() % n_sizes], K = sizes[rng() % n_sizes];
@@ -396,6 +402,6 @@ int main(int argc, char **argv) {
                     g_violations);
         return g_violations ? 1 : 0;
     }
-    std::fprintf(stderr, "usage: extent_check one <kc|tn|nn|tt|gather> M N K lda ldb ldc | sweep <seed> <count>\n");
+    std::fprintf(stderr, "usage: extent_check one <kc|tn|nn|tt|gather|sk> M N K lda ldb ldc | sweep <seed> <count>\n");
     return 2;
 }

@@ -95,8 +95,8 @@ def test_unknown_algorithm_is_argument_one(lib):
     a = (4, 4, 4, 1.0, DUMMY, 4, DUMMY, 4, 0.0, DUMMY, 4, 0)
     assert rt.regtile_gemm_f32_algo(6, *a) == -1
     assert rt.regtile_gemm_f32_algo(-1, *a) == -1
-    assert rt.regtile_gemm_bf16_algo(4, *a) == -1
-    assert rt.regtile_gemm_f16_algo(4, *a) == -1
+    assert rt.regtile_gemm_bf16_algo(5, *a) == -1
+    assert rt.regtile_gemm_f16_algo(5, *a) == -1
 
 
 def test_null_operands_allowed_when_not_read(lib):

@@ -1,8 +1,9 @@
 """Memory extents of the 16-bit kernels' buffer-descriptor accesses, checked on the CPU.
 
 `extent_check.cpp` enumerates every load and store that the edge tiles of the LDS-DMA kernel
-(K-contiguous "n t", M/N-major "t n", register rows "n n" / "t t") and the register-staged
-kernel's M/N-contiguous gather issue through a buffer descriptor, computing each offset with
+(K-contiguous "n t", M/N-major "t n", register rows "n n" / "t t"), the split-K kernel's
+per-wave DMA ("sk") and the register-staged kernel's M/N-contiguous gather issue through a
+buffer descriptor, computing each offset with
 the functions the kernels call (csrc/tile_addressing.h). It checks that every descriptor ends
 inside the caller's matrix, that no access meant for a matrix element straddles or passes a
 descriptor end, that each offset addresses the element the layout assigns it, and that every
@@ -64,6 +65,10 @@ TAKEN = [
     ("kc", 8000, 8000, 8192, 8192, 8192, 8000),
     ("kc", 6000, 6000, 6000, 6000, 6000, 6000),    # K tail
     ("kc", 1, 1, 8, 8, 8, 1),
+    ("sk", 1024, 1024, 16384, 16384, 16384, 1024),  # split-K kernel: few tiles, deep K
+    ("sk", 1000, 1000, 776, 776, 776, 1000),        # ragged tile edge, K tail
+    ("sk", 65, 129, 72, 72, 80, 129),
+    ("sk", 1, 1, 8, 8, 8, 1),
     ("gather", 4000, 4100, 200, 4000, 4100, 4100),
     ("gather", 1000, 1504, 777, 1000, 1504, 1504),
 ]

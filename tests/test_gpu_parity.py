@@ -341,6 +341,88 @@ def test_16bit_dma_kernel_k_tail_integer_bitwise():
     assert np.array_equal(got[I, J].astype(np.float64), ref)
 
 
+# ---- 16-bit split-K kernel: 64x64 tiles, K dealt out to the 4 waves of a workgroup ------------
+# Full comparisons on shapes with ragged tile edges, K tails (K a multiple of 8 ending inside a
+# 64-deep slab, or inside the first 16-wide block), fewer slabs than waves, and C with padded
+# rows (ldc = N + 5: scalar stores) whose padding must stay untouched.
+SK16_SHAPES = [(1024, 1024, 4096), (1000, 1000, 776), (64, 64, 64), (1, 2, 8), (65, 129, 72),
+               (300, 257, 1000), (2048, 512, 8192), (128, 64, 200), (64, 64, 16), (100, 100, 8)]
+
+
+@pytest.mark.parametrize("pad", [0, 5])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", SK16_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SK16_SHAPES])
+def test_16bit_splitk_kernel(shape, dtype, pad):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.5, beta=-0.5, seed=M + 3 * N + K + pad)
+    announce(f"{dtype} split-K {shape} pad {pad}")
+    A, B, C0 = device_operands(inp, torch)
+    big = torch.full((M, N + pad), 1234.5, device="cuda")
+    C = big[:, :N]
+    C.copy_(C0)
+    fn = {"bf16": rt.gemm_bf16, "f16": rt.gemm_f16}[dtype]
+    fn(A, B, C, alpha=inp.alpha, beta=inp.beta, algo=rt.ALGO_BF16_MFMA_SPLITK)
+    torch.cuda.synchronize()
+    name = rt.last_kernel()
+    assert name == f"{dtype}_mfma32x32x16_splitk4_64x64x64" + ("_ktail" if K % 64 else ""), name
+    if pad:
+        assert torch.all(big[:, N:] == 1234.5).item(), "a store landed past column N"
+    assert_parity_full(inp, C.cpu().numpy(), f"{dtype} split-K {shape} pad {pad}")
+
+
+def test_16bit_auto_picks_splitk_by_tile_count():
+    # the default entry points: split-K for few 64x64 tiles with enough K, the LDS-DMA kernel
+    # otherwise (and for any layout other than K-contiguous A and B)
+    cases = [((1024, 1024, 4096), "splitk4"), ((512, 512, 1024), "splitk4"), ((1280, 1280, 8192), "splitk4"),
+             ((1024, 1024, 512), "_dma_"), ((1024, 2048, 2048), "_dma_"), ((1536, 1536, 8192), "_dma_")]
+    for (M, N, K), want in cases:
+        A = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+        Bt = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+        rt.gemm_bf16(A, Bt.t())
+        assert want in rt.last_kernel(), ((M, N, K), rt.last_kernel())
+        rt.gemm_f16(A.half(), Bt.half().t())
+        assert want in rt.last_kernel() and rt.last_kernel().startswith("f16_"), ((M, N, K), rt.last_kernel())
+    # "n n" storage of the same few-tile problem keeps the LDS-DMA kernel
+    rt.gemm_bf16(torch.zeros((1024, 4096), dtype=torch.bfloat16, device="cuda"),
+                 torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda"))
+    assert "splitk" not in rt.last_kernel(), rt.last_kernel()
+    torch.cuda.synchronize()
+
+
+def test_16bit_splitk_integer_inputs_bitwise():
+    # |partial sums| <= 4104 * 256, exact in fp32: the sum over the four waves' partials must
+    # equal the oracle bit for bit (K tail included)
+    rng = np.random.Generator(np.random.PCG64(81))
+    M, N, K = 1000, 1000, 4104
+    A = gi.f32_to_bf16_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+    Bt = gi.f32_to_bf16_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, A, Bt, None)
+    announce("bf16 split-K integer bitwise")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA_SPLITK).cpu().numpy()
+    assert rt.last_kernel() == "bf16_mfma32x32x16_splitk4_64x64x64_ktail", rt.last_kernel()
+    ref, _ = oracle.gemm_inputs(inp)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_16bit_splitk_falls_back_where_it_does_not_apply():
+    # K not a multiple of 8, and a transposed A: the split-K rung hands the problem to the
+    # MFMA kernel, with the same results as that rung
+    for (M, N, K), ta in (((300, 200, 100), False), ((256, 256, 512), True)):
+        inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=1.0, beta=0.0, seed=M + N + K)
+        A, B, _ = device_operands(inp, torch)
+        if ta:
+            A = A.t().contiguous().t()
+        announce(f"bf16 split-K fallback {(M, N, K)} ta={ta}")
+        C1 = rt.gemm_bf16(A, B, algo=rt.ALGO_BF16_MFMA_SPLITK)
+        name = rt.last_kernel()
+        C2 = rt.gemm_bf16(A, B, algo=rt.ALGO_BF16_MFMA)
+        torch.cuda.synchronize()
+        assert "splitk" not in name, name
+        assert name == rt.last_kernel(), (name, rt.last_kernel())
+        assert torch.equal(C1, C2)
+        assert_parity_full(inp, C1.cpu().numpy(), f"split-K fallback {(M, N, K)}")
+
+
 # ---- bitwise: integer-valued operands (every partial sum exact in fp32) ---------------------
 @pytest.mark.parametrize("algo", F32_ALGOS)
 def test_f32_integer_inputs_are_bitwise_exact(algo):

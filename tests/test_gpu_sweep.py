@@ -52,6 +52,8 @@ DETERMINISM = [
     ("f32", (1000, 1500, 777), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x96x8_8x12"),
     ("f32", (256, 256, 256), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_32x32x16_4x4"),
     ("f32", (1024, 1024, 1024), 0, 0, rt.ALGO_F32_AUTO, "f32_regtile_splitk8_64x64x16_8x8"),
+    ("bf16", (1024, 1024, 8192), 0, 1, rt.ALGO_BF16_MFMA_SPLITK, "bf16_mfma32x32x16_splitk4_64x64x64"),
+    ("f16", (1000, 1000, 4104), 0, 1, rt.ALGO_BF16_MFMA_SPLITK, "f16_mfma32x32x16_splitk4_64x64x64_ktail"),
 ]
 
 
@@ -96,7 +98,7 @@ def _sweep_shapes(count, seed):
 
 SWEEP = _sweep_shapes(24, 20261202)
 F32_RUNGS = [rt.ALGO_F32_AUTO, rt.ALGO_F32_REGTILE, rt.ALGO_F32_SPLITK, rt.ALGO_F32_REGTILE_SMALL]
-BF16_RUNGS = [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16]
+BF16_RUNGS = [rt.ALGO_BF16_AUTO, rt.ALGO_BF16_MFMA_16X16, rt.ALGO_BF16_MFMA_SPLITK]
 
 
 @pytest.mark.parametrize("shape", SWEEP, ids=["x".join(map(str, s)) for s in SWEEP])
