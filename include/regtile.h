@@ -109,7 +109,11 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
  *   A, lda  bf16 row-major M x K (lda >= max(1,K));
  *   B, ldb  bf16 column-major K x N: element (k,j) at B[j*ldb + k] (ldb >= max(1,K));
  *   C, ldc  fp32 row-major M x N.
- * Argument positions and rules as for gemm_f32.
+ * Argument positions and rules as for gemm_f32. Kernel choice: problems of at most 256 tiles of
+ * 64x64 with K >= 1024, or at most 512 with K >= 4096, take the split-K kernel
+ * (REGTILE_BF16_MFMA_SPLITK) when its conditions hold; the rest the MFMA kernels
+ * (REGTILE_BF16_MFMA). Both sum each output in a fixed order: repeated calls give identical
+ * bits, but the two kernels' roundings differ.
  */
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
               int ldb, float beta, float *C, int ldc, void *stream);
