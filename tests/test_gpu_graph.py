@@ -4,7 +4,8 @@ A call makes no allocation, memset or synchronisation: it checks its arguments o
 launches one kernel on the caller's stream. So a sequence of calls can be captured into a HIP
 graph once and replayed. The test captures a chain that touches each kernel family (split-K on
 32x32 and guarded 64x96 tiles, the 128x256 square kernel, the 16-bit LDS-DMA kernel on
-128x128 and 256x256 tiles, a beta != 0 call, and a call that reads an earlier call's output),
+128x128 and 256x256 tiles, the 16-bit split-K kernel, beta != 0 calls, and a call that reads
+an earlier call's output),
 then replays it several times. Between replays the inputs are refreshed in place by eager
 work, the same chain runs eagerly into its own outputs, and the device is synchronised. Every
 replay must match the eager chain bitwise (the kernels issue a fixed sequence of operations per
@@ -39,6 +40,7 @@ CHAIN = [
     ("f32 square", "f32", (512, 1024, 256), -0.75, 0.0, rt.ALGO_F32_REGTILE, "f32_regtile_128x256x16_8x16"),
     ("bf16 128x128 tiles", "bf16", (2048, 2048, 512), 1.0, 0.5, rt.ALGO_BF16_AUTO, "bf16_mfma32x32x16_dma_128x128x64"),
     ("bf16 256x256 tiles", "bf16", (4096, 4096, 128), 1.0, 0.0, rt.ALGO_BF16_AUTO, "bf16_mfma32x32x16_dma_256x256x64"),
+    ("bf16 split-K", "bf16", (1024, 1024, 1032), 1.25, -0.5, rt.ALGO_BF16_AUTO, "bf16_mfma32x32x16_splitk4_64x64x64_ktail"),
 ]
 
 
