@@ -66,7 +66,7 @@ enum regtile_algo_f32 {
 
 /* Kernel ladder for the bf16 and fp16 entry points. */
 enum regtile_algo_bf16 {
-    REGTILE_BF16_AUTO = 0,   /* library's choice: the MFMA kernel */
+    REGTILE_BF16_AUTO = 0,   /* library's choice: split-K (4) for few tiles, else the MFMA kernel (2) */
     REGTILE_BF16_NAIVE = 1,  /* one thread per C element, fp32 FMA accumulation */
     REGTILE_BF16_MFMA = 2,   /* LDS-tiled, wave-level 32x32x16 MFMA fragments, fp32 accumulators */
     REGTILE_BF16_MFMA_16X16 = 3, /* the same with 16x16x32 fragments where the LDS-DMA kernel
