@@ -338,10 +338,10 @@ def cmd_datadep(args) -> int:
 
 SHAPES_F32 = [(4096, 4096, 4096), (8192, 8192, 8192), (1000, 1500, 777), (16384, 128, 4096), (256, 256, 256),
               (2048, 2048, 2048), (4096, 2048, 4096), (3072, 3072, 3072), (1024, 1024, 8192), (3000, 2000, 512),
-              (8190, 8190, 1023)]
+              (8190, 8190, 1023), (512, 4096, 4096)]
 SHAPES_16 = [(8192, 8192, 8192), (8000, 8000, 8192), (6000, 6000, 6000), (4096, 4096, 4096), (4000, 4000, 4000),
              (2048, 4096, 4096), (2048, 2048, 8192), (1536, 1536, 8192), (1024, 1024, 16384), (512, 512, 8192),
-             (2048, 512, 4096), (3000, 5000, 2000),
+             (2048, 512, 4096), (1024, 8192, 8192), (3000, 5000, 2000),
              (8190, 8190, 8190)]
 
 
