@@ -546,6 +546,19 @@ def test_beta_zero_never_reads_c(dtype):
     assert_parity_full(inp, got, "beta=0 with NaN C")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(200, 300, 1024), (1000, 1000, 776)], ids=lambda s: "x".join(map(str, s)))
+def test_16bit_splitk_beta_zero_never_reads_c(dtype, shape):
+    M, N, K = shape
+    inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", seed=5)
+    announce(f"beta=0 NaN C {dtype} split-K {shape}")
+    got = run(inp, torch, rt.ALGO_BF16_MFMA_SPLITK, C_init=torch.full((M, N), float("nan"), device="cuda"))
+    assert "splitk4" in rt.last_kernel(), rt.last_kernel()
+    got = got.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert_parity_full(inp, got, "split-K beta=0 with NaN C")
+
+
 F32_EPILOGUE_CASES = [(rt.ALGO_F32_REGTILE, (200, 300, 64), "f32_regtile_128x256"),
                       (rt.ALGO_F32_REGTILE_SMALL, (200, 300, 64), "f32_regtile_64x64x32"),
                       (rt.ALGO_F32_SPLITK, (200, 300, 64), "f32_regtile_splitk8_32x32"),
