@@ -638,6 +638,27 @@ def test_bf16_strided_and_misaligned_views():
     assert_parity_full(inp, C.cpu().numpy(), "bf16 strided views")
 
 
+@pytest.mark.parametrize("pad_a,pad_b,off_a,splitk", [(16, 8, 0, True), (24, 40, 8, True), (5, 3, 1, False)])
+def test_16bit_splitk_padded_rows(pad_a, pad_b, off_a, splitk):
+    # leading dimensions beyond K: multiples of 8 with 16-byte aligned rows take the split-K
+    # kernel; otherwise the split-K rung hands the problem on (same results either way)
+    rng = np.random.Generator(np.random.PCG64(9 + pad_a))
+    M, N, K = 333, 190, 1096
+    ha = gi.f32_to_bf16_bits(rng.standard_normal(M * (K + pad_a), dtype=np.float32)).reshape(M, K + pad_a)
+    hb = gi.f32_to_bf16_bits(rng.standard_normal(N * (K + pad_b), dtype=np.float32)).reshape(N, K + pad_b)
+    da = torch.from_numpy(ha.view(np.int16)).cuda().view(torch.bfloat16)
+    db = torch.from_numpy(hb.view(np.int16)).cuda().view(torch.bfloat16)
+    A = da[:, off_a:off_a + K]
+    B = db[:, :K].t()
+    announce(f"bf16 split-K padded rows lda={K + pad_a} ldb={K + pad_b} offset={off_a}")
+    C = rt.gemm_bf16(A, B, algo=rt.ALGO_BF16_MFMA_SPLITK)
+    torch.cuda.synchronize()
+    assert ("splitk4" in rt.last_kernel()) == splitk, rt.last_kernel()
+    inp = gi.GemmInputs(M, N, K, 1.0, 0.0, "bf16", True, np.ascontiguousarray(ha[:, off_a:off_a + K]),
+                        np.ascontiguousarray(hb[:, :K]), None)
+    assert_parity_full(inp, C.cpu().numpy(), f"bf16 split-K padded rows ({rt.last_kernel()})")
+
+
 def test_runs_on_the_callers_stream_and_is_deterministic():
     inp = gi.make_inputs(1024, 1024, 1024, dist="uniform", seed=8)
     A, B, C = device_operands(inp, torch)
