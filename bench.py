@@ -595,6 +595,29 @@ def main():
             del Am, Bm, Cm
         out["layouts"] = lay
 
+    # ---- a bf16 problem of few output tiles: split-K inside the workgroup against the
+    # LDS-DMA kernel (64 tiles of 128x128 for 256 CUs) --------------------------------------
+    if not args.no_ladder and not args.no_bf16:
+        M_, N_, K_ = 1024, 1024, 16384
+        ift = gi.make_inputs(M_, N_, K_, dtype="bf16", dist="normal", seed=1005)
+        Af = torch.from_numpy(ift.A.view(np.int16)).to(dev)
+        Bf = torch.from_numpy(ift.B.view(np.int16)).to(dev)  # stored N x K
+        Cf = torch.empty((M_, N_), dtype=torch.float32, device=dev)
+        few = {"shape": [M_, N_, K_]}
+        for algo, label in ((rt.ALGO_BF16_AUTO, "default"), (rt.ALGO_BF16_MFMA, "lds_dma_kernel")):
+            def step_f(algo=algo):
+                st = rt.regtile_gemm_bf16_algo(algo, M_, N_, K_, 1.0, Af.data_ptr(), K_, Bf.data_ptr(), K_, 0.0,
+                                               Cf.data_ptr(), N_, stream)
+                if st:
+                    raise rt.RegtileError(st, rt.strerror(st))
+
+            step_f()
+            kms = _steady_median(torch, step_f)
+            few[label] = {"kernel": rt.last_kernel(), "kernel_ms": round(kms, 4),
+                          "TFLOP/s": round(2.0 * M_ * N_ * K_ / (kms * 1e-3) / 1e12, 2)}
+        out["bf16_few_tiles"] = few
+        del Af, Bf, Cf
+
     # ---- the ladder on the headline workload ------------------------------------------------
     if not args.no_ladder:
         ladder = {}
