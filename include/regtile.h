@@ -75,8 +75,10 @@ enum regtile_algo_bf16 {
     REGTILE_BF16_MFMA_SPLITK = 4 /* K split over the 4 waves of a workgroup on 64x64 tiles,
                                     32x32x16 fragments, partials summed in a fixed order (for
                                     problems with few tiles; "寄存器Tiling跨架构解析" sections 2.4
-                                    and 7.2). K-contiguous A and B with 16-byte aligned rows and
-                                    K a multiple of 8; other problems as REGTILE_BF16_MFMA */
+                                    and 7.2). Any storage order with 16-byte aligned rows: a
+                                    K-contiguous operand needs K and its leading dimension
+                                    multiples of 8, an M/N-contiguous one its column count and
+                                    leading dimension; other problems as REGTILE_BF16_MFMA */
 };
 
 /*
@@ -110,10 +112,10 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
  *   B, ldb  bf16 column-major K x N: element (k,j) at B[j*ldb + k] (ldb >= max(1,K));
  *   C, ldc  fp32 row-major M x N.
  * Argument positions and rules as for gemm_f32. Kernel choice: problems of at most 256 tiles of
- * 64x64 with K >= 1024, or at most 512 with K >= 4096, take the split-K kernel
- * (REGTILE_BF16_MFMA_SPLITK) when its conditions hold; the rest the MFMA kernels
- * (REGTILE_BF16_MFMA). Both sum each output in a fixed order: repeated calls give identical
- * bits, but the two kernels' roundings differ.
+ * 64x64 with K >= 1024, or at most 512 with K >= 4096 (for this storage order, and for the _ex
+ * form's "t n"), take the split-K kernel (REGTILE_BF16_MFMA_SPLITK) when its conditions hold;
+ * the rest the MFMA kernels (REGTILE_BF16_MFMA). Both sum each output in a fixed order:
+ * repeated calls give identical bits, but the two kernels' roundings differ.
  */
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
               int ldb, float beta, float *C, int ldc, void *stream);

@@ -50,7 +50,8 @@ constexpr int SK_TPR = SK_NT / SK_T;      // epilogue threads per row
 constexpr int SK_SW = SK_T / SK_TPR;      // columns per epilogue thread
 static_assert(SK_J == 2 && SK_SW % 4 == 0, "two DMA instructions per operand; whole float4 strips");
 
-template <int R, bool F16, bool KTAIL>
+// MN: bit 0, A is stored K x M; bit 1, B is stored K x N (M/N-major slabs, transposing reads).
+template <int R, bool F16, bool KTAIL, int MN>
 __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
     int M, int N, int K, float alpha, const uint16_t *__restrict__ A, int64_t lda,
     const uint16_t *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -61,6 +62,8 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
     constexpr int SLOTS_RING = R * SK_SLAB, SLOTS_PART = SK_NW * SK_T * SK_PSTRIDE / 4;
     static_assert(R >= 4 && 4 * (R - 2) < 64, "ring of at least four slabs; vmcnt range");
     static_assert(SLOTS_RING * 16 <= 160 * 1024 && SLOTS_PART <= SLOTS_RING, "LDS");
+    constexpr bool A_MN = (MN & 1) != 0, B_MN = (MN & 2) != 0;
+    static_assert(!(KTAIL && MN == 3), "the K tail of M/N-major operands is the descriptors' end");
     __shared__ uint4 smem[SLOTS_RING];
 
     const int tid = threadIdx.x;
@@ -69,10 +72,14 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
     grouped_tile<8>(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
     const int m0 = tm * SK_T, n0 = tn * SK_T;
 
-    // Descriptors over the tile's rows of A and columns of B (B stored N x K), each ending at
-    // element K - 1 of its last real row.
-    const rsrc_t a_rsrc = make_rsrc(A + (int64_t)m0 * lda, addr::desc_bytes(min(SK_T, M - m0), lda, K, 2));
-    const rsrc_t b_rsrc = make_rsrc(B + (int64_t)n0 * ldb, addr::desc_bytes(min(SK_T, N - n0), ldb, K, 2));
+    // Descriptors: over the tile's rows of a K-contiguous operand, ending at element K - 1 of its
+    // last real row; over the K rows of an M/N-major operand from the tile's first column,
+    // ending at the operand's last element (rows past K, and that row's columns past M or N,
+    // load zeros; other columns past M or N only feed outputs that are never stored).
+    const rsrc_t a_rsrc = A_MN ? make_rsrc(A + m0, addr::desc_bytes(K, lda, M - m0, 2))
+                               : make_rsrc(A + (int64_t)m0 * lda, addr::desc_bytes(min(SK_T, M - m0), lda, K, 2));
+    const rsrc_t b_rsrc = B_MN ? make_rsrc(B + n0, addr::desc_bytes(K, ldb, N - n0, 2))
+                               : make_rsrc(B + (int64_t)n0 * ldb, addr::desc_bytes(min(SK_T, N - n0), ldb, K, 2));
     const int nslabs = (K + SK_BK - 1) / SK_BK;
     const int k_last = (nslabs - 1) * SK_BK;
     uint32_t a_voff[SK_J], b_voff[SK_J], a_voff_last[SK_J], b_voff_last[SK_J];
@@ -83,7 +90,15 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
         b_voff[j] = addr::kc_dma_lane<SK_KCH, MF>(wave, SK_J, j, lane, ldb, &kb);
         a_voff_last[j] = k_last + ka < K ? a_voff[j] : a_voff[j] | addr::kPastEnd;
         b_voff_last[j] = k_last + kb < K ? b_voff[j] : b_voff[j] | addr::kPastEnd;
+        if (A_MN) a_voff[j] = a_voff_last[j] = addr::sk_mn_dma_lane(lane, lda);
+        if (B_MN) b_voff[j] = b_voff_last[j] = addr::sk_mn_dma_lane(lane, ldb);
     }
+    auto soff_a = [&](int q, int k0) {
+        return A_MN ? addr::mn_dma_instr(wave, SK_J, q, k0, lda, SK_KCH) : addr::kc_dma_instr<SK_KCH>(q, k0, lda);
+    };
+    auto soff_b = [&](int q, int k0) {
+        return B_MN ? addr::mn_dma_instr(wave, SK_J, q, k0, ldb, SK_KCH) : addr::kc_dma_instr<SK_KCH>(q, k0, ldb);
+    };
     // DMA instruction d (0, 1: A; 2, 3: B) of this wave for slab `slab` into ring slot `slot`.
     // A slab past the last takes offsets past the descriptors' ends: it fills its (unused)
     // slot with zeros without touching memory, and keeps every wait's count the same.
@@ -96,9 +111,9 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
         const uint32_t va = past ? a_voff[q] | addr::kPastEnd : last ? a_voff_last[q] : a_voff[q];
         const uint32_t vb = past ? b_voff[q] | addr::kPastEnd : last ? b_voff_last[q] : b_voff[q];
         if (d < 2)
-            dma16_buf(a_rsrc, va, addr::kc_dma_instr<SK_KCH>(q, k0, lda), dst);
+            dma16_buf(a_rsrc, va, soff_a(q, k0), dst);
         else
-            dma16_buf(b_rsrc, vb, addr::kc_dma_instr<SK_KCH>(q, k0, ldb), dst);
+            dma16_buf(b_rsrc, vb, soff_b(q, k0), dst);
     };
 
     typename F::acc_t acc[MI][NI];
@@ -113,20 +128,45 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
     // ring slot `slot` into register buffer `buf`: lane l reads row 32 i + l % 32 (A) or column
     // 32 j + l % 32 (B) at chunk 2 w + l / 32, conflict-free under the slab key.
     const int frag_r = lane & 31, chunk = 2 * wave + (lane >> 5);
+    // M/N-major fragment (two ds_read_b64_tr_b16): in each group of 16 lanes, lane t addresses
+    // k row 16 w + 8 (l / 32) + t / 4 (+ 4 for the second read) at columns 16 ((l / 16) % 2) +
+    // 4 (t % 4) .. + 3 of the fragment, so that lane l receives column l % 32 at the 8 k of its
+    // group (mfma_common.h states the transposing read's lane mapping). Rows r and r + 4 share
+    // the key.
+    const int tr_t = lane & 15;
+    const int tr_row = 16 * wave + 8 * (lane >> 5) + (tr_t >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (tr_t & 3);
+    auto mn_frag = [&](const uint4 *part, int col0) {
+        const char *base = reinterpret_cast<const char *>(part);
+        const int col = col0 + tr_col;
+        const int off = ((col >> 3) ^ addr::sk_mn_key(tr_row)) * 16 + (col & 7) * 2;
+        const uint2 lo = lds_read_tr16(base + tr_row * (SK_KCH * 16) + off);
+        const uint2 hi = lds_read_tr16(base + (tr_row + 4) * (SK_KCH * 16) + off);
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
     bf16x8 fa[2][MI], fb[2][NI];
     auto read_frags = [&](int slot, int buf) {
         const uint4 *sa = smem + slot * SK_SLAB, *sb = sa + SK_OP;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-            const int row = i * MF + frag_r;
-            fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * SK_KCH + (chunk ^ slab_key<SK_KCH, MF>(row))]);
+            if constexpr (A_MN) {
+                fa[buf][i] = mn_frag(sa, i * MF);
+            } else {
+                const int row = i * MF + frag_r;
+                fa[buf][i] = __builtin_bit_cast(bf16x8, sa[row * SK_KCH + (chunk ^ slab_key<SK_KCH, MF>(row))]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int row = j * MF + frag_r;
-            fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * SK_KCH + (chunk ^ slab_key<SK_KCH, MF>(row))]);
+            if constexpr (B_MN) {
+                fb[buf][j] = mn_frag(sb, j * MF);
+            } else {
+                const int row = j * MF + frag_r;
+                fb[buf][j] = __builtin_bit_cast(bf16x8, sb[row * SK_KCH + (chunk ^ slab_key<SK_KCH, MF>(row))]);
+            }
         }
     };
+    constexpr int NREAD = MI * (A_MN ? 2 : 1) + NI * (B_MN ? 2 : 1);  // LDS reads per k step
     auto wrap = [](int x) { return x >= R ? x - R : x; };
 
     // iteration s on register buffer CB (compile-time, so the buffers stay in registers);
@@ -147,7 +187,7 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
 #pragma unroll
         for (int d = 0; d < 4; ++d) dma_one(s + R - 1, refill, d);
         // order: the fragment reads, then MFMA and DMA load in turn
-        __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -261,36 +301,54 @@ __global__ __launch_bounds__(SK_NT) void bf16_mfma_splitk_kernel(
 #define SK_RING 8
 #endif
 
-template <bool F16, bool KTAIL>
+template <bool F16, bool KTAIL, int MN>
 hipError_t launch_sk(const Problem &p, hipStream_t s) {
     const int tiles_m = (p.M + SK_T - 1) / SK_T, tiles_n = (p.N + SK_T - 1) / SK_T;
     const int vec_c = (p.ldc % 4) == 0 && aligned16(p.C);
-    note_launch(reinterpret_cast<const void *>(&bf16_mfma_splitk_kernel<SK_RING, F16, KTAIL>), SK_NT);
-    hipLaunchKernelGGL((bf16_mfma_splitk_kernel<SK_RING, F16, KTAIL>), dim3(tiles_m * tiles_n), dim3(SK_NT), 0, s,
-                       p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
+    note_launch(reinterpret_cast<const void *>(&bf16_mfma_splitk_kernel<SK_RING, F16, KTAIL, MN>), SK_NT);
+    hipLaunchKernelGGL((bf16_mfma_splitk_kernel<SK_RING, F16, KTAIL, MN>), dim3(tiles_m * tiles_n), dim3(SK_NT), 0,
+                       s, p.M, p.N, p.K, p.alpha, (const uint16_t *)p.A, p.lda, (const uint16_t *)p.B, p.ldb,
                        p.beta, p.C, p.ldc, tiles_m, tiles_n, vec_c);
     return hipGetLastError();
+}
+template <bool F16, int MN>
+hipError_t launch_sk_tail(const Problem &p, hipStream_t s, bool ktail) {
+    if constexpr (MN == 3)
+        return launch_sk<F16, false, 3>(p, s);
+    else
+        return ktail ? launch_sk<F16, true, MN>(p, s) : launch_sk<F16, false, MN>(p, s);
+}
+template <bool F16>
+hipError_t launch_sk_layout(const Problem &p, hipStream_t s, int mn, bool ktail) {
+    switch (mn) {
+        case 1: return launch_sk_tail<F16, 1>(p, s, ktail);
+        case 2: return launch_sk_tail<F16, 2>(p, s, ktail);
+        case 3: return launch_sk_tail<F16, 3>(p, s, ktail);
+        default: return launch_sk_tail<F16, 0>(p, s, ktail);
+    }
 }
 
 }  // namespace
 
-// Takes (and launches, status in *err) a problem with K-contiguous A and B (A row-major, B
-// stored N x K) whose rows are 16-byte aligned, K a multiple of 8 and 64 rows of either operand
-// within 2^30 bytes (addr::sk_dma_takes); returns false, launching nothing, otherwise. M, N and
-// K may end anywhere.
+// Takes (and launches, status in *err) a problem whose operands meet addr::sk_dma_takes in
+// their storage: A row-major or stored K x M, B stored N x K (the native form) or K x N,
+// 16-byte aligned; returns false, launching nothing, otherwise. M, N and K may end anywhere.
 bool launch_bf16_mfma_splitk(const Problem &p, hipStream_t s, const char **name, bool f16, hipError_t *err) {
-    if (p.ta || !p.tb || !addr::sk_dma_takes(p.K, p.lda, p.ldb) || !aligned16(p.A) || !aligned16(p.B))
+    if (!addr::sk_dma_takes(p.ta, p.tb, p.M, p.N, p.K, p.lda, p.ldb) || !aligned16(p.A) || !aligned16(p.B))
         return false;
-    const bool ktail = p.K % SK_BK != 0;
-#define REGTILE_SK_NAME(elt) elt "_mfma32x32x16_splitk4_64x64x64"
-    static const char *const names[2][2] = {{REGTILE_SK_NAME("bf16"), REGTILE_SK_NAME("bf16") "_ktail"},
-                                            {REGTILE_SK_NAME("f16"), REGTILE_SK_NAME("f16") "_ktail"}};
+    const int mn = (p.ta ? 1 : 0) | (p.tb ? 0 : 2);
+    const bool ktail = mn != 3 && p.K % SK_BK != 0;  // a K-contiguous operand's last slab
+#define REGTILE_SK_NAME(elt, lay) elt "_mfma32x32x16_splitk4_64x64x64" lay
+#define REGTILE_SK_PAIR(elt, lay) {REGTILE_SK_NAME(elt, lay), REGTILE_SK_NAME(elt, lay) "_ktail"}
+#define REGTILE_SK_SET(elt) \
+    {REGTILE_SK_PAIR(elt, ""), REGTILE_SK_PAIR(elt, "_tt"), REGTILE_SK_PAIR(elt, "_nn"), REGTILE_SK_PAIR(elt, "_tn")}
+    // [f16][mn: 0 "n t" (native), 1 "t t", 2 "n n", 3 "t n"][ktail]
+    static const char *const names[2][4][2] = {REGTILE_SK_SET("bf16"), REGTILE_SK_SET("f16")};
+#undef REGTILE_SK_SET
+#undef REGTILE_SK_PAIR
 #undef REGTILE_SK_NAME
-    *name = names[f16][ktail];
-    if (f16)
-        *err = ktail ? launch_sk<true, true>(p, s) : launch_sk<true, false>(p, s);
-    else
-        *err = ktail ? launch_sk<false, true>(p, s) : launch_sk<false, false>(p, s);
+    *name = names[f16][mn][ktail];
+    *err = f16 ? launch_sk_layout<true>(p, s, mn, ktail) : launch_sk_layout<false>(p, s, mn, ktail);
     return true;
 }
 

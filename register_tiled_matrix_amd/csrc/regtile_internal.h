@@ -55,19 +55,23 @@ bool launch_bf16_mfma_dma_rows(const Problem &p, hipStream_t s, const char **nam
 // and transposing fragment reads; M and N multiples of 8, 16-byte aligned rows.
 bool launch_bf16_mfma_dma_mn(const Problem &p, hipStream_t s, const char **name, bool f16,
                              hipError_t *err);
-// K split over the waves of a workgroup on 64x64 tiles, for problems with few tiles: K-contiguous
-// A and B with 16-byte aligned rows, K a multiple of 8 (addr::sk_dma_takes).
+// K split over the waves of a workgroup on 64x64 tiles, for problems with few tiles: any of the
+// four storage orders, 16-byte aligned rows, within addr::sk_dma_takes.
 bool launch_bf16_mfma_splitk(const Problem &p, hipStream_t s, const char **name, bool f16,
                              hipError_t *err);
 // The default 16-bit entry points take the split-K kernel for problems of few 64x64 tiles with
-// enough K per wave: at most 256 tiles (one per CU) with K >= 1024, or at most 512 with
-// K >= 4096. Measured against the LDS-DMA kernel (bf16, same box, interleaved): 1024^2 x 16384
-// 295 -> 577 TFLOP/s, 512^2 x 8192 74 -> 163, 2048 x 512 x 4096 246 -> 430, 1024^2 x 1024 169
-// -> 193, 1280^2 x 8192 423 -> 488; and on the other side of the rule 1024^2 x 256 70 against
-// 59, 1024 x 2048 x 2048 394 against 350, 1536^2 x 8192 557 against 470 (576 tiles).
+// enough K per wave: at most 256 tiles (one per CU) with K >= 1024 in any storage order, and at
+// most 512 with K >= 4096 for K-contiguous A and B ("n t") or M/N-contiguous both ("t n").
+// Measured against the LDS-DMA kernels (bf16, same box, interleaved, TFLOP/s): "n t" 1024^2 x
+// 16384 295 -> 577, 512^2 x 8192 74 -> 163, 1024^2 x 1024 169 -> 193, 1280^2 x 8192 423 ->
+// 488; 1024^2 x 16384 "n n" 195 -> 325, "t t" 199 -> 313, "t n" 130 -> 315; 1024 x 2048 x 8192
+// "t n" 246 -> 309. Outside the rule: "n t" 1024^2 x 256 70 against 59, 1024 x 2048 x 2048 394
+// against 350; 1024 x 2048 x 8192 "n n" 364 against 317, "t t" 367 against 305; 1536^2 x 8192
+// (576 tiles) 551 against 450 ("n t").
 inline bool bf16_splitk_preferred(const Problem &p) {
     const int64_t t64 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
-    return (t64 <= 256 && p.K >= 1024) || (t64 <= 512 && p.K >= 4096);
+    if (t64 <= 256 && p.K >= 1024) return true;
+    return p.ta != p.tb && t64 <= 512 && p.K >= 4096;  // "n t" or "t n"
 }
 
 // Host-side launch checks.

@@ -101,14 +101,32 @@ REGTILE_HD uint32_t row_block_off(int b, int width, int64_t ld) {
 }
 REGTILE_HD uint32_t row_run_off(int k, int64_t ld) { return (uint32_t)k * (uint32_t)ld * 2u; }
 
-// The split-K kernel (gemm_bf16_mfma_splitk.hip) stages 64x64 tiles in the K-contiguous DMA
-// layout above (kc_dma_lane / kc_dma_instr, 64-row tiles, four waves). It takes K-contiguous A
-// and B with K a multiple of 8 (every chunk lies wholly before or wholly past K), leading
-// dimensions multiples of 8 and 64 rows of either operand within 2^30 bytes, so that a lane
-// offset carrying kPastEnd plus any uniform part stays below 2^32.
-REGTILE_HD bool sk_dma_takes(int K, int64_t lda, int64_t ldb) {
-    const int64_t lim = int64_t(1) << 30;
-    return K > 0 && K % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && 64 * lda * 2 < lim && 64 * ldb * 2 < lim;
+// The split-K kernel (gemm_bf16_mfma_splitk.hip) stages 64x64 tiles. A K-contiguous operand
+// takes the K-contiguous DMA layout above (kc_dma_lane / kc_dma_instr, 64-row tiles, four
+// waves). An M/N-contiguous one keeps its storage: a slab of 64 k-rows of 8 chunks (the tile's
+// 64 columns), chunk c of row r at slot c ^ sk_mn_key(r); DMA instruction q of wave w fills
+// rows 8 (2 w + q) .. + 7, lane l row l / 8 of those at slot l % 8 (mn_dma_instr with 8
+// chunks per row gives the uniform part). A transposing fragment read takes 4 consecutive rows
+// and 4 chunks in each 32 lanes; rows two apart lie 256 bytes apart, on the same banks, so the
+// key moves the chunks of every other pair of rows to the row's other 64 bytes, and the 32
+// lanes reach 256 distinct bytes. It depends on row bit 1 only, so every instruction's lanes
+// share it.
+REGTILE_HD int sk_mn_key(int row) { return 4 * ((row >> 1) & 1); }
+REGTILE_HD uint32_t sk_mn_dma_lane(int lane, int64_t ld) {
+    const int r_in = lane >> 3, slot = lane & 7;
+    return (uint32_t)(r_in * ld + (slot ^ sk_mn_key(r_in)) * 8) * 2u;
+}
+// Problems it takes, in storage order (ta: A stored K x M; tb: B stored N x K, the 16-bit
+// native form). A K-contiguous operand: K a multiple of 8 (every chunk lies wholly before or
+// wholly past K), leading dimension a multiple of 8 and 64 rows within 2^30 bytes, so that a
+// lane offset carrying kPastEnd plus any uniform part stays below 2^32. An M/N-contiguous
+// operand: column count and leading dimension multiples of 8 (no chunk straddles the
+// descriptor's end) and K + 64 rows within 2^31 bytes.
+REGTILE_HD bool sk_dma_takes(bool ta, bool tb, int M, int N, int K, int64_t lda, int64_t ldb) {
+    const int64_t lim30 = int64_t(1) << 30, lim31 = int64_t(1) << 31;
+    auto kc_ok = [&](int64_t ld) { return K % 8 == 0 && ld % 8 == 0 && 64 * ld * 2 < lim30; };
+    auto mn_ok = [&](int64_t cols, int64_t ld) { return runs_fit(cols, ld, 8) && ((int64_t)K + 64) * ld * 2 + 512 < lim31; };
+    return K > 0 && (ta ? mn_ok(M, lda) : kc_ok(lda)) && (tb ? kc_ok(ldb) : mn_ok(N, ldb));
 }
 
 // C fragment layout of the two gfx950 MFMA shapes: accumulator v of lane l of an MF x MF

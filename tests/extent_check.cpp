@@ -14,7 +14,7 @@
 //   5. every store inside the C descriptor writes an element of C, each element of the tile
 //      exactly once.
 // Usage:
-//   extent_check one <kc|tn|nn|tt|gather|sk> M N K lda ldb ldc
+//   extent_check one <kc|tn|nn|tt|gather|sk|sk_tn|sk_nn|sk_tt> M N K lda ldb ldc
 //   extent_check force ...                   (the same, also where the launcher would refuse)
 //   extent_check sweep <seed> <count>        (seeded shapes the launchers take, every path)
 // Prints one line per violation (at most 20) and a summary; exit status 1 on any violation.
@@ -154,8 +154,10 @@ std::vector<int64_t> tiles_of(int64_t extent, int64_t t) {
 // K-contiguous operand over DMA: `rows` (M or N) rows of K elements at leading dimension ld.
 // Layout: slot p = (wave * J + q) * 64 + lane of a stage holds tile row p / 8, chunk
 // (p % 8) ^ slab_key(row) (8 elements of k); chunks of the last slab past K are flagged.
+// past_zero: loads for slabs past the last take offsets flagged past the end (zeros, meant for
+// no element), as the split-K kernel issues them; otherwise they repeat the last slab.
 template <int MF>
-void check_kc_operand(const char *name, int64_t rows, int K, int64_t ld, int t) {
+void check_kc_operand(const char *name, int64_t rows, int K, int64_t ld, int t, bool past_zero = false) {
     const Mat m{rows, K, ld, 2};
     const bool ktail = K % BK != 0;
     const int nslabs = ktail ? (K + BK - 1) / BK : K / BK, k_last = (nslabs - 1) * BK;
@@ -172,11 +174,43 @@ void check_kc_operand(const char *name, int64_t rows, int K, int64_t ld, int t) 
                 for (int q = 0; q < J; ++q)
                     for (int lane = 0; lane < 64; ++lane) {
                         const int p = (w * J + q) * 64 + lane, r = p / KCH;
-                        const int64_t col = k0 + 8 * ((p % KCH) ^ addr::slab_key<KCH, MF>(r));
+                        const bool past = past_zero && s >= nslabs;
+                        const int64_t col = (past ? (int64_t)nslabs * BK : k0) + 8 * ((p % KCH) ^ addr::slab_key<KCH, MF>(r));
                         int ck;
                         uint32_t voff = addr::kc_dma_lane<KCH, MF>(w, J, q & 1, lane, ld, &ck);
-                        if (ktail && k0 == k_last && k_last + ck >= K) voff |= addr::kPastEnd;
+                        if (past || (ktail && k0 == k_last && k_last + ck >= K)) voff |= addr::kPastEnd;
                         access(m, d, voff, addr::kc_dma_instr<KCH>(q, k0, ld), 8, false, r0 + r, col,
+                               s < nslabs ? &cov : nullptr, head + fmt(" slab %d wave %d instr %d lane %d", s, w, q, lane));
+                    }
+            if (s < nslabs) cov.verify(m, head + fmt(" slab %d", s));
+        }
+    }
+}
+
+// M/N-major operand of the split-K kernel: K rows of `cols` (M or N) elements at ld, 64-wide
+// tiles. A slab is 64 k-rows of 8 chunks; instruction q of wave w fills rows 8 (2 w + q) ..,
+// lane l row l / 8 of those, slot l % 8, holding chunk slot ^ sk_mn_key(row). Slabs past the
+// last load zeros (offsets flagged past the end).
+void check_sk_mn_operand(const char *name, int64_t cols, int K, int64_t ld) {
+    const Mat m{K, cols, ld, 2};
+    const int nslabs = (K + BK - 1) / BK;
+    for (int64_t c0 : tiles_of(cols, 64)) {
+        const std::string head = fmt("sk-mn %s tile col %ld cols %ld K %d ld %ld", name, (long)c0, (long)cols, K, (long)ld);
+        const Desc d{c0, addr::desc_bytes(K, ld, cols - c0, 2)};
+        check_desc(m, d, head);
+        for (int s : slabs_of(nslabs)) {
+            const int k0 = std::min(s, nslabs - 1) * BK;
+            Cover cov(k0, c0, BK, 64);
+            for (int w = 0; w < NWAVES; ++w)
+                for (int q = 0; q < 2; ++q)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int row = 8 * (2 * w + q) + lane / 8;  // within the slab
+                        const int64_t col = c0 + 8 * ((lane % 8) ^ addr::sk_mn_key(row));
+                        const bool past = s >= nslabs;  // meant for no element: rows from K on
+                        uint32_t voff = addr::sk_mn_dma_lane(lane, ld);
+                        if (past) voff |= addr::kPastEnd;
+                        access(m, d, voff, addr::mn_dma_instr(w, 2, q, k0, ld, 8), 8, false,
+                               (past ? (int64_t)nslabs * BK : k0) + row, col,
                                s < nslabs ? &cov : nullptr, head + fmt(" slab %d wave %d instr %d lane %d", s, w, q, lane));
                     }
             if (s < nslabs) cov.verify(m, head + fmt(" slab %d", s));
@@ -327,10 +361,13 @@ bool check_problem(const std::string &path, int M, int N, int K, int64_t lda, in
         check_c<32>(M, N, ldc, t);
         return true;
     }
-    if (path == "sk") {  // split-K kernel: A row-major, B stored N x K, 64x64 tiles
-        if (!addr::sk_dma_takes(K, lda, ldb) && !g_force) return false;
-        check_kc_operand<32>("A", M, K, lda, 64);
-        check_kc_operand<32>("B", N, K, ldb, 64);
+    if (path.rfind("sk", 0) == 0) {  // split-K kernel, 64x64 tiles: sk ("n t"), sk_tn, sk_nn, sk_tt
+        const bool ta = path == "sk_tn" || path == "sk_tt", tb = path == "sk" || path == "sk_tt";
+        if (!addr::sk_dma_takes(ta, tb, M, N, K, lda, ldb) && !g_force) return false;
+        if (ta) check_sk_mn_operand("A", M, K, lda);
+        else check_kc_operand<32>("A", M, K, lda, 64, true);
+        if (tb) check_kc_operand<32>("B", N, K, ldb, 64, true);
+        else check_sk_mn_operand("B", N, K, ldb);
         return true;
     }
     if (path == "tn") {
@@ -384,14 +421,15 @@ int main(int argc, char **argv) {
         const int sizes[] = {1, 2, 3, 4, 7, 8, 12, 16, 24, 56, 63, 64, 65, 96, 120, 127, 128, 129, 136, 200,
                              248, 255, 256, 257, 263, 264, 384, 509, 512, 520, 1000, 1088, 1504, 2040};
         const int n_sizes = sizeof sizes / sizeof sizes[0];
-        const char *paths[] = {"kc", "tn", "nn", "tt", "gather", "sk"};
+        const char *paths[] = {"kc", "tn", "nn", "tt", "gather", "sk", "sk_tn", "sk_nn", "sk_tt"};
         long taken = 0;
         for (int c = 0; c < count; ++c) {
             const int M = sizes[rng() % n_sizes], N = sizes[rng() % n_sizes], K = sizes[rng() % n_sizes];
             for (const char *path : paths) {
                 // leading dimensions: the smallest legal, or that plus a small pad
                 const std::string p = path;
-                const bool a_km = p == "tn" || p == "tt" || p == "gather", b_kn = p == "tn" || p == "nn" || p == "gather";
+                const bool a_km = p == "tn" || p == "tt" || p == "gather" || p == "sk_tn" || p == "sk_tt";
+                const bool b_kn = p == "tn" || p == "nn" || p == "gather" || p == "sk_tn" || p == "sk_nn";
                 const int64_t lda = (a_km ? M : K) + (rng() % 3 == 0 ? 8 * (int64_t)(rng() % 3) : 0);
                 const int64_t ldb = (b_kn ? N : K) + (rng() % 3 == 0 ? 8 * (int64_t)(rng() % 3) : 0);
                 const int64_t ldc = N + (rng() % 3 == 0 ? (int64_t)(rng() % 5) : 0);
@@ -402,6 +440,6 @@ int main(int argc, char **argv) {
                     g_violations);
         return g_violations ? 1 : 0;
     }
-    std::fprintf(stderr, "usage: extent_check one <kc|tn|nn|tt|gather|sk> M N K lda ldb ldc | sweep <seed> <count>\n");
+    std::fprintf(stderr, "usage: extent_check one <kc|tn|nn|tt|gather|sk|sk_tn|sk_nn|sk_tt> M N K lda ldb ldc | sweep <seed> <count>\n");
     return 2;
 }

@@ -292,3 +292,37 @@ def test_16bit_unaligned_column_counts_take_the_staged_gather(dtype, ta, tb, sha
     assert "_dma_" not in name and "_edge" in name, name
     assert torch.all(big[:, N:] == -77.0).item(), "a store landed past column N"
     assert_parity_full(inp, C.cpu().numpy(), f"{dtype} ({ta},{tb}) {shape} ({name})")
+
+
+# ---- the 16-bit split-K kernel in every storage order ------------------------------------------
+# M/N-contiguous operands keep their storage in LDS (64 k-rows of the tile's 64 columns) and
+# reach the MFMAs through transposing reads. Shapes: few tiles with deep K, ragged tile edges with
+# a K tail (K a multiple of 8 where an operand is K-contiguous), and K below one slab; integer
+# inputs compare bitwise, normal inputs within the bound.
+SK_LAYOUT_CASES = [((1024, 1024, 2048), "normal"), ((1000, 1000, 776), "normal"), ((72, 136, 72), "normal"),
+                   ((512, 256, 4104), "int"), ((64, 64, 8), "normal")]
+SK_SUFFIX = {(1, 1): "_tt", (0, 0): "_nn", (1, 0): "_tn", (0, 1): ""}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("case", SK_LAYOUT_CASES, ids=lambda c: "x".join(map(str, c[0])) + "-" + c[1])
+def test_16bit_splitk_every_layout(case, ta, tb, dtype):
+    (M, N, K), dist = case
+    if dist == "int":
+        rng = np.random.Generator(np.random.PCG64(M + N + K + 2 * ta + tb))
+        to_bits = gi.f32_to_bf16_bits if dtype == "bf16" else gi.f32_to_f16_bits
+        A = to_bits(rng.integers(-16, 17, M * K).astype(np.float32)).reshape(M, K)
+        Bt = to_bits(rng.integers(-16, 17, N * K).astype(np.float32)).reshape(N, K)
+        inp = gi.GemmInputs(M, N, K, 1.0, 0.0, dtype, True, A, Bt, None)
+    else:
+        inp = gi.make_inputs(M, N, K, dtype=dtype, dist="normal", alpha=1.25, beta=-0.5, seed=M + N + K + 4 * ta + tb)
+    announce(f"{dtype} split-K layout {ta}{tb} {(M, N, K)} {dist}")
+    got, name = _run(inp, ta, tb, rt.ALGO_BF16_MFMA_SPLITK)
+    ktail = K % 64 != 0 and (ta, tb) != (1, 0)
+    assert name == f"{dtype}_mfma32x32x16_splitk4_64x64x64{SK_SUFFIX[(ta, tb)]}" + ("_ktail" if ktail else ""), name
+    if dist == "int":
+        ref, _ = oracle.gemm_inputs(inp)
+        assert np.array_equal(got.astype(np.float64), ref)
+    else:
+        assert_parity_full(inp, got, f"{dtype} split-K layout ({ta},{tb}) {(M, N, K)} ({name})")

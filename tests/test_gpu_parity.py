@@ -372,7 +372,7 @@ def test_16bit_splitk_kernel(shape, dtype, pad):
 
 def test_16bit_auto_picks_splitk_by_tile_count():
     # the default entry points: split-K for few 64x64 tiles with enough K, the LDS-DMA kernel
-    # otherwise (and for any layout other than K-contiguous A and B)
+    # otherwise
     cases = [((1024, 1024, 4096), "splitk4"), ((512, 512, 1024), "splitk4"), ((1280, 1280, 8192), "splitk4"),
              ((1024, 1024, 512), "_dma_"), ((1024, 2048, 2048), "_dma_"), ((1536, 1536, 8192), "_dma_")]
     for (M, N, K), want in cases:
@@ -382,10 +382,21 @@ def test_16bit_auto_picks_splitk_by_tile_count():
         assert want in rt.last_kernel(), ((M, N, K), rt.last_kernel())
         rt.gemm_f16(A.half(), Bt.half().t())
         assert want in rt.last_kernel() and rt.last_kernel().startswith("f16_"), ((M, N, K), rt.last_kernel())
-    # "n n" storage of the same few-tile problem keeps the LDS-DMA kernel
-    rt.gemm_bf16(torch.zeros((1024, 4096), dtype=torch.bfloat16, device="cuda"),
-                 torch.zeros((4096, 1024), dtype=torch.bfloat16, device="cuda"))
-    assert "splitk" not in rt.last_kernel(), rt.last_kernel()
+    # other storage orders: up to 256 tiles with K >= 1024 in all of them; up to 512 with K >=
+    # 4096 only for "t n" (and "n t" above)
+    def storage(M, N, K, ta, tb):
+        A = torch.zeros((K, M) if ta else (M, K), dtype=torch.bfloat16, device="cuda")
+        B = torch.zeros((N, K) if tb else (K, N), dtype=torch.bfloat16, device="cuda")
+        return (A.t() if ta else A), (B.t() if tb else B)
+    for (M, N, K), (ta, tb), want in (((1024, 1024, 4096), (0, 0), "splitk4_64x64x64_nn"),
+                                      ((1024, 1024, 4096), (1, 1), "splitk4_64x64x64_tt"),
+                                      ((1024, 1024, 4096), (1, 0), "splitk4_64x64x64_tn"),
+                                      ((1024, 2048, 8192), (1, 0), "splitk4_64x64x64_tn"),
+                                      ((1024, 2048, 8192), (0, 0), "_dma_"),
+                                      ((1024, 2048, 8192), (1, 1), "_dma_")):
+        A, B = storage(M, N, K, ta, tb)
+        rt.gemm_bf16(A, B)
+        assert want in rt.last_kernel(), ((M, N, K), (ta, tb), rt.last_kernel())
     torch.cuda.synchronize()
 
 
@@ -405,9 +416,10 @@ def test_16bit_splitk_integer_inputs_bitwise():
 
 
 def test_16bit_splitk_falls_back_where_it_does_not_apply():
-    # K not a multiple of 8, and a transposed A: the split-K rung hands the problem to the
+    # K not a multiple of 8 with a K-contiguous operand, and an M-contiguous A whose column count
+    # and leading dimension are not multiples of 8: the split-K rung hands the problem to the
     # MFMA kernel, with the same results as that rung
-    for (M, N, K), ta in (((300, 200, 100), False), ((256, 256, 512), True)):
+    for (M, N, K), ta in (((300, 200, 100), False), ((300, 256, 512), True)):
         inp = gi.make_inputs(M, N, K, dtype="bf16", dist="normal", alpha=1.0, beta=0.0, seed=M + N + K)
         A, B, _ = device_operands(inp, torch)
         if ta:
