@@ -54,7 +54,7 @@ def _parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--only", choices=["f32_4096", "bf16_8192", "f16_8192", "f32_ragged",
-                                      "f32_tall", "f32_256", "copy"],
+                                      "f32_tall", "f32_256", "bf16_few", "copy"],
                    help="profiler mode: run just this workload's kernel (warmup + steps) and "
                         "print one summary line; 'copy' runs a plain 1 GiB device copy used to "
                         "calibrate the HBM byte counters")
@@ -598,8 +598,9 @@ def main():
     # ---- a bf16 problem of few output tiles: split-K inside the workgroup against the
     # LDS-DMA kernel (64 tiles of 128x128 for 256 CUs) --------------------------------------
     if not args.no_ladder and not args.no_bf16:
-        M_, N_, K_ = 1024, 1024, 16384
-        ift = gi.make_inputs(M_, N_, K_, dtype="bf16", dist="normal", seed=1005)
+        wf = gi.WORKLOADS["bf16_few"]
+        M_, N_, K_ = wf.M, wf.N, wf.K
+        ift = gi.workload_inputs(wf)
         Af = torch.from_numpy(ift.A.view(np.int16)).to(dev)
         Bf = torch.from_numpy(ift.B.view(np.int16)).to(dev)  # stored N x K
         Cf = torch.empty((M_, N_), dtype=torch.float32, device=dev)

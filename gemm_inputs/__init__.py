@@ -62,7 +62,8 @@ class Workload:
 
 # The five workloads: a small correctness case, the square fp32 case, a ragged case
 # with a non-trivial epilogue, the square bf16 case (column-major B) and a tall-skinny case;
-# then fp16 operands at the bf16 case's shape, and the fp32 path at that shape.
+# then fp16 operands at the bf16 case's shape, the fp32 path at that shape, and a bf16 problem of
+# few output tiles with a deep K.
 WORKLOADS = {
     "f32_256": Workload("f32_256", 256, 256, 256, "f32", "uniform", 1.0, 0.0, 1001,
                         description="fp32 256^3, U[-1,1], alpha=1, beta=0"),
@@ -80,6 +81,10 @@ WORKLOADS = {
                          description="fp16 8192^3, A row-major, B column-major, N(0,1) rounded to fp16, fp32 C"),
     "f32_8192": Workload("f32_8192", 8192, 8192, 8192, "f32", "uniform", 1.0, 0.0, 1007,
                          description="fp32 8192^3, U[-1,1], alpha=1, beta=0 (the fp32 path at the bf16 size)"),
+    "bf16_few": Workload("bf16_few", 1024, 1024, 16384, "bf16", "normal", 1.0, 0.0, 1008,
+                         b_col_major=True,
+                         description="bf16 M=N=1024 K=16384 (few output tiles), A row-major, B column-major, "
+                                     "N(0,1) rounded to bf16, fp32 C"),
 }
 
 

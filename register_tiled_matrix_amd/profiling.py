@@ -71,7 +71,7 @@ KERNELS = {
 }
 PMC_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged", "copy"]
 # one kernel trace per workload, so that each summary's statistics are that workload's alone
-TRACE_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged"]
+TRACE_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged", "bf16_few"]
 TRACE_STEPS, TRACE_WARMUP = 200, 50
 SQ_WORKLOADS = ["f32_4096", "bf16_8192", "f32_tall", "f32_ragged"]
 

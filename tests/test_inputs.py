@@ -54,7 +54,9 @@ def test_workload_table():
     assert h.dtype == "f16" and h.b_col_major and (h.M, h.N, h.K) == (8192, 8192, 8192)
     e = w["f32_8192"]
     assert e.dtype == "f32" and not e.b_col_major and (e.M, e.N, e.K) == (8192, 8192, 8192)
-    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005, 1006, 1007]
+    f = w["bf16_few"]
+    assert f.dtype == "bf16" and f.b_col_major and (f.M, f.N, f.K) == (1024, 1024, 16384)
+    assert [x.seed for x in w.values()] == [1001, 1002, 1003, 1004, 1005, 1006, 1007, 1008]
 
 
 def test_determinism_and_layout():
